@@ -1,0 +1,315 @@
+"""Pins of the fp64 oracle against facts the pages and the mathematics fix.
+
+None of these re-types the oracle's own formula: each checks it against a
+different route to the same number (an SVD closed form, a brute-force loop, a
+scalar recurrence, an identity the pages state, or a library routine).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import muonclip_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def phi_n(x, n, a=O.NS_A, b=O.NS_B, c=O.NS_C):
+    """phi(x) = a x + b x^3 + c x^5 composed n times (scalar route)."""
+    for _ in range(n):
+        x = a * x + b * x ** 3 + c * x ** 5
+    return x
+
+
+def closed_form_ns(m, steps=5, eps=1e-7):
+    """U phi^N(S / (||M||_F + eps)) V^T from numpy's SVD (Notes on Muon blog,
+    "Newton-Schulz": N steps of the iteration act on singular values only)."""
+    u, s, vt = np.linalg.svd(m, full_matrices=False)
+    sn = s / (np.linalg.norm(m) + eps)
+    return (u * phi_n(sn, steps)) @ vt
+
+
+@pytest.mark.parametrize("shape", [(16, 64), (64, 16), (64, 64), (8, 8), (48, 200), (200, 48), (1, 7), (7, 1)])
+def test_ns_matches_svd_closed_form(shape):
+    rng = np.random.default_rng(11)
+    m = rng.standard_normal(shape)
+    got = oracle.newton_schulz(m)
+    want = closed_form_ns(m)
+    assert np.linalg.norm(got - want) <= 1e-12 * max(1.0, np.linalg.norm(want))
+
+
+def test_ns_rank_one_value():
+    # rank-1 M = u v^T has one normalised singular value ~1 -> phi^5(1) u^ v^T
+    rng = np.random.default_rng(3)
+    u, v = rng.standard_normal(37), rng.standard_normal(53)
+    m = np.outer(u, v)
+    got = oracle.newton_schulz(m)
+    s1 = np.linalg.norm(m) / (np.linalg.norm(m) + 1e-7)
+    want = phi_n(s1, 5) * np.outer(u / np.linalg.norm(u), v / np.linalg.norm(v))
+    assert np.allclose(got, want, atol=1e-12)
+    # the value printed in the band table below: phi^5(1) = 0.69643...
+    assert abs(phi_n(1.0, 5) - 0.6964364) < 1e-6
+
+
+def test_ns_zero_matrix_gives_zero():
+    got = oracle.newton_schulz(np.zeros((5, 9)))
+    assert np.all(got == 0.0)
+
+
+def test_ns_scale_and_transpose_invariance():
+    # Ortho(cM) = Ortho(M) (Notes on Muon blog, rescaling); the transpose rule
+    # of newtonschulz5 makes NS(M^T) = NS(M)^T exactly in exact arithmetic.
+    rng = np.random.default_rng(5)
+    m = rng.standard_normal((24, 40))
+    o = oracle.newton_schulz(m)
+    assert np.allclose(oracle.newton_schulz(m * 1e3), o, atol=1e-9)
+    assert np.allclose(oracle.newton_schulz(m.T), o.T, atol=1e-12)
+
+
+def test_ns_singular_values_in_band():
+    # the band phi^5 reaches on [0.002, 1] (brute force on a fine grid) holds
+    # every normalised singular value of a well-conditioned Gaussian matrix
+    xs = np.linspace(0.002, 1.0, 200001)
+    ys = phi_n(xs, 5)
+    lo, hi = ys.min(), ys.max()
+    assert 0.68 < lo < 0.69 and 1.20 < hi < 1.21
+    rng = np.random.default_rng(9)
+    for shape in [(32, 128), (128, 32), (50, 300)]:
+        m = rng.standard_normal(shape)
+        s = np.linalg.svd(oracle.newton_schulz(m), compute_uv=False)
+        assert s.min() >= lo - 1e-9 and s.max() <= hi + 1e-9
+
+
+def test_ns_coefficient_sign():
+    # with b = -4.7750 phi(1) lies in the [0.7, 1.3] target band of "Coefficient
+    # Optimization"; with the +4.7750 printed in the Moonlight notes it is 10.25
+    assert O.NS_B < 0
+    assert 0.7 <= phi_n(1.0, 1) <= 1.3
+    assert phi_n(1.0, 1, b=+4.7750) > 10.0
+    assert (O.NS_A, O.NS_C, O.NS_STEPS, O.NS_EPS) == (3.4445, 2.0315, 5, 1e-7)
+
+
+def test_rms_lemma():
+    # Notes on Moonlight, "Scaling up Muon": RMS(U V^T) = sqrt(r/(AB)); for a
+    # full-rank [A, B] matrix 0.2*sqrt(max(A,B))*UV^T has RMS exactly 0.2
+    rng = np.random.default_rng(2)
+    for A, B in [(30, 70), (70, 30), (40, 40)]:
+        u, _, vt = np.linalg.svd(rng.standard_normal((A, B)), full_matrices=False)
+        upd = oracle.rms_matched(u @ vt, A, B, 0.2)
+        assert abs(np.sqrt(np.mean(upd ** 2)) - 0.2) < 1e-12
+        # with the NS approximation the RMS sits in 0.2 x the phi^5 band
+        o = oracle.newton_schulz(rng.standard_normal((A, B)))
+        r = np.sqrt(np.mean(oracle.rms_matched(o, A, B) ** 2))
+        assert 0.2 * 0.68 < r < 0.2 * 1.21
+
+
+def test_decay_only_special_case():
+    # G = 0 and M = 0 -> O = 0 -> W' = (1 - lr*lambda) W
+    rng = np.random.default_rng(4)
+    w = rng.standard_normal((12, 20)).astype(np.float32).astype(np.float64)
+    z = np.zeros_like(w)
+    w_new, m_new, o = oracle.muonclip_step_matrix(w, z, z, lr=0.01, mu=0.95, weight_decay=0.1,
+                                                  w_dtype="f32")
+    assert np.all(o == 0) and np.all(m_new == 0)
+    assert np.array_equal(w_new, (w * (1 - 0.01 * 0.1)).astype(np.float32).astype(np.float64))
+
+
+def test_momentum_cold_start_and_closed_form():
+    rng = np.random.default_rng(6)
+    g1, g2 = rng.standard_normal((3, 4)), rng.standard_normal((3, 4))
+    m1 = oracle.momentum(np.zeros((3, 4)), g1, 0.9)      # M_0 = 0
+    assert np.array_equal(m1, g1)
+    m2 = oracle.momentum(m1, g2, 0.9)
+    assert np.allclose(m2, 0.9 * g1 + g2, rtol=0, atol=0)
+
+
+def test_update_step_order_against_hand_expansion():
+    # one full step on a tiny matrix, against the update written out by hand
+    # from the Moonlight rule with the closed-form NS
+    rng = np.random.default_rng(8)
+    w = rng.standard_normal((6, 10))
+    g = rng.standard_normal((6, 10))
+    m = rng.standard_normal((6, 10))
+    lr, mu, wd = 0.05, 0.9, 0.1
+    w_new, m_new, o = oracle.muonclip_step_matrix(w, g, m, lr=lr, mu=mu, weight_decay=wd, w_dtype="f64")
+    mm = mu * m + g
+    upd = 0.2 * math.sqrt(10) * closed_form_ns(mm)
+    want = w - lr * upd - lr * wd * w
+    assert np.allclose(w_new, want, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- S_max
+
+def _tiny_qk(rng, B, T, H, dk, ds):
+    q = rng.standard_normal((B, T, H, dk + ds))
+    k = rng.standard_normal((B, T, H, dk))
+    ks = rng.standard_normal((B, T, ds)) if ds else None
+    return q, k, ks
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("ds", [0, 3])
+def test_max_logits_blocked_equals_bruteforce(causal, ds):
+    rng = np.random.default_rng(12 + ds)
+    q, k, ks = _tiny_qk(rng, 2, 9, 3, 4, ds)
+    a = oracle.max_logits(q, k, ks, causal, 0.5, block=4)
+    b = oracle.max_logits_bruteforce(q, k, ks, causal, 0.5)
+    assert np.allclose(a, b, rtol=1e-14, atol=1e-14)
+
+
+def test_max_logits_torch_route():
+    # the same quantity computed through torch CPU einsum projections (the
+    # route the essay's MHA sample takes): x -> Q, K per head -> QK^T -> amax
+    import torch
+    g = torch.Generator().manual_seed(1)
+    x = torch.randn(2, 7, 6, generator=g, dtype=torch.float64)
+    wq = torch.randn(3, 6, 4, generator=g, dtype=torch.float64)
+    wk = torch.randn(3, 6, 4, generator=g, dtype=torch.float64)
+    qh = torch.einsum("btd,hdf->bthf", x, wq)
+    kh = torch.einsum("btd,hdf->bthf", x, wk)
+    ref = torch.einsum("bihf,bjhf->bhij", qh, kh).amax(dim=(0, 2, 3)) / 2.0
+    got = oracle.max_logits(qh.numpy(), kh.numpy(), None, False, 0.5)
+    assert np.allclose(got, ref.numpy(), rtol=1e-14)
+
+
+def test_max_logits_ignores_nan_and_empty():
+    q = np.ones((1, 2, 1, 2))
+    k = np.ones((1, 2, 1, 2))
+    k[0, 1, 0, 0] = np.nan
+    got = oracle.max_logits(q, k, None, False, 1.0)
+    assert got[0] == 2.0
+    empty = oracle.max_logits(np.zeros((0, 3, 2, 4)), np.zeros((0, 3, 2, 4)), None, True, 1.0)
+    assert np.all(np.isneginf(empty))
+
+
+# ---------------------------------------------------------------- gamma / clip
+
+def test_gamma_policy_special_cases():
+    s = np.array([-3.0, 0.0, np.nan, 50.0, 100.0, 200.0, np.inf])
+    g = oracle.clip_factor(s, 100.0)
+    assert list(g[:5]) == [1.0, 1.0, 1.0, 1.0, 1.0]
+    assert g[5] == 0.5 and g[6] == 0.0
+    assert np.all(g <= 1.0)
+
+
+def test_essay_worked_example_invariants():
+    # the essay's MHA sample: seeded x, W_q, W_k (scaled by 8), tau = 10;
+    # after the per-head sqrt(gamma) rescale the max logit equals before*gamma
+    # and does not exceed tau; gamma <= 1.
+    import torch
+    spec = json.load(open(os.path.join(GOLDEN, "essay_mha_example.json")))
+    torch.manual_seed(spec["seed"])
+    x = torch.randn(*spec["x_shape"])
+    wq = torch.randn(*spec["w_shape"]) * spec["w_scale"]
+    wk = torch.randn(*spec["w_shape"]) * spec["w_scale"]
+    tau = spec["tau"]
+    x64, wq64, wk64 = (t.double().numpy() for t in (x, wq, wk))
+    H, dm, dh = wq64.shape
+
+    def smax(wqm, wkm):
+        q = np.einsum("btd,hdf->bthf", x64, wqm)
+        k = np.einsum("btd,hdf->bthf", x64, wkm)
+        return oracle.max_logits(q, k, None, False, 1.0 / math.sqrt(dh))
+
+    before = smax(wq64, wk64)
+    gamma = oracle.clip_factor(before, tau)
+    # as projection matrices [H*dh, dm]: row h*dh+f = W[h, :, f]
+    def as_rows(w):
+        return w.transpose(0, 2, 1).reshape(H * dh, dm)
+
+    def from_rows(m):
+        return m.reshape(H, dh, dm).transpose(0, 2, 1)
+    seg = [(0, dh, 0.5)]
+    wq2 = from_rows(oracle.qk_clip_rows(as_rows(wq64), gamma, dh, seg))
+    wk2 = from_rows(oracle.qk_clip_rows(as_rows(wk64), gamma, dh, seg))
+    after = smax(wq2, wk2)
+    assert np.allclose(after, before * gamma, rtol=1e-12)
+    assert np.all(after <= tau * (1 + spec["rel_slack"]))
+    assert np.all(gamma <= 1.0)
+    assert np.any(gamma < 1.0)
+
+
+def test_mla_clip_identity_and_shared_rope_untouched():
+    # tiny MLA: per-head q rows [q^C | q^R], kv_b rows [k^C | v], shared k^R.
+    # After clipping with the MLA exponents every head's max logit becomes
+    # before*gamma (content sqrt*sqrt, rope gamma*1), k^R rows are unchanged.
+    rng = np.random.default_rng(21)
+    H, dc, dr, dv, dm, lq, lkv, B, T = 3, 4, 2, 4, 10, 6, 5, 2, 8
+    q_a = rng.standard_normal((lq, dm))
+    q_b = rng.standard_normal((H * (dc + dr), lq))
+    q_b[: dc + dr] *= 8.0  # head 0 hot
+    kv_a = rng.standard_normal((lkv + dr, dm))
+    kv_b = rng.standard_normal((H * (dc + dv), lkv))
+    kv_b[: dc + dv] *= 8.0
+    x = rng.standard_normal((B, T, dm))
+
+    def smax(q_b_, kv_a_, kv_b_):
+        q = (x @ q_a.T) @ q_b_.T
+        q = q.reshape(B, T, H, dc + dr)
+        ckv = x @ kv_a_[:lkv].T
+        kr = x @ kv_a_[lkv:].T
+        kc = (ckv @ kv_b_.reshape(H, dc + dv, lkv)[:, :dc].reshape(H * dc, lkv).T).reshape(B, T, H, dc)
+        return oracle.max_logits(q, kc, kr, True, 1.0 / math.sqrt(dc + dr))
+
+    before = smax(q_b, kv_a, kv_b)
+    tau = float(np.sort(before)[-1]) / 3.0
+    gamma = oracle.clip_factor(before, tau)
+    assert gamma[0] < 1.0
+    q_b2 = oracle.qk_clip_rows(q_b, gamma, dc + dr, [(0, dc, 0.5), (dc, dr, 1.0)])
+    kv_b2 = oracle.qk_clip_rows(kv_b, gamma, dc + dv, [(0, dc, 0.5)])
+    after = smax(q_b2, kv_a, kv_b2)
+    assert np.allclose(after, before * gamma, rtol=1e-12)
+    assert np.all(after <= tau * (1 + 1e-12))
+    # untouched: v rows of kv_b and all of kv_a (holds k^R)
+    for h in range(H):
+        r0 = h * (dc + dv)
+        assert np.array_equal(kv_b2[r0 + dc: r0 + dc + dv], kv_b[r0 + dc: r0 + dc + dv])
+    # heads with gamma == 1 are bit-identical
+    for h in np.nonzero(gamma == 1.0)[0]:
+        r0 = h * (dc + dr)
+        assert np.array_equal(q_b2[r0:r0 + dc + dr], q_b[r0:r0 + dc + dr])
+
+
+def test_wrong_exponent_breaks_the_identity():
+    # the identity above is a real pin: swapping the rope exponent to 1/2 fails it
+    rng = np.random.default_rng(22)
+    H, dc, dr = 2, 3, 2
+    q = rng.standard_normal((1, 6, H, dc + dr)) * 5
+    kc = rng.standard_normal((1, 6, H, dc)) * 5
+    kr = rng.standard_normal((1, 6, dr)) * 5
+    before = oracle.max_logits(q, kc, kr, False, 1.0)
+    gamma = np.array([0.25, 0.5])
+    q_ok = q.copy()
+    q_bad = q.copy()
+    for h in range(H):
+        q_ok[..., h, :dc] *= math.sqrt(gamma[h]); q_ok[..., h, dc:] *= gamma[h]
+        q_bad[..., h, :dc] *= math.sqrt(gamma[h]); q_bad[..., h, dc:] *= math.sqrt(gamma[h])
+    kc_ok = kc * np.sqrt(gamma)[None, None, :, None]
+    assert np.allclose(oracle.max_logits(q_ok, kc_ok, kr, False, 1.0), before * gamma)
+    assert not np.allclose(oracle.max_logits(q_bad, kc_ok, kr, False, 1.0), before * gamma)
+
+
+# ---------------------------------------------------------------- rounding
+
+def test_round_to_bf16_against_torch_and_ties():
+    import torch
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(20000) * np.exp(rng.uniform(-30, 30, 20000))).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.round_to_bf16(x.astype(np.float64))
+    assert np.array_equal(got, want)
+    # ties to even: 1 + 2^-8 is halfway between 1 and 1 + 2^-7
+    assert oracle.round_to_bf16(np.array([1 + 2 ** -8]))[0] == 1.0
+    assert oracle.round_to_bf16(np.array([1 + 3 * 2 ** -8]))[0] == 1 + 2 ** -6
+    # a single rounding from fp64: just above the tie goes up
+    assert oracle.round_to_bf16(np.array([1 + 2 ** -8 + 2 ** -40]))[0] == 1 + 2 ** -7
+    assert np.isinf(oracle.round_to_bf16(np.array([3.5e38]))[0])
+
+
+def test_ns_flops_formula():
+    # Notes on Muon blog, "Analysis": 2(2nm^2 + m^3) per step, m <= n
+    assert oracle.ns_flops(2048, 7168, 1) == 2 * (2 * 7168 * 2048 ** 2 + 2048 ** 3)
+    assert oracle.ns_flops(7168, 2048, 5) == oracle.ns_flops(2048, 7168, 5)
