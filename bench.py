@@ -1,0 +1,249 @@
+"""Benchmark of one MuonClip optimizer step on one MI355X.
+
+A step is the whole hot path over one batch of synthetic input: the per-head
+max logit of every attention layer (max_logits_per_head) followed by
+muonclip_step (momentum, Newton-Schulz, RMS-matched decoupled update, QK-Clip)
+over every 2-D parameter of the workload. Inputs are resident in HBM before
+the timed region starts.
+
+Default workload: the MHA layer (W_q, W_k, W_v, W_o 2048x2048 bf16 with fp32
+momentum; S_max over 4 x 4096 causal tokens, 16 heads of 128).
+
+Prints one JSON line. `value` is the step time in ms (lower is better); the
+same line carries the Newton-Schulz TFLOP/s, S_max Glogits/s, elementwise
+GB/s, the roofline of the dominant kernel (the NS GEMM) measured with HIP
+events around every launch of the library, and the fp64 oracle timed on the
+host cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MuonClip step ms & NS TFLOP/s (% MFMA peak); S_max Glogits/s; elementwise GB/s"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default: 2, the MHA layer)")
+    ap.add_argument("--experts", type=int, default=385, help="expert count for workloads 4/5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-s", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def ns_flops(rows, cols, steps):
+    m, n = min(rows, cols), max(rows, cols)
+    return steps * 2.0 * (2.0 * n * m * m + m ** 3)
+
+
+def build_workload(cfg, dev):
+    """Device buffers for every matrix plus Q/K of every attention layer."""
+    import numpy as np
+    import torch
+
+    import muonclip_step_amd as mc
+    import workloads as wl
+
+    mats, keep = [], []
+    host_w = {}
+    for i, s in enumerate(cfg.matrices):
+        if s.device_drawn:
+            w, g, m = wl.draw_device_tensors(cfg, i, dev)
+        else:
+            wh = wl.draw_weight(cfg, i)
+            host_w[s.name] = wh
+            w = torch.from_numpy(wh).to(torch.bfloat16 if s.w_dtype == "bf16" else torch.float32).to(dev)
+            g = torch.from_numpy(wl.draw_grad(cfg, i)).to(dev)
+            m = torch.from_numpy(wl.draw_momentum(cfg, i)).to(dev)
+        keep += [w, g, m]
+        mats.append(mc.matrix(w, g, m, clip_slot=s.clip_slot, period=s.period, segments=s.segments))
+    attn = None
+    if cfg.attn is not None:
+        q, k, ks = wl.draw_attention_inputs(cfg, host_w)
+        dt = torch.bfloat16 if cfg.attn.dtype == "bf16" else torch.float32
+        qd = torch.from_numpy(np.ascontiguousarray(q)).to(dt).to(dev)
+        kd = torch.from_numpy(np.ascontiguousarray(k)).to(dt).to(dev)
+        ksd = torch.from_numpy(np.ascontiguousarray(ks)).to(dt).to(dev) if ks is not None else None
+        attn = (qd, kd, ksd)
+        del q, k, ks
+    return mats, keep, attn
+
+
+def cpu_baseline(cfg, budget_s):
+    """The fp64 oracle on a bounded sample of the same workload, scaled to a
+    full step: whole matrices (momentum -> NS -> update -> clip) until the
+    budget is spent, and S_max of a few (sample, head) slices."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    hp = cfg.hparams
+    t_mat, done_mats, flops_done = 0.0, 0, 0.0
+    total_flops = sum(ns_flops(s.rows, s.cols, hp["ns_steps"]) for s in cfg.matrices)
+    order = [i for i, s in enumerate(cfg.matrices) if not s.device_drawn] or [0]
+    for i in order:
+        s = cfg.matrices[i]
+        if s.device_drawn:
+            break
+        w, g, m = wl.draw_weight(cfg, i), wl.draw_grad(cfg, i), wl.draw_momentum(cfg, i)
+        t0 = time.perf_counter()
+        oracle.muonclip_step_matrix(w.astype(np.float64), g.astype(np.float64), m.astype(np.float64),
+                                    lr=hp["lr"], mu=hp["mu"], weight_decay=hp["weight_decay"],
+                                    w_dtype=s.w_dtype)
+        t_mat += time.perf_counter() - t0
+        done_mats += 1
+        flops_done += ns_flops(s.rows, s.cols, hp["ns_steps"])
+        if t_mat > budget_s * 0.7:
+            break
+    ms_muon = t_mat / flops_done * total_flops * 1e3 if flops_done else float("nan")
+    ms_smax, sl = 0.0, 0
+    a = cfg.attn
+    if a is not None:
+        q = wl.quantize_bf16(wl.normal(99, 0, (1, a.T, 1, a.d_q), 1.0))
+        k = wl.quantize_bf16(wl.normal(99, 1, (1, a.T, 1, a.d_k), 1.0))
+        ks = wl.quantize_bf16(wl.normal(99, 2, (1, a.T, a.d_shared), 1.0)) if a.d_shared else None
+        t0 = time.perf_counter()
+        while True:
+            oracle.max_logits(q, k, ks, a.causal, 1.0 / math.sqrt(a.d_q))
+            sl += 1
+            if time.perf_counter() - t0 > budget_s * 0.3:
+                break
+        per = (time.perf_counter() - t0) / sl
+        ms_smax = per * a.B * a.H * 1e3
+    return {"value": ms_muon + ms_smax, "unit": "ms per step (extrapolated)", "cores": cores, "kind": "oracle",
+            "sample": f"{done_mats} of {len(cfg.matrices)} matrices through the full fp64 step, scaled by NS "
+                      f"FLOPs to all matrices; S_max on {sl} single (sample, head) slices of T={a.T if a else 0},"
+                      f" scaled by B*H" if a else f"{done_mats} matrices, scaled by NS FLOPs"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported by this build "
+              "(the step shards by whole matrices; no multi-GPU path exists here).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import muonclip_step_amd as mc
+    import workloads as wl
+
+    mc.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kw = {"n_experts": args.experts} if args.config in (4, 5) else {}
+    cfg = wl.config(args.config, **kw)
+    print(f"[bench] building workload {cfg.name}", file=sys.stderr, flush=True)
+    mats, keep, attn = build_workload(cfg, dev)
+    hp = mc.hparams(**{**cfg.hparams, "tau": cfg.tau})
+    H = cfg.attn.H if cfg.attn else 1
+    s_max = torch.empty(H, dtype=torch.float32, device=dev)
+    gamma = torch.empty(H, dtype=torch.float32, device=dev)
+    ws = torch.empty(mc.workspace_size(mats, hp), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        if attn is not None:
+            q, k, ks = attn
+            mc.max_logits_per_head(q, k, ks, causal=cfg.attn.causal, out=s_max)
+            mc.muonclip_step(mats, hp, s_max=s_max, slots=1, heads=H, gamma_out=gamma, workspace=ws)
+        else:
+            mc.muonclip_step(mats, hp, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel HIP events around every launch of the library (same stream)
+    mc.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof = mc.profile_read()
+    mc.profile_enable(False)
+    per_step = {k: {"ms": v["ms"] / args.steps, "launches": v["launches"] // args.steps} for k, v in prof.items()}
+    g = prof.get("ns_gemm", {"ms": float("nan"), "flops": 0.0, "launches": 1})
+    gemm_tflops = g["flops"] / (g["ms"] * 1e-3) / 1e12 if g["ms"] else float("nan")
+    ml = prof.get("max_logits")
+    n_logits = 0
+    if cfg.attn is not None:
+        a = cfg.attn
+        n_logits = a.B * a.H * (a.T * (a.T + 1) // 2 if a.causal else a.T * a.T)
+    smax_glogits = (n_logits * args.steps / (ml["ms"] * 1e-3) / 1e9) if ml and ml["ms"] else None
+    ew_bytes = sum(prof[k]["bytes"] for k in ("momentum_norm", "update_clip") if k in prof)
+    ew_ms = sum(prof[k]["ms"] for k in ("momentum_norm", "update_clip") if k in prof)
+    ew_gbs = ew_bytes / (ew_ms * 1e-3) / 1e9 if ew_ms else None
+    ns_total = sum(ns_flops(s.rows, s.cols, hp.ns_steps) for s in cfg.matrices)
+    ns_ms = sum(prof[k]["ms"] for k in ("ns_gemm", "splitk_reduce", "norm_finalize") if k in prof) / args.steps
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on a host sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, args.cpu_sample_s)
+    out = {
+        "metric": METRIC,
+        "value": round(ms, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "config": args.config, "matrices": len(cfg.matrices),
+                   "elements": wl.elements(cfg),
+                   "attention": None if cfg.attn is None else
+                   f"B{cfg.attn.B} T{cfg.attn.T} H{cfg.attn.H} d{cfg.attn.d_q} "
+                   f"{'causal' if cfg.attn.causal else 'full'} {cfg.attn.kind}",
+                   "parallelism": "single GPU"},
+        "ns_tflops_algorithmic": round(ns_total / (ns_ms * 1e-3) / 1e12, 2) if ns_ms else None,
+        "ns_gemm_tflops": round(gemm_tflops, 2),
+        "ns_mfma_frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+        "smax_glogits_s": round(smax_glogits, 1) if smax_glogits else None,
+        "elementwise_gbs": round(ew_gbs, 1) if ew_gbs else None,
+        "kernels_ms_per_step": {k: round(v["ms"], 4) for k, v in per_step.items()},
+        "roofline": {"bound": "mfma", "kernel": "ns_gemm", "achieved": round(gemm_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "launches_per_step": per_step.get("ns_gemm", {}).get("launches"),
+                     "avg_launch_us": round(g["ms"] / max(1, g["launches"]) * 1e3, 2)},
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+    del keep
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,264 @@
+// HBM-bound kernels of the MuonClip step (gfx950).
+//
+//  momentum_kernel   M <- mu M + G (Notes on Moonlight, "Background"), the
+//                    per-block sum of squares of the new M for its Frobenius
+//                    norm, and the bf16 copy of M in both orientations that the
+//                    Newton-Schulz GEMMs read (Notes on Muon blog, "Algorithm":
+//                    bf16 copy, normalisation, transpose when rows > cols). The
+//                    1/(||M||+eps) scale is not applied here; the first GEMM
+//                    epilogues fold it in.
+//  norm_finalize     fixed-order fp64 sum of the partials -> scale per matrix.
+//  update_kernel     W <- s_row ((1 - lr wd) W - lr 0.2 sqrt(max(r,c)) O): the
+//                    RMS-matched, decoupled-decay update (Notes on Moonlight,
+//                    "Scaling up Muon"), with the post-update QK-Clip row scale
+//                    s_row = gamma_h^expo (Kimi K2 essay, MHA equations and the
+//                    MLA table; gamma_h = min(1, tau / S_max^h)) fused in.
+//  gamma_kernel      gamma_h for every (layer, head).
+//  clip_apply_kernel the QK-Clip rescale alone on an existing weight.
+//
+// Tiles are 64x64 elements per 256-thread block; each thread moves 4
+// consecutive elements per row (128-bit fp32 / 64-bit bf16 accesses) when the
+// row stride and base allow, scalar accesses otherwise.
+#include "mc_internal.h"
+
+namespace mc {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ inline float gamma_of(float s, float tau) {
+  // 1 when S is not > 0 (covers S <= 0 and NaN); tau/inf = 0 zeroes the head
+  return s > 0.0f ? fminf(1.0f, tau / s) : 1.0f;
+}
+
+__device__ inline float row_clip_scale(const ClipRule& c, int row, const float* s_max, int heads, float tau) {
+  if (c.slot < 0 || !s_max || c.nseg == 0) return 1.0f;
+  const int h = row / c.period, o = row - h * c.period;
+  float expo = 0.0f;
+  if (c.nseg > 0 && o >= c.off[0] && o < c.off[0] + c.len[0]) expo = c.expo[0];
+  else if (c.nseg > 1 && o >= c.off[1] && o < c.off[1] + c.len[1]) expo = c.expo[1];
+  if (expo == 0.0f) return 1.0f;
+  const float g = gamma_of(s_max[c.slot * heads + h], tau);
+  if (expo == 0.5f) return sqrtf(g);
+  if (expo == 1.0f) return g;
+  return powf(g, expo);
+}
+
+template <typename M>
+__device__ inline int find_mat(const M* mats, int nmat, int blk) {
+  int j = 0;
+  for (int t = 1; t < nmat; ++t)
+    if (blk >= mats[t].block_start) j = t;
+  return j;
+}
+
+// ---------------------------------------------------------------- momentum
+
+__global__ void __launch_bounds__(256) momentum_kernel(const MomArgs a) {
+  __shared__ uint16_t tile[64][66];
+  __shared__ float red[4];
+  const int j = find_mat(a.mat, a.nmat, blockIdx.x);
+  const MomMat& mm = a.mat[j];
+  const int local = blockIdx.x - mm.block_start;
+  const int tr = local / mm.tiles_c, tc = local - tr * mm.tiles_c;
+  const int tid = threadIdx.x, cx = tid & 15, ry = tid >> 4;
+  const int col = tc * 64 + cx * 4;
+  float ss = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int lr = ry + 16 * k, row = tr * 64 + lr;
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (row < mm.rows) {
+      const int64_t base = (int64_t)row * mm.ld + col;
+      if (mm.vec && col < mm.cols) {
+        f32x4_t mv = *(const f32x4_t*)(mm.m + base);
+        f32x4_t gv;
+        if (mm.g_bf16) {
+          const u16x4_t gb = *(const u16x4_t*)((const uint16_t*)mm.g + base);
+          gv = f32x4_t{bf16_to_f32(gb[0]), bf16_to_f32(gb[1]), bf16_to_f32(gb[2]), bf16_to_f32(gb[3])};
+        } else {
+          gv = *(const f32x4_t*)((const float*)mm.g + base);
+        }
+        f32x4_t nv;
+        nv[0] = fmaf(a.mu, mv[0], gv[0]); nv[1] = fmaf(a.mu, mv[1], gv[1]);
+        nv[2] = fmaf(a.mu, mv[2], gv[2]); nv[3] = fmaf(a.mu, mv[3], gv[3]);
+        *(f32x4_t*)(mm.m + base) = nv;
+        v[0] = nv[0]; v[1] = nv[1]; v[2] = nv[2]; v[3] = nv[3];
+      } else if (!mm.vec) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (col + e < mm.cols) {
+            const float g = mm.g_bf16 ? bf16_to_f32(((const uint16_t*)mm.g)[base + e]) : ((const float*)mm.g)[base + e];
+            const float n = fmaf(a.mu, mm.m[base + e], g);
+            mm.m[base + e] = n;
+            v[e] = n;
+          }
+        }
+      }
+    }
+    u16x4_t h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ss = fmaf(v[e], v[e], ss);
+      h[e] = f32_to_bf16(v[e]);
+      tile[lr][cx * 4 + e] = h[e];
+    }
+    // stored orientation (zeros in the padding)
+    *(u16x4_t*)(mm.x_orig + (int64_t)row * mm.ld_orig + col) = h;
+  }
+  // block sum of squares (fixed order)
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  if (tid == 0) mm.partial[local] = (red[0] + red[1]) + (red[2] + red[3]);
+  // transposed orientation: output row tc*64 + jj, 16 consecutive elements
+  const int jj = tid >> 2, i0 = (tid & 3) * 16;
+  uint16_t o[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) o[e] = tile[i0 + e][jj];
+  u32x4_t w0, w1;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    w0[e] = (uint32_t)o[2 * e] | ((uint32_t)o[2 * e + 1] << 16);
+    w1[e] = (uint32_t)o[8 + 2 * e] | ((uint32_t)o[8 + 2 * e + 1] << 16);
+  }
+  uint16_t* dst = mm.x_tr + (int64_t)(tc * 64 + jj) * mm.ld_tr + tr * 64 + i0;
+  *(u32x4_t*)dst = w0;
+  *(u32x4_t*)(dst + 8) = w1;
+}
+
+hipError_t launch_momentum(const MomArgs& a, hipStream_t s) {
+  if (a.total_blocks <= 0) return hipSuccess;
+  momentum_kernel<<<a.total_blocks, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) norm_finalize_kernel(const float* partial, int parts, int64_t stride,
+                                                            float* scale, float eps) {
+  __shared__ double red[256];
+  const float* p = partial + (int64_t)blockIdx.x * stride;
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < parts; i += 256) acc += (double)p[i];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) scale[blockIdx.x] = (float)(1.0 / (sqrt(red[0]) + (double)eps));
+}
+
+hipError_t launch_norm_finalize(const float* partial, int32_t parts, int64_t stride, float* scale,
+                                int32_t nmat, float eps, hipStream_t s) {
+  if (nmat <= 0) return hipSuccess;
+  norm_finalize_kernel<<<nmat, 256, 0, s>>>(partial, parts, stride, scale, eps);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- update
+
+__global__ void __launch_bounds__(256) update_kernel(const UpdArgs a) {
+  const int j = find_mat(a.mat, a.nmat, blockIdx.x);
+  const UpdMat& u = a.mat[j];
+  const int local = blockIdx.x - u.block_start;
+  const int tr = local / u.tiles_c, tc = local - tr * u.tiles_c;
+  const int tid = threadIdx.x, cx = tid & 15, ry = tid >> 4;
+  const int col = tc * 64 + cx * 4;
+  if (col >= u.cols) return;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int row = tr * 64 + ry + 16 * k;
+    if (row >= u.rows) break;
+    const float sc = row_clip_scale(u.clip, row, a.s_max, a.heads, a.tau);
+    const int64_t wb = (int64_t)row * u.ld + col;
+    const uint16_t* op = u.o + (int64_t)row * u.ld_o + col;
+    if (u.vec) {
+      const u16x4_t ov = *(const u16x4_t*)op;
+      float o[4] = {bf16_to_f32(ov[0]), bf16_to_f32(ov[1]), bf16_to_f32(ov[2]), bf16_to_f32(ov[3])};
+      if (u.o_out) *(u16x4_t*)(u.o_out + (int64_t)row * u.cols + col) = ov;
+      if (u.w_bf16) {
+        uint16_t* wp = (uint16_t*)u.w + wb;
+        const u16x4_t wv = *(const u16x4_t*)wp;
+        u16x4_t r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          r[e] = f32_to_bf16(fmaf(-u.lr_rms, o[e], bf16_to_f32(wv[e]) * a.decay) * sc);
+        *(u16x4_t*)wp = r;
+      } else {
+        float* wp = (float*)u.w + wb;
+        const f32x4_t wv = *(const f32x4_t*)wp;
+        f32x4_t r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = fmaf(-u.lr_rms, o[e], wv[e] * a.decay) * sc;
+        *(f32x4_t*)wp = r;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (col + e >= u.cols) break;
+        const uint16_t ob = op[e];
+        const float o = bf16_to_f32(ob);
+        if (u.o_out) u.o_out[(int64_t)row * u.cols + col + e] = ob;
+        if (u.w_bf16) {
+          uint16_t* wp = (uint16_t*)u.w + wb + e;
+          *wp = f32_to_bf16(fmaf(-u.lr_rms, o, bf16_to_f32(*wp) * a.decay) * sc);
+        } else {
+          float* wp = (float*)u.w + wb + e;
+          *wp = fmaf(-u.lr_rms, o, *wp * a.decay) * sc;
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_update(const UpdArgs& a, hipStream_t s) {
+  if (a.total_blocks <= 0) return hipSuccess;
+  update_kernel<<<a.total_blocks, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- gamma / clip
+
+__global__ void gamma_kernel(const float* s_max, float* gamma, int n, float tau) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) gamma[i] = gamma_of(s_max[i], tau);
+}
+
+hipError_t launch_gamma(const float* s_max, float* gamma, int32_t n, float tau, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  gamma_kernel<<<(n + 255) / 256, 256, 0, s>>>(s_max, gamma, n, tau);
+  return hipGetLastError();
+}
+
+// grid.x: 1024-column chunks, grid.y strides over rows. Rows whose scale is
+// exactly 1 are skipped before touching memory, so gamma = 1 heads stay
+// bit-identical.
+__global__ void __launch_bounds__(256) clip_apply_kernel(const ClipApplyArgs a) {
+  for (int row = blockIdx.y; row < a.rows; row += gridDim.y) {
+    const float sc = row_clip_scale(a.clip, row, a.s_max, a.heads, a.tau);
+    if (sc == 1.0f) continue;
+    const int c0 = blockIdx.x * 1024 + threadIdx.x;
+    for (int e = 0; e < 4; ++e) {
+      const int col = c0 + e * 256;
+      if (col >= a.cols) break;
+      const int64_t i = (int64_t)row * a.ld + col;
+      if (a.w_bf16) {
+        uint16_t* w = (uint16_t*)a.w;
+        w[i] = f32_to_bf16(bf16_to_f32(w[i]) * sc);
+      } else {
+        float* w = (float*)a.w;
+        w[i] = w[i] * sc;
+      }
+    }
+  }
+}
+
+hipError_t launch_clip_apply(const ClipApplyArgs& a, hipStream_t s) {
+  if (a.rows <= 0 || a.cols <= 0) return hipSuccess;
+  dim3 grid((a.cols + 1023) / 1024, a.rows < 32768 ? a.rows : 32768);
+  clip_apply_kernel<<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace mc

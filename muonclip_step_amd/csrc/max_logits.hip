@@ -1,0 +1,248 @@
+// Per-head max attention logit S_max^h = (1/sqrt(d)) max over the batch and
+// over query/key pairs of Q_i^h . K_j^h (Kimi K2 essay, section on Muon and
+// attention logits, S_max equation; K2 report 2.1). The logits are never
+// written to memory.
+//
+// MFMA kernel (bf16): a 256-thread block owns 256 query rows of one (head,
+// sample); each wave keeps its 64 query rows as MFMA A-fragments in registers
+// for the whole kernel and streams 64-key tiles of K through double-buffered,
+// XOR-swizzled LDS. Each 32x32x16 bf16 MFMA (fp32 accumulate) yields a 32x32
+// logit tile that is folded straight into a per-lane running max; only tiles
+// on the causal diagonal or the ragged end apply a mask, and a wave skips key
+// tiles lying wholly above its causal diagonal. Blocks are issued heaviest
+// causal row first. The block max goes through an order-preserving integer
+// encoding into one atomicMax per block, so the result does not depend on
+// scheduling. MLA keys are [k^C_h | k^R]: the shared rotary key supplies the
+// last d_s dimensions of every head's key (K2 report, per-head MLA clipping).
+//
+// The generic kernel (fp32 inputs, or shapes the MFMA kernel does not cover)
+// computes the same definition with one fp32 dot product per pair.
+#include <math.h>
+
+#include "mc_internal.h"
+
+namespace mc {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ inline uint32_t order_enc(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline float order_dec(uint32_t k) {
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __builtin_bit_cast(float, u);
+}
+
+__device__ inline void block_max_commit(float mx, uint32_t* out, float* red) {
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = red[0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, red[w]);
+    atomicMax(out, order_enc(m));
+  }
+}
+
+template <int DK, int DS>
+__global__ void __launch_bounds__(256, 1) max_logits_mfma_kernel(const MaxLogitArgs a) {
+  constexpr int D = DK + DS, DC = D / 8, KS = D / 16;
+  constexpr int BQ = 256, BKV = 64;
+  constexpr int PT = BKV * DC / 256;              // 16-byte chunks per thread per key tile
+  static_assert((BKV * DC) % 256 == 0 && (DC % 8) == 0, "tile shape");
+  __shared__ u32x4_t kt[2][BKV * DC];
+  __shared__ float red[4];
+
+  const int HB = a.H * a.B;
+  const int nqt = (a.T + BQ - 1) / BQ;
+  const int hb = blockIdx.x % HB;
+  const int qt = nqt - 1 - (int)(blockIdx.x / HB);   // heaviest causal rows first
+  const int h = hb % a.H, b = hb / a.H;
+  const int q0 = qt * BQ;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr0 = q0 + wave * 64;
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+
+  const uint16_t* Q = (const uint16_t*)a.q + (int64_t)b * a.qs_b + (int64_t)h * a.qs_h;
+  const uint16_t* K = (const uint16_t*)a.k + (int64_t)b * a.ks_b + (int64_t)h * a.ks_h;
+  const uint16_t* KS_ = DS > 0 ? (const uint16_t*)a.ks + (int64_t)b * a.kss_b : nullptr;
+
+  // this wave's query rows as A-fragments: lane l holds row l%32, k-chunk l/32
+  bf16x8_t qf[2][KS];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int row = wr0 + 32 * f + (lane & 31);
+    const int rr = row < a.T ? row : a.T - 1;
+    const uint16_t* base = Q + (int64_t)rr * a.qs_t + 8 * (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const u32x4_t v = *(const u32x4_t*)(base + 16 * s);
+      qf[f][s] = __builtin_bit_cast(bf16x8_t, row < a.T ? v : zero);
+    }
+  }
+
+  const int kend = a.causal ? min(a.T, q0 + BQ) : a.T;
+  const int nkv = (kend + BKV - 1) / BKV;
+  float mx = -INFINITY;
+  u32x4_t st[PT];
+
+#define ML_GLOAD(it_)                                                                  \
+  {                                                                                    \
+    const int kv0_ = (it_) * BKV;                                                      \
+    _Pragma("unroll") for (int i = 0; i < PT; ++i) {                                   \
+      const int q = tid + i * 256, r = q / DC, c = q - r * DC;                         \
+      const int key = kv0_ + r, kr = key < a.T ? key : a.T - 1;                        \
+      const uint16_t* src = (DS == 0 || c < DK / 8)                                    \
+                                ? K + (int64_t)kr * a.ks_t + c * 8                     \
+                                : KS_ + (int64_t)kr * a.kss_t + (c - DK / 8) * 8;      \
+      const u32x4_t v = *(const u32x4_t*)src;                                          \
+      st[i] = key < a.T ? v : zero;                                                    \
+    }                                                                                  \
+  }
+#define ML_LSTORE(buf_)                                                                \
+  {                                                                                    \
+    _Pragma("unroll") for (int i = 0; i < PT; ++i) {                                   \
+      const int q = tid + i * 256, r = q / DC, c = q - r * DC;                         \
+      kt[(buf_)][r * DC + (c ^ (r & 7))] = st[i];                                      \
+    }                                                                                  \
+  }
+
+  if (nkv > 0) {
+    ML_GLOAD(0);
+    ML_LSTORE(0);
+    __syncthreads();
+  }
+  for (int it = 0; it < nkv; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < nkv) ML_GLOAD(it + 1);
+    const int kv0 = it * BKV;
+    if (!(a.causal && kv0 > wr0 + 63) && wr0 < a.T) {
+      const bool need_mask = (a.causal && kv0 + BKV - 1 > wr0) || (kv0 + BKV > a.T) || (wr0 + 63 >= a.T);
+#pragma unroll
+      for (int fk = 0; fk < 2; ++fk) {
+        f32x16_t acc0 = f32x16_t{}, acc1 = f32x16_t{};
+        const int r = fk * 32 + (lane & 31);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const int c = 2 * s + (lane >> 5);
+          const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, kt[cur][r * DC + (c ^ (r & 7))]);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf, acc1, 0, 0, 0);
+        }
+        if (!need_mask) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(acc0[e], acc1[e]));
+        } else {
+          // register e of lane l: query row 8*(e/4) + 4*(l/32) + e%4, key column l%32
+          const int j = kv0 + fk * 32 + (lane & 31);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int i0 = wr0 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            const int i1 = i0 + 32;
+            const bool ok0 = i0 < a.T && j < a.T && (!a.causal || j <= i0);
+            const bool ok1 = i1 < a.T && j < a.T && (!a.causal || j <= i1);
+            if (ok0) mx = fmaxf(mx, acc0[e]);
+            if (ok1) mx = fmaxf(mx, acc1[e]);
+          }
+        }
+      }
+    }
+    if (it + 1 < nkv) ML_LSTORE(cur ^ 1);
+    __syncthreads();
+  }
+#undef ML_GLOAD
+#undef ML_LSTORE
+  block_max_commit(mx, a.out_enc + h, red);
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(256) max_logits_generic_kernel(const MaxLogitArgs a) {
+  __shared__ float red[4];
+  const int h = blockIdx.x % a.H, b = blockIdx.x / a.H;
+  float mx = -INFINITY;
+  const int64_t pairs = (int64_t)a.T * a.T;
+  for (int64_t p = threadIdx.x; p < pairs; p += 256) {
+    const int i = (int)(p / a.T), j = (int)(p - (int64_t)i * a.T);
+    if (a.causal && j > i) continue;
+    const int64_t qo = (int64_t)b * a.qs_b + (int64_t)i * a.qs_t + (int64_t)h * a.qs_h;
+    const int64_t ko = (int64_t)b * a.ks_b + (int64_t)j * a.ks_t + (int64_t)h * a.ks_h;
+    const int64_t so = (int64_t)b * a.kss_b + (int64_t)j * a.kss_t;
+    float dot = 0.0f;
+    if (BF16) {
+      const uint16_t* q = (const uint16_t*)a.q;
+      const uint16_t* k = (const uint16_t*)a.k;
+      const uint16_t* ks = (const uint16_t*)a.ks;
+      for (int f = 0; f < a.d_k; ++f) dot = fmaf(bf16_to_f32(q[qo + f]), bf16_to_f32(k[ko + f]), dot);
+      for (int f = 0; f < a.d_s; ++f) dot = fmaf(bf16_to_f32(q[qo + a.d_k + f]), bf16_to_f32(ks[so + f]), dot);
+    } else {
+      const float* q = (const float*)a.q;
+      const float* k = (const float*)a.k;
+      const float* ks = (const float*)a.ks;
+      for (int f = 0; f < a.d_k; ++f) dot = fmaf(q[qo + f], k[ko + f], dot);
+      for (int f = 0; f < a.d_s; ++f) dot = fmaf(q[qo + a.d_k + f], ks[so + f], dot);
+    }
+    mx = fmaxf(mx, dot);
+  }
+  block_max_commit(mx, a.out_enc + h, red);
+}
+
+__global__ void max_logits_init_kernel(uint32_t* enc, int H) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < H) enc[i] = order_enc(-INFINITY);
+}
+
+__global__ void max_logits_finalize_kernel(uint32_t* enc, float scale, int H) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < H) {
+    const float m = order_dec(enc[i]);
+    reinterpret_cast<float*>(enc)[i] = m * scale;
+  }
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool max_logits_mfma_supported(const MaxLogitArgs& a) {
+  if (!a.bf16) return false;
+  const bool shape = (a.d_k == 128 && (a.d_s == 0 || a.d_s == 64)) || (a.d_k == 64 && a.d_s == 0);
+  if (!shape) return false;
+  if (!aligned16(a.q) || !aligned16(a.k) || (a.d_s && !aligned16(a.ks))) return false;
+  if ((a.qs_b | a.qs_t | a.qs_h | a.ks_b | a.ks_t | a.ks_h) & 7) return false;
+  if (a.d_s && ((a.kss_b | a.kss_t) & 7)) return false;
+  return true;
+}
+
+hipError_t launch_max_logits_init(uint32_t* enc, int32_t H, hipStream_t s) {
+  if (H <= 0) return hipSuccess;
+  max_logits_init_kernel<<<(H + 255) / 256, 256, 0, s>>>(enc, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_max_logits(const MaxLogitArgs& a, hipStream_t s, bool* used_mfma) {
+  *used_mfma = false;
+  if (a.B <= 0 || a.T <= 0 || a.H <= 0) return hipSuccess;
+  if (max_logits_mfma_supported(a)) {
+    *used_mfma = true;
+    const int nqt = (a.T + 255) / 256;
+    const int grid = nqt * a.H * a.B;
+    if (a.d_k == 128 && a.d_s == 64) max_logits_mfma_kernel<128, 64><<<grid, 256, 0, s>>>(a);
+    else if (a.d_k == 128) max_logits_mfma_kernel<128, 0><<<grid, 256, 0, s>>>(a);
+    else max_logits_mfma_kernel<64, 0><<<grid, 256, 0, s>>>(a);
+  } else if (a.bf16) {
+    max_logits_generic_kernel<true><<<a.H * a.B, 256, 0, s>>>(a);
+  } else {
+    max_logits_generic_kernel<false><<<a.H * a.B, 256, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_max_logits_finalize(uint32_t* enc, float scale, int32_t H, hipStream_t s) {
+  if (H <= 0) return hipSuccess;
+  max_logits_finalize_kernel<<<(H + 255) / 256, 256, 0, s>>>(enc, scale, H);
+  return hipGetLastError();
+}
+
+}  // namespace mc

@@ -1,0 +1,633 @@
+// Host dispatcher and C ABI of the MuonClip library (see include/muonclip.h).
+//
+// muonclip_step: matrices are grouped by (m, n) = (min, max) of their shape;
+// each group runs in waves of as many matrices as the workspace holds. Per
+// wave, on the caller's stream:
+//   momentum_kernel   M <- mu M + G, norm partials, bf16 X0 in both layouts
+//   norm_finalize     s = 1 / (||M||_F + eps)
+//   5 x { Gram  A = s0^2 X X^T          -> A (fp32), A_hi (+ A_lo if m < 1024)
+//         Poly  P = a I + b A + c A A   -> P_hi (+ P_lo if m < 1024)
+//         Apply X' = s0 P X             -> X', X'^T  (last step: O) }
+//   update_kernel     W <- clip_row ((1 - lr wd) W - lr rms sqrt(max) O)
+// (s0 = s on the first step, 1 after). The apply is the quintic step of the
+// Notes on Muon blog, "Newton-Schulz", written as X' = (aI + bA + cA^2) X.
+// Operands are bf16, accumulation and every epilogue fp32; for m < 1024 the
+// Gram matrix and the polynomial enter their products as hi + lo bf16 pairs
+// (3 and 2 MFMA passes), which keeps those small-m shapes well inside the
+// 2e-2 relative Frobenius bound.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/muonclip.h"
+#include "mc_internal.h"
+
+using namespace mc;
+
+namespace {
+
+thread_local std::string g_err;
+
+mc_status fail(mc_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+inline int64_t round64(int64_t x) { return (x + 63) / 64 * 64; }
+constexpr int kWaveCap = 64;
+constexpr int kCUs = 256;
+constexpr int kSplitThreshold = 1024;   // m below this: hi/lo operand pairs
+
+// ---------------------------------------------------------------- profiling
+
+enum Family {
+  F_MOMENTUM = 0, F_NORM, F_GEMM, F_SPLITK, F_UPDATE, F_GAMMA, F_CLIP,
+  F_ML_INIT, F_ML, F_ML_FIN, F_COUNT
+};
+const char* kFamilyNames[F_COUNT] = {"momentum_norm", "norm_finalize", "ns_gemm", "splitk_reduce",
+                                     "update_clip", "gamma", "clip_apply", "max_logits_init",
+                                     "max_logits", "max_logits_finalize"};
+
+struct ProfRec { int fam; hipEvent_t a, b; double flops, bytes; };
+std::mutex g_prof_mu;
+bool g_prof = false;
+std::vector<ProfRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+size_t g_pool_used = 0;
+
+hipEvent_t pool_event() {
+  if (g_pool_used == g_pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    g_pool.push_back(e);
+  }
+  return g_pool[g_pool_used++];
+}
+
+struct Prof {
+  int fam; hipStream_t s; double flops, bytes; hipEvent_t a = nullptr, b = nullptr;
+  Prof(int f, hipStream_t st, double fl, double by) : fam(f), s(st), flops(fl), bytes(by) {
+    if (!g_prof) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    a = pool_event(); b = pool_event();
+    if (a) (void)hipEventRecord(a, s);
+  }
+  ~Prof() {
+    if (!a || !b) return;
+    (void)hipEventRecord(b, s);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_recs.push_back({fam, a, b, flops, bytes});
+  }
+};
+
+// ---------------------------------------------------------------- validation
+
+bool dtype_ok(int32_t d) { return d == MC_F32 || d == MC_BF16; }
+size_t dtype_size(int32_t d) { return d == MC_F32 ? 4 : 2; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+mc_status check_hparams(const mc_hparams* hp) {
+  if (!hp) return fail(MC_ERR_NULL, "hparams is NULL");
+  const float v[] = {hp->lr, hp->mu, hp->weight_decay, hp->rms_scale, hp->tau,
+                     hp->ns_a, hp->ns_b, hp->ns_c, hp->ns_eps};
+  for (float x : v)
+    if (!isfinite(x)) return fail(MC_ERR_HPARAM, "hyper-parameters must be finite");
+  if (hp->ns_steps < 1 || hp->ns_steps > 16) return fail(MC_ERR_HPARAM, "ns_steps must be in 1..16 (got %d)", hp->ns_steps);
+  if (hp->ns_eps < 0.0f) return fail(MC_ERR_HPARAM, "ns_eps must be >= 0");
+  if (hp->tau <= 0.0f) return fail(MC_ERR_HPARAM, "tau must be > 0");
+  return MC_OK;
+}
+
+mc_status check_clip(const mc_matrix& m, int i, int32_t slots, int32_t heads, bool need_slots) {
+  if (m.clip_slot < 0) return MC_OK;
+  if (need_slots && m.clip_slot >= slots)
+    return fail(MC_ERR_SHAPE, "matrix %d: clip_slot %d >= slots %d", i, m.clip_slot, slots);
+  if (m.period <= 0 || m.rows % m.period != 0)
+    return fail(MC_ERR_SHAPE, "matrix %d: rows %lld not a multiple of period %d", i, (long long)m.rows, m.period);
+  if (need_slots && m.rows / m.period > heads)
+    return fail(MC_ERR_SHAPE, "matrix %d: %lld head blocks > heads %d", i, (long long)(m.rows / m.period), heads);
+  if (m.nseg < 0 || m.nseg > 2) return fail(MC_ERR_SHAPE, "matrix %d: nseg must be 0..2", i);
+  for (int s = 0; s < m.nseg; ++s) {
+    const mc_segment& g = m.seg[s];
+    if (g.offset < 0 || g.length <= 0 || g.offset + g.length > m.period)
+      return fail(MC_ERR_SHAPE, "matrix %d: segment %d outside the head period", i, s);
+    if (!(g.expo > 0.0f) || !isfinite(g.expo)) return fail(MC_ERR_HPARAM, "matrix %d: segment expo must be > 0", i);
+  }
+  if (m.nseg == 2) {
+    const mc_segment &a = m.seg[0], &b = m.seg[1];
+    if (a.offset < b.offset + b.length && b.offset < a.offset + a.length)
+      return fail(MC_ERR_SHAPE, "matrix %d: segments overlap", i);
+  }
+  return MC_OK;
+}
+
+mc_status check_matrix_common(const mc_matrix& m, int i) {
+  if (!m.w) return fail(MC_ERR_NULL, "matrix %d: w is NULL", i);
+  if (m.rows <= 0 || m.cols <= 0) return fail(MC_ERR_SHAPE, "matrix %d: rows and cols must be >= 1", i);
+  if (m.rows > (1 << 20) || m.cols > (1 << 20)) return fail(MC_ERR_SHAPE, "matrix %d: dimension above 2^20", i);
+  if (m.ld < m.cols) return fail(MC_ERR_SHAPE, "matrix %d: ld %lld < cols %lld", i, (long long)m.ld, (long long)m.cols);
+  if (!dtype_ok(m.w_dtype)) return fail(MC_ERR_DTYPE, "matrix %d: w_dtype %d", i, m.w_dtype);
+  if (!aligned(m.w, dtype_size(m.w_dtype))) return fail(MC_ERR_ALIGN, "matrix %d: w misaligned", i);
+  return MC_OK;
+}
+
+mc_status check_matrices_step(const mc_matrix* mats, int32_t n, int32_t slots, int32_t heads, bool have_smax) {
+  if (n < 0) return fail(MC_ERR_SHAPE, "n < 0");
+  if (n > 0 && !mats) return fail(MC_ERR_NULL, "mats is NULL");
+  for (int i = 0; i < n; ++i) {
+    const mc_matrix& m = mats[i];
+    mc_status st = check_matrix_common(m, i);
+    if (st) return st;
+    if (!m.g || !m.m) return fail(MC_ERR_NULL, "matrix %d: g or m is NULL", i);
+    if (!dtype_ok(m.g_dtype)) return fail(MC_ERR_DTYPE, "matrix %d: g_dtype %d", i, m.g_dtype);
+    if (!aligned(m.g, dtype_size(m.g_dtype)) || !aligned(m.m, 4)) return fail(MC_ERR_ALIGN, "matrix %d: g or m misaligned", i);
+    if (m.o_out && !aligned(m.o_out, 2)) return fail(MC_ERR_ALIGN, "matrix %d: o_out misaligned", i);
+    if (have_smax) { st = check_clip(m, i, slots, heads, true); if (st) return st; }
+    else if (m.clip_slot >= 0) { st = check_clip(m, i, 0, 0, false); if (st) return st; }
+  }
+  return MC_OK;
+}
+
+// ---------------------------------------------------------------- planning
+
+struct Group {
+  int64_t m, n, mp, np;
+  bool split;
+  std::vector<int> idx;
+};
+
+std::vector<Group> make_groups(const mc_matrix* mats, int32_t n) {
+  std::vector<Group> gs;
+  std::map<std::pair<int64_t, int64_t>, size_t> where;
+  for (int i = 0; i < n; ++i) {
+    const int64_t m = std::min(mats[i].rows, mats[i].cols), nn = std::max(mats[i].rows, mats[i].cols);
+    auto key = std::make_pair(m, nn);
+    auto it = where.find(key);
+    if (it == where.end()) {
+      Group g;
+      g.m = m; g.n = nn; g.mp = round64(m); g.np = round64(nn);
+      g.split = m < kSplitThreshold;
+      where[key] = gs.size();
+      gs.push_back(g);
+      it = where.find(key);
+    }
+    gs[it->second].idx.push_back(i);
+  }
+  return gs;
+}
+
+struct GemmPlan { GemmTile tile; int tiles_m, tiles_n, splits, kt_per_split; size_t partial_bytes; };
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int ktiles, int batch) {
+  GemmPlan p{};
+  auto tiles_for = [&](int d) { return (int)(((M + d - 1) / d) * ((N + d - 1) / d)) * batch; };
+  if (M >= 256 && N >= 256 && tiles_for(256) >= kCUs) p.tile = TILE_256;
+  else if (M >= 128 && N >= 128) p.tile = TILE_128;
+  else p.tile = TILE_64;
+  const int d = gemm_tile_dim(p.tile);
+  p.tiles_m = (int)((M + d - 1) / d);
+  p.tiles_n = (int)((N + d - 1) / d);
+  const int tiles = p.tiles_m * p.tiles_n * batch;
+  int splits = 1;
+  if (tiles < kCUs && ktiles >= 8) {
+    splits = std::min((2 * kCUs + tiles - 1) / tiles, ktiles / 4);
+    splits = std::max(splits, 1);
+  }
+  p.kt_per_split = (ktiles + splits - 1) / splits;
+  p.splits = (ktiles + p.kt_per_split - 1) / p.kt_per_split;
+  p.partial_bytes = p.splits > 1 ? (size_t)p.splits * batch * M * N * 4 : 0;
+  return p;
+}
+
+struct WavePlan {
+  int nb;
+  size_t off_x, off_xt0, off_xt1, off_a32, off_ahi, off_alo, off_phi, off_plo, off_part, off_scale, off_splitk;
+  size_t bytes;
+  int64_t mom_blocks;          // momentum blocks per matrix
+  GemmPlan gram, poly, apply;
+  int kt_gram, kt_poly, kt_apply;
+};
+
+WavePlan plan_wave(const Group& g, int nb) {
+  WavePlan w{};
+  w.nb = nb;
+  const size_t mp = (size_t)g.mp, np = (size_t)g.np;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  w.off_x = take(nb * mp * np * 2);
+  w.off_xt0 = take(nb * np * mp * 2);
+  w.off_xt1 = take(nb * np * mp * 2);
+  w.off_a32 = take(nb * mp * mp * 4);
+  w.off_ahi = take(nb * mp * mp * 2);
+  w.off_alo = g.split ? take(nb * mp * mp * 2) : 0;
+  w.off_phi = take(nb * mp * mp * 2);
+  w.off_plo = g.split ? take(nb * mp * mp * 2) : 0;
+  w.mom_blocks = (int64_t)(mp / 64) * (int64_t)(np / 64);
+  w.off_part = take(nb * (size_t)w.mom_blocks * 4);
+  w.off_scale = take(nb * 4);
+  w.kt_gram = (int)(np / 64);
+  w.kt_poly = (int)(mp / 64) * (g.split ? 3 : 1);
+  w.kt_apply = (int)(mp / 64) * (g.split ? 2 : 1);
+  w.gram = plan_gemm(g.mp, g.mp, w.kt_gram, nb);
+  w.poly = plan_gemm(g.mp, g.mp, w.kt_poly, nb);
+  w.apply = plan_gemm(g.mp, g.np, w.kt_apply, nb);
+  const size_t sk = std::max(w.gram.partial_bytes, std::max(w.poly.partial_bytes, w.apply.partial_bytes));
+  w.off_splitk = sk ? take(sk) : 0;
+  w.bytes = off;
+  return w;
+}
+
+mc_status launch_gemm_planned(const GemmPlan& gp, GemmArgs a, hipStream_t s, void* ws_base, size_t off_splitk,
+                              double flops) {
+  a.tiles_m = gp.tiles_m; a.tiles_n = gp.tiles_n;
+  a.splits = gp.splits; a.kt_per_split = gp.kt_per_split;
+  a.partial = gp.splits > 1 ? (float*)((char*)ws_base + off_splitk) : nullptr;
+  {
+    Prof pr(F_GEMM, s, flops, 0.0);
+    hipError_t e = launch_ns_gemm(gp.tile, a, s);
+    if (e != hipSuccess) return fail(MC_ERR_HIP, "ns_gemm launch: %s", hipGetErrorString(e));
+  }
+  if (gp.splits > 1) {
+    Prof pr(F_SPLITK, s, 0.0, (double)gp.partial_bytes);
+    hipError_t e = launch_splitk_reduce(a, s);
+    if (e != hipSuccess) return fail(MC_ERR_HIP, "splitk_reduce launch: %s", hipGetErrorString(e));
+  }
+  return MC_OK;
+}
+
+ClipRule clip_rule(const mc_matrix& m, bool clip_on) {
+  ClipRule c{};
+  c.slot = clip_on ? m.clip_slot : -1;
+  c.period = m.period > 0 ? m.period : 1;
+  c.nseg = clip_on && m.clip_slot >= 0 ? m.nseg : 0;
+  for (int s = 0; s < 2; ++s) {
+    c.off[s] = s < m.nseg ? m.seg[s].offset : 0;
+    c.len[s] = s < m.nseg ? m.seg[s].length : 0;
+    c.expo[s] = s < m.nseg ? m.seg[s].expo : 0.0f;
+  }
+  return c;
+}
+
+mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb, const mc_hparams& hp,
+                   const float* s_max, int32_t heads, char* ws, hipStream_t s) {
+  const WavePlan w = plan_wave(g, nb);
+  const int64_t mp = g.mp, np = g.np;
+  uint16_t* X = (uint16_t*)(ws + w.off_x);
+  uint16_t* XT[2] = {(uint16_t*)(ws + w.off_xt0), (uint16_t*)(ws + w.off_xt1)};
+  float* A32 = (float*)(ws + w.off_a32);
+  uint16_t* Ahi = (uint16_t*)(ws + w.off_ahi);
+  uint16_t* Alo = g.split ? (uint16_t*)(ws + w.off_alo) : nullptr;
+  uint16_t* Phi = (uint16_t*)(ws + w.off_phi);
+  uint16_t* Plo = g.split ? (uint16_t*)(ws + w.off_plo) : nullptr;
+  float* part = (float*)(ws + w.off_part);
+  float* scale = (float*)(ws + w.off_scale);
+
+  // 1. momentum + norm partials + bf16 X0 in both orientations
+  for (int b0 = 0; b0 < nb; b0 += kMaxBatchMats) {
+    MomArgs a{};
+    a.mu = hp.mu;
+    int blocks = 0;
+    double bytes = 0;
+    for (int j = 0; j < kMaxBatchMats && b0 + j < nb; ++j) {
+      const int slot = b0 + j;
+      const mc_matrix& m = mats[ids[slot]];
+      const bool wide = m.rows <= m.cols;
+      MomMat& mm = a.mat[a.nmat++];
+      mm.g = m.g; mm.m = m.m; mm.ld = m.ld;
+      mm.rows = (int32_t)m.rows; mm.cols = (int32_t)m.cols;
+      mm.g_bf16 = m.g_dtype == MC_BF16;
+      mm.vec = (m.cols % 4 == 0) && (m.ld % 4 == 0) && aligned(m.m, 16) && aligned(m.g, 4 * dtype_size(m.g_dtype));
+      uint16_t* xs = X + (size_t)slot * mp * np;
+      uint16_t* xts = XT[0] + (size_t)slot * np * mp;
+      mm.x_orig = wide ? xs : xts; mm.ld_orig = (int32_t)(wide ? np : mp);
+      mm.x_tr = wide ? xts : xs;   mm.ld_tr = (int32_t)(wide ? mp : np);
+      mm.rp = (int32_t)(wide ? mp : np); mm.cp = (int32_t)(wide ? np : mp);
+      mm.tiles_c = mm.cp / 64;
+      mm.block_start = blocks;
+      mm.partial = part + (size_t)slot * w.mom_blocks;
+      blocks += (mm.rp / 64) * mm.tiles_c;
+      bytes += (double)m.rows * m.cols * (dtype_size(m.g_dtype) + 8);
+    }
+    a.total_blocks = blocks;
+    Prof pr(F_MOMENTUM, s, 0.0, bytes);
+    hipError_t e = launch_momentum(a, s);
+    if (e != hipSuccess) return fail(MC_ERR_HIP, "momentum launch: %s", hipGetErrorString(e));
+  }
+  {
+    Prof pr(F_NORM, s, 0.0, 0.0);
+    hipError_t e = launch_norm_finalize(part, (int32_t)w.mom_blocks, w.mom_blocks, scale, nb, hp.ns_eps, s);
+    if (e != hipSuccess) return fail(MC_ERR_HIP, "norm_finalize launch: %s", hipGetErrorString(e));
+  }
+
+  // 2. Newton-Schulz iterations
+  const double mm_ = (double)g.m, nn_ = (double)g.n;
+  for (int it = 0; it < hp.ns_steps; ++it) {
+    const bool first = it == 0, last = it == hp.ns_steps - 1;
+    uint16_t* xt_cur = XT[it & 1];
+    uint16_t* xt_nxt = XT[(it + 1) & 1];
+    // Gram: A = s0^2 X X^T
+    {
+      GemmArgs a{};
+      a.M = (int32_t)mp; a.N = (int32_t)mp; a.batch = nb;
+      a.lda = (int32_t)np; a.ldb = (int32_t)np; a.bsa = mp * np; a.bsb = mp * np;
+      a.nseg = 1; a.seg[0] = {X, X, w.kt_gram}; a.ktiles = w.kt_gram;
+      a.epi.alpha = 1.0f; a.epi.scale_pow = first ? 2 : 0; a.epi.scale = scale;
+      a.epi.out_f32 = A32; a.epi.ld_f32 = (int32_t)mp; a.epi.bs_f32 = mp * mp;
+      a.epi.out_hi = Ahi; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
+      if (Alo) { a.epi.out_lo = Alo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp; }
+      mc_status st = launch_gemm_planned(w.gram, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * nn_ * nb);
+      if (st) return st;
+    }
+    // Poly: P = a I + b A + c A A
+    {
+      GemmArgs a{};
+      a.M = (int32_t)mp; a.N = (int32_t)mp; a.batch = nb;
+      a.lda = (int32_t)mp; a.ldb = (int32_t)mp; a.bsa = mp * mp; a.bsb = mp * mp;
+      const int kt = (int)(mp / 64);
+      if (g.split) {
+        a.nseg = 3;
+        a.seg[0] = {Ahi, Ahi, kt}; a.seg[1] = {Ahi, Alo, kt}; a.seg[2] = {Alo, Ahi, kt};
+      } else {
+        a.nseg = 1; a.seg[0] = {Ahi, Ahi, kt};
+      }
+      a.ktiles = w.kt_poly;
+      a.epi.alpha = hp.ns_c; a.epi.beta = hp.ns_b; a.epi.diag = hp.ns_a;
+      a.epi.cin = A32; a.epi.ld_cin = (int32_t)mp; a.epi.bs_cin = mp * mp;
+      a.epi.out_hi = Phi; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
+      if (Plo) { a.epi.out_lo = Plo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp; }
+      mc_status st = launch_gemm_planned(w.poly, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * mm_ * nb);
+      if (st) return st;
+    }
+    // Apply: X' = s0 P X, read as C[i][j] = sum_k P[i][k] X^T[j][k]
+    {
+      GemmArgs a{};
+      a.M = (int32_t)mp; a.N = (int32_t)np; a.batch = nb;
+      a.lda = (int32_t)mp; a.ldb = (int32_t)mp; a.bsa = mp * mp; a.bsb = np * mp;
+      const int kt = (int)(mp / 64);
+      if (g.split) { a.nseg = 2; a.seg[0] = {Phi, xt_cur, kt}; a.seg[1] = {Plo, xt_cur, kt}; }
+      else { a.nseg = 1; a.seg[0] = {Phi, xt_cur, kt}; }
+      a.ktiles = w.kt_apply;
+      a.epi.alpha = 1.0f; a.epi.scale_pow = first ? 1 : 0; a.epi.scale = scale;
+      // both layouts every step: the next Gram reads X, the next apply X^T;
+      // after the last step O is read from whichever matches the matrix's
+      // own orientation (one group can mix [m][n] and [n][m] matrices)
+      a.epi.out_hi = X; a.epi.ld_hi = (int32_t)np; a.epi.bs_hi = mp * np;
+      a.epi.out_t = xt_nxt; a.epi.ld_t = (int32_t)mp; a.epi.bs_t = np * mp;
+      (void)last;
+      mc_status st = launch_gemm_planned(w.apply, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * nn_ * nb);
+      if (st) return st;
+    }
+  }
+
+  // 3. update + decay + QK-Clip rows
+  uint16_t* xt_final = XT[hp.ns_steps & 1];
+  const float decay = (float)(1.0 - (double)hp.lr * (double)hp.weight_decay);
+  for (int b0 = 0; b0 < nb; b0 += kMaxBatchMats) {
+    UpdArgs a{};
+    a.decay = decay; a.s_max = s_max; a.heads = heads; a.tau = hp.tau;
+    int blocks = 0;
+    double bytes = 0;
+    for (int j = 0; j < kMaxBatchMats && b0 + j < nb; ++j) {
+      const int slot = b0 + j;
+      const mc_matrix& m = mats[ids[slot]];
+      const bool wide = m.rows <= m.cols;
+      UpdMat& u = a.mat[a.nmat++];
+      u.w = m.w; u.w_bf16 = m.w_dtype == MC_BF16; u.ld = m.ld;
+      u.rows = (int32_t)m.rows; u.cols = (int32_t)m.cols;
+      u.vec = (m.cols % 4 == 0) && (m.ld % 4 == 0) && aligned(m.w, 4 * dtype_size(m.w_dtype)) &&
+              (!m.o_out || aligned(m.o_out, 8));
+      u.o = wide ? X + (size_t)slot * mp * np : xt_final + (size_t)slot * np * mp;
+      u.ld_o = (int32_t)(wide ? np : mp);
+      u.o_out = (uint16_t*)m.o_out;
+      u.lr_rms = (float)((double)hp.lr * (double)hp.rms_scale * sqrt((double)std::max(m.rows, m.cols)));
+      u.clip = clip_rule(m, s_max != nullptr);
+      u.tiles_c = (int32_t)((m.cols + 63) / 64);
+      u.block_start = blocks;
+      blocks += (int)((m.rows + 63) / 64) * u.tiles_c;
+      bytes += (double)m.rows * m.cols * 2.0 * dtype_size(m.w_dtype);
+    }
+    a.total_blocks = blocks;
+    Prof pr(F_UPDATE, s, 0.0, bytes);
+    hipError_t e = launch_update(a, s);
+    if (e != hipSuccess) return fail(MC_ERR_HIP, "update launch: %s", hipGetErrorString(e));
+  }
+  return MC_OK;
+}
+
+int largest_wave(const Group& g, int limit, size_t ws_bytes) {
+  int best = 0;
+  for (int nb = 1; nb <= limit; ++nb)
+    if (plan_wave(g, nb).bytes <= ws_bytes) best = nb;
+  return best;
+}
+
+}  // namespace
+
+// ================================================================ C ABI
+
+extern "C" {
+
+void mc_default_hparams(mc_hparams* hp) {
+  if (!hp) return;
+  hp->lr = 2e-4f; hp->mu = 0.95f; hp->weight_decay = 0.1f; hp->rms_scale = 0.2f; hp->tau = 100.0f;
+  hp->ns_a = 3.4445f; hp->ns_b = -4.7750f; hp->ns_c = 2.0315f; hp->ns_eps = 1e-7f; hp->ns_steps = 5;
+}
+
+const char* mc_last_error(void) { return g_err.c_str(); }
+const char* mc_version(void) { return "muonclip-gfx950 0.1"; }
+
+static size_t workspace_for(const mc_matrix* mats, int32_t n, const mc_hparams* hp, bool minimal) {
+  if (check_hparams(hp) != MC_OK) return 0;
+  if (check_matrices_step(mats, n, 0, 0, false) != MC_OK) return 0;
+  size_t best = 0;
+  for (const Group& g : make_groups(mats, n)) {
+    const int nb = minimal ? 1 : std::min<int>((int)g.idx.size(), kWaveCap);
+    best = std::max(best, plan_wave(g, nb).bytes);
+  }
+  return best;
+}
+
+size_t mc_workspace_size(const mc_matrix* mats, int32_t n, const mc_hparams* hp) {
+  return workspace_for(mats, n, hp, false);
+}
+size_t mc_workspace_min_size(const mc_matrix* mats, int32_t n, const mc_hparams* hp) {
+  return workspace_for(mats, n, hp, true);
+}
+
+mc_status muonclip_step(const mc_matrix* mats, int32_t n, const mc_hparams* hp, const float* s_max,
+                        int32_t slots, int32_t heads, float* gamma_out, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  mc_status st = check_hparams(hp);
+  if (st) return st;
+  const bool have_smax = s_max != nullptr;
+  if (have_smax && (slots <= 0 || heads <= 0)) return fail(MC_ERR_SHAPE, "slots and heads must be >= 1 with s_max");
+  if (gamma_out && !have_smax) return fail(MC_ERR_NULL, "gamma_out given without s_max");
+  if ((have_smax && !aligned(s_max, 4)) || (gamma_out && !aligned(gamma_out, 4)))
+    return fail(MC_ERR_ALIGN, "s_max / gamma_out misaligned");
+  st = check_matrices_step(mats, n, slots, heads, have_smax);
+  if (st) return st;
+  if (n == 0) return MC_OK;
+  if (!workspace) return fail(MC_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, kAlign)) return fail(MC_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const std::vector<Group> groups = make_groups(mats, n);
+  std::vector<int> wave_cap(groups.size());
+  for (size_t gi = 0; gi < groups.size(); ++gi) {
+    const Group& g = groups[gi];
+    wave_cap[gi] = largest_wave(g, std::min<int>((int)g.idx.size(), kWaveCap), workspace_bytes);
+    if (wave_cap[gi] == 0)
+      return fail(MC_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for one %lldx%lld matrix", workspace_bytes,
+                  plan_wave(g, 1).bytes, (long long)g.m, (long long)g.n);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (gamma_out) {
+    Prof pr(F_GAMMA, s, 0.0, 0.0);
+    hipError_t e = launch_gamma(s_max, gamma_out, slots * heads, hp->tau, s);
+    if (e != hipSuccess) return fail(MC_ERR_HIP, "gamma launch: %s", hipGetErrorString(e));
+  }
+  for (size_t gi = 0; gi < groups.size(); ++gi) {
+    const Group& g = groups[gi];
+    const int count = (int)g.idx.size();
+    for (int b0 = 0; b0 < count;) {
+      int nb = std::min(wave_cap[gi], count - b0);
+      while (nb > 1 && plan_wave(g, nb).bytes > workspace_bytes) --nb;
+      st = run_wave(mats, g, g.idx.data() + b0, nb, *hp, s_max, heads, (char*)workspace, s);
+      if (st) return st;
+      b0 += nb;
+    }
+  }
+  return MC_OK;
+}
+
+mc_status max_logits_per_head(const void* q, const void* k, const void* k_shared, int32_t dtype, int32_t B, int32_t T,
+                              int32_t H, int32_t d_q, int32_t d_k, int32_t d_shared, const int64_t* q_stride,
+                              const int64_t* k_stride, const int64_t* ks_stride, int32_t causal, float scale,
+                              float* s_max_out, void* stream) {
+  if (!s_max_out) return fail(MC_ERR_NULL, "s_max_out is NULL");
+  if (!dtype_ok(dtype)) return fail(MC_ERR_DTYPE, "dtype %d", dtype);
+  if (B < 0 || T < 0 || H <= 0) return fail(MC_ERR_SHAPE, "B, T must be >= 0 and H >= 1");
+  if (d_k <= 0 || d_shared < 0 || d_q != d_k + d_shared)
+    return fail(MC_ERR_SHAPE, "need d_q == d_k + d_shared with d_k >= 1 (got %d, %d, %d)", d_q, d_k, d_shared);
+  if (!q_stride || !k_stride) return fail(MC_ERR_NULL, "q_stride / k_stride is NULL");
+  if (!isfinite(scale) || scale <= 0.0f) return fail(MC_ERR_HPARAM, "scale must be finite and > 0");
+  if (!aligned(s_max_out, 4)) return fail(MC_ERR_ALIGN, "s_max_out misaligned");
+  const bool empty = B == 0 || T == 0;
+  if (!empty) {
+    if (!q || !k) return fail(MC_ERR_NULL, "q or k is NULL");
+    if (d_shared > 0 && (!k_shared || !ks_stride)) return fail(MC_ERR_NULL, "k_shared / ks_stride is NULL");
+    const size_t es = dtype_size(dtype);
+    if (!aligned(q, es) || !aligned(k, es) || (d_shared > 0 && !aligned(k_shared, es)))
+      return fail(MC_ERR_ALIGN, "q / k / k_shared misaligned");
+    for (int i = 0; i < 3; ++i)
+      if (q_stride[i] < 0 || k_stride[i] < 0) return fail(MC_ERR_SHAPE, "negative stride");
+    if ((T > 1 && q_stride[1] < d_q) || (T > 1 && k_stride[1] < d_k))
+      return fail(MC_ERR_SHAPE, "t stride smaller than the head dimension");
+  }
+  MaxLogitArgs a{};
+  a.q = q; a.k = k; a.ks = d_shared > 0 ? k_shared : nullptr;
+  a.qs_b = q_stride[0]; a.qs_t = q_stride[1]; a.qs_h = q_stride[2];
+  a.ks_b = k_stride[0]; a.ks_t = k_stride[1]; a.ks_h = k_stride[2];
+  a.kss_b = d_shared > 0 ? ks_stride[0] : 0; a.kss_t = d_shared > 0 ? ks_stride[1] : 0;
+  a.B = B; a.T = T; a.H = H; a.d_q = d_q; a.d_k = d_k; a.d_s = d_shared;
+  a.causal = causal ? 1 : 0; a.bf16 = dtype == MC_BF16;
+  a.out_enc = (uint32_t*)s_max_out;
+  hipStream_t s = (hipStream_t)stream;
+  {
+    Prof pr(F_ML_INIT, s, 0.0, 0.0);
+    hipError_t e = launch_max_logits_init(a.out_enc, H, s);
+    if (e != hipSuccess) return fail(MC_ERR_HIP, "max_logits init: %s", hipGetErrorString(e));
+  }
+  {
+    const double pairs = causal ? (double)T * (T + 1) / 2.0 : (double)T * T;
+    Prof pr(F_ML, s, 2.0 * d_q * pairs * B * H, 0.0);
+    bool mfma = false;
+    hipError_t e = launch_max_logits(a, s, &mfma);
+    if (e != hipSuccess) return fail(MC_ERR_HIP, "max_logits launch: %s", hipGetErrorString(e));
+  }
+  {
+    Prof pr(F_ML_FIN, s, 0.0, 0.0);
+    hipError_t e = launch_max_logits_finalize(a.out_enc, scale, H, s);
+    if (e != hipSuccess) return fail(MC_ERR_HIP, "max_logits finalize: %s", hipGetErrorString(e));
+  }
+  return MC_OK;
+}
+
+mc_status qk_clip_apply(const mc_matrix* mats, int32_t n, const float* s_max, int32_t slots, int32_t heads,
+                        float tau, float* gamma_out, void* stream) {
+  if (!s_max) return fail(MC_ERR_NULL, "s_max is NULL");
+  if (n < 0) return fail(MC_ERR_SHAPE, "n < 0");
+  if (n > 0 && !mats) return fail(MC_ERR_NULL, "mats is NULL");
+  if (slots <= 0 || heads <= 0) return fail(MC_ERR_SHAPE, "slots and heads must be >= 1");
+  if (!isfinite(tau) || tau <= 0.0f) return fail(MC_ERR_HPARAM, "tau must be finite and > 0");
+  if (!aligned(s_max, 4) || (gamma_out && !aligned(gamma_out, 4))) return fail(MC_ERR_ALIGN, "s_max / gamma_out misaligned");
+  for (int i = 0; i < n; ++i) {
+    mc_status st = check_matrix_common(mats[i], i);
+    if (st) return st;
+    st = check_clip(mats[i], i, slots, heads, true);
+    if (st) return st;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (gamma_out) {
+    Prof pr(F_GAMMA, s, 0.0, 0.0);
+    hipError_t e = launch_gamma(s_max, gamma_out, slots * heads, tau, s);
+    if (e != hipSuccess) return fail(MC_ERR_HIP, "gamma launch: %s", hipGetErrorString(e));
+  }
+  for (int i = 0; i < n; ++i) {
+    const mc_matrix& m = mats[i];
+    if (m.clip_slot < 0 || m.nseg == 0) continue;
+    ClipApplyArgs a{};
+    a.w = m.w; a.w_bf16 = m.w_dtype == MC_BF16; a.ld = m.ld;
+    a.rows = (int32_t)m.rows; a.cols = (int32_t)m.cols;
+    a.clip = clip_rule(m, true);
+    a.s_max = s_max; a.heads = heads; a.tau = tau;
+    Prof pr(F_CLIP, s, 0.0, 0.0);
+    hipError_t e = launch_clip_apply(a, s);
+    if (e != hipSuccess) return fail(MC_ERR_HIP, "clip_apply launch: %s", hipGetErrorString(e));
+  }
+  return MC_OK;
+}
+
+mc_status mc_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (on) { g_recs.clear(); g_pool_used = 0; }
+  g_prof = on != 0;
+  return MC_OK;
+}
+
+int32_t mc_profile_read(mc_profile_entry* out, int32_t cap) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  mc_profile_entry agg[F_COUNT];
+  memset(agg, 0, sizeof agg);
+  for (int f = 0; f < F_COUNT; ++f) snprintf(agg[f].name, sizeof agg[f].name, "%s", kFamilyNames[f]);
+  for (const ProfRec& r : g_recs) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return fail(MC_ERR_HIP, "event sync failed"), -1;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return fail(MC_ERR_HIP, "event elapsed failed"), -1;
+    agg[r.fam].launches += 1;
+    agg[r.fam].ms += ms;
+    agg[r.fam].flops += r.flops;
+    agg[r.fam].bytes += r.bytes;
+  }
+  int k = 0;
+  for (int f = 0; f < F_COUNT; ++f) {
+    if (agg[f].launches == 0) continue;
+    if (out && k < cap) out[k] = agg[f];
+    ++k;
+  }
+  return k;
+}
+
+}  // extern "C"

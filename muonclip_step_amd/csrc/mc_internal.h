@@ -1,0 +1,146 @@
+// Internal declarations shared by the HIP kernels and the host dispatcher of
+// the MuonClip library. Not installed; the public surface is include/muonclip.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mc {
+
+// ---------------------------------------------------------------- bf16 bits
+
+// fp32 -> bf16 with round-to-nearest-even (NaN kept quiet).
+__host__ __device__ inline uint16_t f32_to_bf16(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__host__ __device__ inline float bf16_to_f32(uint16_t h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+// ---------------------------------------------------------------- NS GEMM
+
+// One K segment of C = sum_s A_s B_s^T; both operands are bf16 row-major with
+// the contraction index contiguous ("NT" form).
+struct GemmSeg {
+  const uint16_t* a;
+  const uint16_t* b;
+  int32_t ktiles;       // K_s / 64
+};
+
+// Epilogue: v = alpha * scale[b]^pow * acc + beta * cin[i][j] + diag * (i==j),
+// then any of: fp32 store, bf16 store (hi), bf16 residual store (lo = v - hi),
+// bf16 store of the transpose. Every pointer is the batch-0 base; bs_* are the
+// per-batch strides in elements.
+struct GemmEpi {
+  float alpha;
+  int32_t scale_pow;
+  const float* scale;
+  float beta;
+  const float* cin; int32_t ld_cin; int64_t bs_cin;
+  float diag;
+  float* out_f32; int32_t ld_f32; int64_t bs_f32;
+  uint16_t* out_hi; int32_t ld_hi; int64_t bs_hi;
+  uint16_t* out_lo; int32_t ld_lo; int64_t bs_lo;
+  uint16_t* out_t; int32_t ld_t; int64_t bs_t;
+};
+
+struct GemmArgs {
+  int32_t M, N, batch;
+  int32_t lda, ldb;
+  int64_t bsa, bsb;
+  int32_t nseg;
+  GemmSeg seg[3];
+  int32_t ktiles;        // total over segments
+  int32_t splits;        // split-K count (>= 1)
+  int32_t kt_per_split;
+  float* partial;        // [splits][batch][M][N] fp32 when splits > 1
+  int32_t tiles_m, tiles_n;
+  GemmEpi epi;
+};
+
+enum GemmTile { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2 };
+int gemm_tile_dim(GemmTile t);
+hipError_t launch_ns_gemm(GemmTile tile, const GemmArgs& a, hipStream_t s);
+hipError_t launch_splitk_reduce(const GemmArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- elementwise
+
+constexpr int kMaxBatchMats = 8;
+
+// momentum update + sum of squares + bf16 copies in both orientations
+struct MomMat {
+  const void* g; float* m;
+  int64_t ld;
+  int32_t rows, cols, g_bf16, vec;
+  uint16_t* x_orig; int32_t ld_orig;   // [rp][cp], the stored orientation
+  uint16_t* x_tr;   int32_t ld_tr;     // [cp][rp]
+  int32_t rp, cp;                      // padded extents, multiples of 64
+  int32_t tiles_c;                     // cp / 64
+  int32_t block_start;
+  float* partial;                      // one fp32 per block of this matrix
+};
+struct MomArgs { int32_t nmat; float mu; int32_t total_blocks; MomMat mat[kMaxBatchMats]; };
+hipError_t launch_momentum(const MomArgs& a, hipStream_t s);
+
+// sum of per-block partials -> scale = 1 / (sqrt(sum) + eps), one matrix per block
+hipError_t launch_norm_finalize(const float* partial, int32_t parts_per_mat, int64_t partial_stride,
+                                float* scale, int32_t nmat, float eps, hipStream_t s);
+
+struct ClipRule {
+  int32_t slot, period, nseg;
+  int32_t off[2], len[2];
+  float expo[2];
+};
+
+// W <- clip_row * ((1 - lr wd) W - lr * rms * O)
+struct UpdMat {
+  void* w; int32_t w_bf16, vec;
+  int64_t ld;
+  int32_t rows, cols;
+  const uint16_t* o; int32_t ld_o;
+  uint16_t* o_out;                     // optional copy of O, [rows][cols] contiguous
+  float lr_rms;
+  ClipRule clip;
+  int32_t tiles_c, block_start;
+};
+struct UpdArgs {
+  int32_t nmat; int32_t total_blocks;
+  float decay;
+  const float* s_max; int32_t heads; float tau;
+  UpdMat mat[kMaxBatchMats];
+};
+hipError_t launch_update(const UpdArgs& a, hipStream_t s);
+
+hipError_t launch_gamma(const float* s_max, float* gamma, int32_t n, float tau, hipStream_t s);
+
+struct ClipApplyArgs {
+  void* w; int32_t w_bf16;
+  int64_t ld;
+  int32_t rows, cols;
+  ClipRule clip;
+  const float* s_max; int32_t heads; float tau;
+};
+hipError_t launch_clip_apply(const ClipApplyArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- max logits
+
+struct MaxLogitArgs {
+  const void* q; const void* k; const void* ks;
+  int64_t qs_b, qs_t, qs_h;
+  int64_t ks_b, ks_t, ks_h;
+  int64_t kss_b, kss_t;
+  int32_t B, T, H, d_q, d_k, d_s;
+  int32_t causal, bf16;
+  uint32_t* out_enc;     // [H] ordered-integer encoding of the running max
+};
+// true when the MFMA kernel covers this shape (bf16, d_k and d_s supported,
+// 16-byte aligned rows); otherwise the generic kernel runs.
+bool max_logits_mfma_supported(const MaxLogitArgs& a);
+hipError_t launch_max_logits_init(uint32_t* enc, int32_t H, hipStream_t s);
+hipError_t launch_max_logits(const MaxLogitArgs& a, hipStream_t s, bool* used_mfma);
+hipError_t launch_max_logits_finalize(uint32_t* enc, float scale, int32_t H, hipStream_t s);
+
+}  // namespace mc

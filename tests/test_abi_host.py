@@ -1,0 +1,148 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+include/muonclip.h declares, and rejects bad arguments before any launch
+(no GPU needed: validation runs before the first HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import muonclip_step_amd as mc
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "muonclip.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text))
+    keywords = {"if", "sizeof", "defined", "return"}
+    return sorted(n for n in names if n not in keywords and (n.startswith("mc_") or n in (
+        "muonclip_step", "max_logits_per_head", "qk_clip_apply")))
+
+
+def test_library_exports_every_declared_function():
+    lib = mc.load()
+    decl = declared_functions()
+    assert set(decl) >= {"muonclip_step", "max_logits_per_head", "qk_clip_apply", "mc_last_error"}
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert set(mc.EXPORTS) == set(decl)
+
+
+def test_default_hparams():
+    hp = mc.hparams()
+    assert abs(hp.lr - 2e-4) < 1e-10 and abs(hp.mu - 0.95) < 1e-7 and abs(hp.weight_decay - 0.1) < 1e-7
+    assert abs(hp.rms_scale - 0.2) < 1e-7 and hp.tau == 100.0 and hp.ns_steps == 5
+    assert (round(hp.ns_a, 4), round(hp.ns_b, 4), round(hp.ns_c, 4)) == (3.4445, -4.775, 2.0315)
+    assert abs(hp.ns_eps - 1e-7) < 1e-12
+
+
+def fake_matrix(rows, cols, ld=None, w_dtype=mc.MC_BF16, g_dtype=mc.MC_F32, clip_slot=-1, period=0, segs=()):
+    m = mc.Matrix()
+    m.w, m.g, m.m = 0x100000, 0x200000, 0x300000   # never dereferenced: only validated
+    m.rows, m.cols, m.ld = rows, cols, cols if ld is None else ld
+    m.w_dtype, m.g_dtype = w_dtype, g_dtype
+    m.clip_slot, m.period, m.nseg = clip_slot, period, len(segs)
+    for i, s in enumerate(segs):
+        m.seg[i] = mc.Segment(*s)
+    return m
+
+
+def step_status(mats, hp=None, s_max=None, slots=0, heads=0, gamma=None, ws=0x400000, ws_bytes=1 << 40):
+    lib = mc.load()
+    hp = hp or mc.hparams()
+    arr = (mc.Matrix * max(1, len(mats)))(*mats)
+    return lib.muonclip_step(arr, len(mats), ctypes.byref(hp), s_max, slots, heads, gamma, ws, ws_bytes, None)
+
+
+def test_step_rejects_bad_arguments():
+    assert step_status([fake_matrix(64, 0)]) == mc.MC_ERR_SHAPE
+    assert step_status([fake_matrix(64, 64, ld=32)]) == mc.MC_ERR_SHAPE
+    assert step_status([fake_matrix(64, 64, w_dtype=7)]) == mc.MC_ERR_DTYPE
+    m = fake_matrix(64, 64); m.g = None
+    assert step_status([m]) == mc.MC_ERR_NULL
+    m = fake_matrix(64, 64); m.w = 0x100001
+    assert step_status([m]) == mc.MC_ERR_ALIGN
+    hp = mc.hparams(ns_steps=0)
+    assert step_status([fake_matrix(64, 64)], hp=hp) == mc.MC_ERR_HPARAM
+    hp = mc.hparams(tau=-1.0)
+    assert step_status([fake_matrix(64, 64)], hp=hp) == mc.MC_ERR_HPARAM
+    hp = mc.hparams(lr=float("nan"))
+    assert step_status([fake_matrix(64, 64)], hp=hp) == mc.MC_ERR_HPARAM
+    # workspace: NULL, misaligned, too small
+    assert step_status([fake_matrix(64, 64)], ws=None) == mc.MC_ERR_WORKSPACE
+    assert step_status([fake_matrix(64, 64)], ws=0x400010) == mc.MC_ERR_WORKSPACE
+    assert step_status([fake_matrix(64, 64)], ws_bytes=1024) == mc.MC_ERR_WORKSPACE
+    assert "workspace" in mc.load().mc_last_error().decode()
+    # clip layout: slot out of range, period not dividing rows, segment outside period, overlap
+    seg = ((0, 16, 0.5),)
+    assert step_status([fake_matrix(64, 64, clip_slot=1, period=16, segs=seg)], s_max=0x500000, slots=1,
+                       heads=4) == mc.MC_ERR_SHAPE
+    assert step_status([fake_matrix(64, 64, clip_slot=0, period=24, segs=seg)], s_max=0x500000, slots=1,
+                       heads=4) == mc.MC_ERR_SHAPE
+    assert step_status([fake_matrix(64, 64, clip_slot=0, period=16, segs=((8, 16, 0.5),))], s_max=0x500000,
+                       slots=1, heads=4) == mc.MC_ERR_SHAPE
+    assert step_status([fake_matrix(64, 64, clip_slot=0, period=16, segs=((0, 10, 0.5), (8, 4, 1.0)))],
+                       s_max=0x500000, slots=1, heads=4) == mc.MC_ERR_SHAPE
+    assert step_status([fake_matrix(64, 64, clip_slot=0, period=16, segs=seg)], s_max=0x500000, slots=1,
+                       heads=2) == mc.MC_ERR_SHAPE
+    # gamma_out without s_max
+    assert step_status([fake_matrix(64, 64)], gamma=0x600000) == mc.MC_ERR_NULL
+    # empty list is a no-op
+    assert step_status([]) == mc.MC_OK
+
+
+def test_workspace_sizes_are_monotone_and_grouped():
+    one = [fake_matrix(2048, 2048)]
+    four = one * 4
+    s1 = mc.workspace_size(one)
+    s4 = mc.workspace_size(four)
+    assert s4 > s1 > 0
+    assert mc.workspace_size(four, minimal=True) == s1
+    # a tall and a wide matrix of the same shape share one group
+    mixed = [fake_matrix(7168, 2048), fake_matrix(2048, 7168)]
+    assert mc.workspace_size(mixed) == mc.workspace_size([fake_matrix(2048, 7168)] * 2)
+    # 64 matrices per wave at most
+    assert mc.workspace_size([fake_matrix(256, 512)] * 200) == mc.workspace_size([fake_matrix(256, 512)] * 64)
+
+
+def test_max_logits_rejects_bad_arguments():
+    lib = mc.load()
+    st = (ctypes.c_int64 * 3)(0, 0, 0)
+    ks = (ctypes.c_int64 * 2)(0, 0)
+    f = lib.max_logits_per_head
+    out = 0x700000
+    assert f(0x1000, 0x2000, None, 1, 1, 8, 2, 192, 128, 0, st, st, None, 1, 0.1, out, None) == mc.MC_ERR_SHAPE
+    assert f(0x1000, 0x2000, None, 1, 1, 8, 2, 192, 128, 64, st, st, None, 1, 0.1, out, None) == mc.MC_ERR_NULL
+    assert f(0x1000, 0x2000, None, 5, 1, 8, 2, 128, 128, 0, st, st, None, 1, 0.1, out, None) == mc.MC_ERR_DTYPE
+    assert f(0x1000, 0x2000, None, 1, 1, 8, 2, 128, 128, 0, st, st, None, 1, -1.0, out, None) == mc.MC_ERR_HPARAM
+    assert f(0x1000, 0x2000, None, 1, 1, 8, 2, 128, 128, 0, st, st, None, 1, 0.1, None, None) == mc.MC_ERR_NULL
+    assert f(0x1001, 0x2000, None, 1, 1, 8, 2, 128, 128, 0, st, st, None, 1, 0.1, out, None) == mc.MC_ERR_ALIGN
+    _ = ks
+
+
+def test_qk_clip_apply_rejects_bad_arguments():
+    lib = mc.load()
+    seg = ((0, 16, 0.5),)
+    arr = (mc.Matrix * 1)(fake_matrix(64, 64, clip_slot=0, period=16, segs=seg))
+    assert lib.qk_clip_apply(arr, 1, None, 1, 4, 100.0, None, None) == mc.MC_ERR_NULL
+    assert lib.qk_clip_apply(arr, 1, 0x500000, 1, 4, 0.0, None, None) == mc.MC_ERR_HPARAM
+    assert lib.qk_clip_apply(arr, 1, 0x500000, 1, 2, 100.0, None, None) == mc.MC_ERR_SHAPE
+
+
+def test_oracle_and_product_are_independent():
+    # the product package never imports the oracle, and the oracle never
+    # imports the product package or the HIP library
+    root = os.path.dirname(os.path.dirname(__file__))
+    for dirpath, _, files in os.walk(os.path.join(root, "muonclip_step_amd")):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in txt and "from oracle" not in txt, f
+    for f in os.listdir(os.path.join(root, "oracle")):
+        if f.endswith(".py"):
+            txt = open(os.path.join(root, "oracle", f)).read()
+            assert "muonclip_step_amd" not in txt and "libmuonclip" not in txt
+    ws = open(os.path.join(root, "workloads", "__init__.py")).read()
+    assert "import oracle" not in ws and "muonclip_step_amd" not in ws

@@ -1,0 +1,272 @@
+"""GPU parity of the HIP library against the fp64 oracle, through the C ABI.
+
+Tolerances: S_max 1e-3 relative; gamma 1e-3 relative; Newton-Schulz output
+2e-2 relative Frobenius; momentum within 1 fp32 ulp; parameters within 1 ulp
+of their dtype plus the part of the update the NS difference moves; rows the
+clip leaves alone bit-identical to an unclipped run.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import muonclip_step_amd as mc
+import oracle
+import workloads as wl
+from gpu_harness import (State, check_matrix, dev_tensor, host64, hp_for, load_config_states, oracle_step,
+                         qk_to_device, rel_fro)
+
+pytestmark = pytest.mark.gpu
+
+
+def smax_oracle(cfg, q, k, ks):
+    a = cfg.attn
+    return oracle.max_logits(q, k, ks, a.causal, 1.0 / math.sqrt(a.d_q))
+
+
+def weights_of(cfg):
+    return {s.name: wl.draw_weight(cfg, i) for i, s in enumerate(cfg.matrices)
+            if not s.device_drawn}
+
+
+# ----------------------------------------------------------------- config 1
+
+@pytest.mark.parametrize("lr", [2e-4, 0.02])
+def test_config1_tiny_mha_full_step(lr):
+    print("config 1 tiny MHA, lr", lr, flush=True)
+    cfg = wl.config(1)
+    q, k, ks = wl.draw_attention_inputs(cfg, weights_of(cfg))
+    qd, kd, _ = qk_to_device(q, k, ks, "f32")
+    s_gpu = mc.max_logits_per_head(qd, kd, None, causal=False)
+    s_orc = smax_oracle(cfg, q, k, None)
+    assert np.allclose(host64(s_gpu), s_orc, rtol=1e-3, atol=0)
+    gam_orc = oracle.clip_factor(s_orc, cfg.tau)
+    assert np.all(gam_orc < 1.0)          # tau = 10: every head clips
+    states = load_config_states(cfg)
+    hp = hp_for(cfg, lr=lr)
+    gamma = torch.empty(4, dtype=torch.float32, device="cuda")
+    mc.muonclip_step([s.desc() for s in states], hp, s_max=s_gpu, slots=1, heads=4, gamma_out=gamma)
+    torch.cuda.synchronize()
+    assert np.allclose(host64(gamma), gam_orc, rtol=1e-3, atol=0)
+    for s in states:
+        check_matrix(s, hp, gam_orc, gamma_gpu=host64(gamma))
+    if lr == 0.02:
+        # the update is visible above rounding: W0 (never clipped) moves by
+        # the RMS-matched step; compare the change itself
+        s0 = states[0]
+        w_o, _, _ = oracle_step(s0, hp, None)
+        d_g = host64(s0.w) - s0.w0
+        d_o = w_o - s0.w0
+        assert rel_fro(d_g, d_o) < 2e-2
+
+
+def test_cold_start_momentum_is_gradient():
+    cfg = wl.config(1)
+    states = load_config_states(cfg, indices=[0], cold=True)
+    hp = hp_for(cfg)
+    mc.muonclip_step([states[0].desc()], hp)
+    torch.cuda.synchronize()
+    assert np.array_equal(host64(states[0].m), states[0].g0.astype(np.float64))
+    check_matrix(states[0], hp)
+
+
+# ----------------------------------------------------------------- ragged / edge shapes
+
+@pytest.mark.parametrize("shape,w_dtype,g_dtype,ld_pad", [
+    ((1, 7), "bf16", "f32", 0),
+    ((7, 1), "f32", "f32", 3),
+    ((100, 37), "bf16", "bf16", 5),
+    ((37, 100), "f32", "f32", 0),
+    ((130, 300), "bf16", "f32", 2),
+    ((300, 130), "bf16", "f32", 0),
+    ((1000, 257), "bf16", "f32", 8),
+    ((257, 1100), "f32", "bf16", 0),
+])
+def test_ragged_shapes(shape, w_dtype, g_dtype, ld_pad):
+    print("ragged", shape, w_dtype, g_dtype, ld_pad, flush=True)
+    rows, cols = shape
+    spec = wl.MatrixSpec("r", rows, cols, w_dtype, init_std=0.5, grad_std=1.0, mom_std=1.0)
+    seed = 1000 + rows * 7 + cols
+    w = wl.normal(seed, 0, shape, 0.5)
+    w = wl.quantize_bf16(w) if w_dtype == "bf16" else wl.quantize_f32(w)
+    g = wl.normal(seed, 1, shape, 1.0)
+    g = wl.quantize_bf16(g) if g_dtype == "bf16" else wl.quantize_f32(g)
+    m = wl.quantize_f32(wl.normal(seed, 2, shape, 1.0))
+    st = State(spec, w, g, m, g_dtype=g_dtype, ld_pad=ld_pad)
+    hp = mc.hparams(lr=0.01)
+    mc.muonclip_step([st.desc()], hp)
+    torch.cuda.synchronize()
+    check_matrix(st, hp)
+    # the padding columns of the row stride are untouched
+    if ld_pad:
+        assert torch.all(st.w_full[:, cols:] == 0) and torch.all(st.m_full[:, cols:] == 0)
+
+
+def test_zero_gradient_and_momentum_decay_only():
+    spec = wl.MatrixSpec("z", 96, 160, "f32")
+    w = wl.quantize_f32(wl.normal(77, 0, (96, 160), 1.0))
+    z = np.zeros((96, 160), np.float32)
+    st = State(spec, w, z, z)
+    hp = mc.hparams(lr=0.05)
+    mc.muonclip_step([st.desc()], hp)
+    torch.cuda.synchronize()
+    assert torch.all(st.o == 0)
+    decay = np.float32(1.0 - np.float64(np.float32(0.05)) * np.float64(np.float32(0.1)))
+    assert np.array_equal(host64(st.w), (w * decay).astype(np.float32).astype(np.float64))
+
+
+# ----------------------------------------------------------------- config 2
+
+def test_config2_mha_layer_full_step():
+    print("config 2 MHA layer", flush=True)
+    cfg = wl.config(2)
+    q, k, _ = wl.draw_attention_inputs(cfg, weights_of(cfg))
+    qd, kd, _ = qk_to_device(q, k, None, "bf16")
+    s_gpu = mc.max_logits_per_head(qd, kd, None, causal=True)
+    s_orc = smax_oracle(cfg, q, k, None)
+    assert np.allclose(host64(s_gpu), s_orc, rtol=1e-3, atol=0)
+    gam_orc = oracle.clip_factor(s_orc, cfg.tau)
+    assert np.all(gam_orc[:4] < 1.0) and np.all(gam_orc[4:] == 1.0)
+    states = load_config_states(cfg)
+    hp = hp_for(cfg)
+    gamma = torch.empty(16, dtype=torch.float32, device="cuda")
+    mc.muonclip_step([s.desc() for s in states], hp, s_max=s_gpu, slots=1, heads=16, gamma_out=gamma)
+    torch.cuda.synchronize()
+    assert np.allclose(host64(gamma), gam_orc, rtol=1e-3, atol=0)
+    for s in states:
+        err = check_matrix(s, hp, gam_orc, gamma_gpu=host64(gamma))
+        print(s.spec.name, "NS rel err %.3e" % err, flush=True)
+
+
+def test_clip_rows_versus_unclipped_run():
+    """gamma = 1 heads are bit-identical to the run without QK-Clip; clipped
+    rows equal that run's rows times gamma^expo (one rounding)."""
+    cfg = wl.config(2)
+    idx = [0]
+    a = load_config_states(cfg, idx)
+    b = load_config_states(cfg, idx)
+    s_max = torch.tensor([1000.0, 150.0, 100.0, 50.0] + [1.0] * 12, device="cuda")
+    hp = hp_for(cfg)
+    mc.muonclip_step([a[0].desc()], hp, s_max=s_max, slots=1, heads=16)
+    mc.muonclip_step([b[0].desc()], hp)
+    torch.cuda.synchronize()
+    wa, wb = host64(a[0].w), host64(b[0].w)
+    assert np.array_equal(wa[256:], wb[256:])          # heads 2..15: gamma == 1
+    for h, sm in enumerate([1000.0, 150.0]):
+        g = np.float32(100.0) / np.float32(sm)
+        want = oracle.round_to_bf16(wb[h * 128:(h + 1) * 128] * math.sqrt(g))
+        diff = np.abs(wa[h * 128:(h + 1) * 128] - want)
+        assert np.all(diff <= 1.001 * np.ldexp(1.0, np.frexp(np.abs(want))[1] - 8) + 1e-30)
+    assert np.array_equal(host64(a[0].m), host64(b[0].m))  # the clip does not touch momentum
+
+
+def test_determinism_and_wave_split():
+    """Bit-identical results run to run; a group run in several waves (a
+    minimal workspace) still matches the oracle."""
+    cfg = wl.config(1)
+    outs = []
+    for ws_mode in ("full", "full", "min"):
+        states = load_config_states(cfg, indices=[1, 2])   # two 64x64 matrices: one group
+        descs = [s.desc() for s in states]
+        hp = hp_for(cfg)
+        size = mc.workspace_size(descs, hp, minimal=(ws_mode == "min"))
+        ws = torch.empty(size, dtype=torch.uint8, device="cuda")
+        mc.muonclip_step(descs, hp, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append([(s.w.cpu().clone(), s.m.cpu().clone(), s.o.cpu().clone()) for s in states])
+        if ws_mode == "min":
+            for s in states:
+                check_matrix(s, hp)
+    for (w0, m0, o0), (w1, m1, o1) in zip(outs[0], outs[1]):
+        assert torch.equal(w0, w1) and torch.equal(m0, m1) and torch.equal(o0, o1)
+
+
+# ----------------------------------------------------------------- QK-Clip alone
+
+def test_qk_clip_apply_essay_invariants():
+    """After qk_clip_apply the max logit recomputed from the clipped weights
+    is before*gamma and <= tau; gamma <= 1; gamma = 1 heads untouched."""
+    cfg = wl.config(2)
+    wts = weights_of(cfg)
+    q, k, _ = wl.draw_attention_inputs(cfg, wts)
+    qd, kd, _ = qk_to_device(q, k, None, "bf16")
+    before = mc.max_logits_per_head(qd, kd, None, causal=True)
+    wq = dev_tensor(wts["wq"], "bf16")
+    wk = dev_tensor(wts["wk"], "bf16")
+    dummy = torch.zeros_like(wq, dtype=torch.float32)
+    seg = ((0, 128, 0.5),)
+    mats = [mc.matrix(wq, dummy, dummy, clip_slot=0, period=128, segments=seg),
+            mc.matrix(wk, dummy, dummy, clip_slot=0, period=128, segments=seg)]
+    gamma = torch.empty(16, dtype=torch.float32, device="cuda")
+    mc.qk_clip_apply(mats, before, 1, 16, cfg.tau, gamma_out=gamma)
+    torch.cuda.synchronize()
+    g = host64(gamma)
+    assert np.all(g <= 1.0) and np.all(g[:4] < 1.0) and np.all(g[4:] == 1.0)
+    wq_h, wk_h = host64(wq), host64(wk)
+    assert np.array_equal(wq_h[512:], wts["wq"][512:].astype(np.float64))
+    assert np.array_equal(wk_h[512:], wts["wk"][512:].astype(np.float64))
+    # recompute Q, K from the clipped weights (same activations) -> S_max
+    cfg_c = wl.config(2)
+    q2, k2, _ = wl.draw_attention_inputs(cfg_c, {"wq": wq_h.astype(np.float32), "wk": wk_h.astype(np.float32)})
+    q2d, k2d, _ = qk_to_device(q2, k2, None, "bf16")
+    after = host64(mc.max_logits_per_head(q2d, k2d, None, causal=True))
+    b = host64(before)
+    # bf16 rounding of the clipped weights and of the recomputed Q/K moves
+    # the product by a few bf16 ulps
+    assert np.allclose(after, b * g, rtol=2e-2)
+    assert np.all(after <= cfg.tau * 1.02)
+
+
+# ----------------------------------------------------------------- max logits
+
+@pytest.mark.parametrize("B,T,H,dk,ds,causal,dtype", [
+    (1, 1, 2, 128, 0, True, "bf16"),
+    (2, 63, 3, 128, 0, True, "bf16"),
+    (2, 65, 2, 128, 64, True, "bf16"),
+    (1, 300, 4, 128, 64, False, "bf16"),
+    (3, 257, 2, 64, 0, True, "bf16"),
+    (2, 513, 2, 128, 0, False, "bf16"),
+    (2, 40, 3, 16, 0, True, "bf16"),      # generic kernel
+    (2, 33, 2, 16, 8, False, "f32"),      # generic kernel, fp32
+])
+def test_max_logits_shapes(B, T, H, dk, ds, causal, dtype):
+    print("max_logits", B, T, H, dk, ds, causal, dtype, flush=True)
+    seed = B * 1000 + T * 10 + H
+    q = wl.normal(seed, 0, (B, T, H, dk + ds), 2.0)
+    k = wl.normal(seed, 1, (B, T, H, dk), 2.0)
+    ks = wl.normal(seed, 2, (B, T, ds), 2.0) if ds else None
+    qz = wl.quantize_bf16 if dtype == "bf16" else wl.quantize_f32
+    q, k = qz(q), qz(k)
+    ks = qz(ks) if ds else None
+    qd, kd, ksd = qk_to_device(q, k, ks, dtype)
+    got = host64(mc.max_logits_per_head(qd, kd, ksd, causal=causal))
+    want = oracle.max_logits(q, k, ks, causal, 1.0 / math.sqrt(dk + ds))
+    assert np.allclose(got, want, rtol=1e-3, atol=0), (got, want)
+
+
+def test_max_logits_strided_views_and_nan():
+    B, T, H, d = 2, 130, 3, 128
+    big = wl.quantize_bf16(wl.normal(5, 0, (B, T, H + 1, 2 * d), 1.0))
+    q = big[:, :, :H, :d]
+    k = big[:, :, 1:, d:]
+    qd_full = dev_tensor(big, "bf16")
+    qd, kd = qd_full[:, :, :H, :d], qd_full[:, :, 1:, d:]
+    got = host64(mc.max_logits_per_head(qd, kd, None, causal=True))
+    want = oracle.max_logits(q, k, None, True, 1.0 / math.sqrt(d))
+    assert np.allclose(got, want, rtol=1e-3)
+    # one NaN key element: that key's logits are NaN and ignored
+    k2 = np.array(k)
+    k2[0, 5, 1, 3] = np.nan
+    kd2 = dev_tensor(k2, "bf16")
+    qd2 = dev_tensor(np.ascontiguousarray(q), "bf16")
+    got2 = host64(mc.max_logits_per_head(qd2, kd2, None, causal=True))
+    want2 = oracle.max_logits(q, k2, None, True, 1.0 / math.sqrt(d))
+    assert np.allclose(got2, want2, rtol=1e-3)
+
+
+def test_max_logits_empty_gives_neg_inf_and_gamma_one():
+    q = torch.zeros(0, 4, 2, 128, dtype=torch.bfloat16, device="cuda")
+    out = mc.max_logits_per_head(q, q, None, causal=True)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isneginf(out))
