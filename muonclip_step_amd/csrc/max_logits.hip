@@ -65,13 +65,14 @@ __global__ void __launch_bounds__(256, 1) max_logits_mfma_kernel(const MaxLogitA
   const int q0 = qt * BQ;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr0 = q0 + wave * 64;
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
 
   const uint16_t* Q = (const uint16_t*)a.q + (int64_t)b * a.qs_b + (int64_t)h * a.qs_h;
   const uint16_t* K = (const uint16_t*)a.k + (int64_t)b * a.ks_b + (int64_t)h * a.ks_h;
   const uint16_t* KS_ = DS > 0 ? (const uint16_t*)a.ks + (int64_t)b * a.kss_b : nullptr;
 
-  // this wave's query rows as A-fragments: lane l holds row l%32, k-chunk l/32
+  // this wave's query rows as A-fragments: lane l holds row l%32, k-chunk l/32.
+  // Rows and keys past T re-read the last valid one; every logit they touch
+  // is masked before the max.
   bf16x8_t qf[2][KS];
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
@@ -79,10 +80,7 @@ __global__ void __launch_bounds__(256, 1) max_logits_mfma_kernel(const MaxLogitA
     const int rr = row < a.T ? row : a.T - 1;
     const uint16_t* base = Q + (int64_t)rr * a.qs_t + 8 * (lane >> 5);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const u32x4_t v = *(const u32x4_t*)(base + 16 * s);
-      qf[f][s] = __builtin_bit_cast(bf16x8_t, row < a.T ? v : zero);
-    }
+    for (int s = 0; s < KS; ++s) qf[f][s] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(base + 16 * s));
   }
 
   const int kend = a.causal ? min(a.T, q0 + BQ) : a.T;
@@ -99,8 +97,7 @@ __global__ void __launch_bounds__(256, 1) max_logits_mfma_kernel(const MaxLogitA
       const uint16_t* src = (DS == 0 || c < DK / 8)                                    \
                                 ? K + (int64_t)kr * a.ks_t + c * 8                     \
                                 : KS_ + (int64_t)kr * a.kss_t + (c - DK / 8) * 8;      \
-      const u32x4_t v = *(const u32x4_t*)src;                                          \
-      st[i] = key < a.T ? v : zero;                                                    \
+      st[i] = *(const u32x4_t*)src;                                                    \
     }                                                                                  \
   }
 #define ML_LSTORE(buf_)                                                                \

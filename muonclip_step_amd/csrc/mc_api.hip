@@ -192,19 +192,28 @@ std::vector<Group> make_groups(const mc_matrix* mats, int32_t n) {
 
 struct GemmPlan { GemmTile tile; int tiles_m, tiles_n, splits, kt_per_split; size_t partial_bytes; };
 
-GemmPlan plan_gemm(int64_t M, int64_t N, int ktiles, int batch) {
+// Tile size and split-K for one batched product. 256x256 tiles when they give
+// at least two full waves of workgroups, else 128x128 (64x64 below 128 rows);
+// K is split only when the tiles alone cannot fill the chip, keeping every
+// split at least 8 k-stages long. Symmetric products count upper tiles only.
+GemmPlan plan_gemm(int64_t M, int64_t N, int ktiles, int batch, bool sym) {
   GemmPlan p{};
-  auto tiles_for = [&](int d) { return (int)(((M + d - 1) / d) * ((N + d - 1) / d)) * batch; };
-  if (M >= 256 && N >= 256 && tiles_for(256) >= kCUs) p.tile = TILE_256;
+  auto count = [&](int d) {
+    const int tm = (int)((M + d - 1) / d), tn = (int)((N + d - 1) / d);
+    return (sym ? tm * (tm + 1) / 2 : tm * tn) * batch;
+  };
+  if (M >= 256 && N >= 256 && count(256) >= 2 * kCUs) p.tile = TILE_256;
   else if (M >= 128 && N >= 128) p.tile = TILE_128;
   else p.tile = TILE_64;
   const int d = gemm_tile_dim(p.tile);
   p.tiles_m = (int)((M + d - 1) / d);
   p.tiles_n = (int)((N + d - 1) / d);
-  const int tiles = p.tiles_m * p.tiles_n * batch;
+  const int tiles = count(d);
   int splits = 1;
-  if (tiles < kCUs && ktiles >= 8) {
-    splits = std::min((2 * kCUs + tiles - 1) / tiles, ktiles / 4);
+  if (tiles < kCUs && ktiles >= 16) {
+    // split-K runs the full (non-symmetric) tile set
+    const int full = p.tiles_m * p.tiles_n * batch;
+    splits = std::min((2 * kCUs + full - 1) / full, ktiles / 8);
     splits = std::max(splits, 1);
   }
   p.kt_per_split = (ktiles + splits - 1) / splits;
@@ -239,26 +248,26 @@ WavePlan plan_wave(const Group& g, int nb) {
   w.mom_blocks = (int64_t)(mp / 64) * (int64_t)(np / 64);
   w.off_part = take(nb * (size_t)w.mom_blocks * 4);
   w.off_scale = take(nb * 4);
-  w.kt_gram = (int)(np / 64);
-  w.kt_poly = (int)(mp / 64) * (g.split ? 3 : 1);
-  w.kt_apply = (int)(mp / 64) * (g.split ? 2 : 1);
-  w.gram = plan_gemm(g.mp, g.mp, w.kt_gram, nb);
-  w.poly = plan_gemm(g.mp, g.mp, w.kt_poly, nb);
-  w.apply = plan_gemm(g.mp, g.np, w.kt_apply, nb);
+  w.kt_gram = (int)(np / kGemmBK);
+  w.kt_poly = (int)(mp / kGemmBK) * (g.split ? 3 : 1);
+  w.kt_apply = (int)(mp / kGemmBK) * (g.split ? 2 : 1);
+  w.gram = plan_gemm(g.mp, g.mp, w.kt_gram, nb, true);
+  w.poly = plan_gemm(g.mp, g.mp, w.kt_poly, nb, true);
+  w.apply = plan_gemm(g.mp, g.np, w.kt_apply, nb, false);
   const size_t sk = std::max(w.gram.partial_bytes, std::max(w.poly.partial_bytes, w.apply.partial_bytes));
   w.off_splitk = sk ? take(sk) : 0;
   w.bytes = off;
   return w;
 }
 
-mc_status launch_gemm_planned(const GemmPlan& gp, GemmArgs a, hipStream_t s, void* ws_base, size_t off_splitk,
-                              double flops) {
+mc_status launch_gemm_planned(const GemmPlan& gp, GemmKind kind, bool split_pair, GemmArgs a, hipStream_t s,
+                              void* ws_base, size_t off_splitk, double flops) {
   a.tiles_m = gp.tiles_m; a.tiles_n = gp.tiles_n;
   a.splits = gp.splits; a.kt_per_split = gp.kt_per_split;
   a.partial = gp.splits > 1 ? (float*)((char*)ws_base + off_splitk) : nullptr;
   {
     Prof pr(F_GEMM, s, flops, 0.0);
-    hipError_t e = launch_ns_gemm(gp.tile, a, s);
+    hipError_t e = launch_ns_gemm(gp.tile, kind, split_pair, a, s);
     if (e != hipSuccess) return fail(MC_ERR_HIP, "ns_gemm launch: %s", hipGetErrorString(e));
   }
   if (gp.splits > 1) {
@@ -349,7 +358,8 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
       a.epi.out_f32 = A32; a.epi.ld_f32 = (int32_t)mp; a.epi.bs_f32 = mp * mp;
       a.epi.out_hi = Ahi; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
       if (Alo) { a.epi.out_lo = Alo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp; }
-      mc_status st = launch_gemm_planned(w.gram, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * nn_ * nb);
+      mc_status st = launch_gemm_planned(w.gram, GEMM_GRAM, g.split, a, s, ws, w.off_splitk,
+                                         2.0 * mm_ * mm_ * nn_ * nb);
       if (st) return st;
     }
     // Poly: P = a I + b A + c A A
@@ -357,7 +367,7 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
       GemmArgs a{};
       a.M = (int32_t)mp; a.N = (int32_t)mp; a.batch = nb;
       a.lda = (int32_t)mp; a.ldb = (int32_t)mp; a.bsa = mp * mp; a.bsb = mp * mp;
-      const int kt = (int)(mp / 64);
+      const int kt = (int)(mp / kGemmBK);
       if (g.split) {
         a.nseg = 3;
         a.seg[0] = {Ahi, Ahi, kt}; a.seg[1] = {Ahi, Alo, kt}; a.seg[2] = {Alo, Ahi, kt};
@@ -369,7 +379,8 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
       a.epi.cin = A32; a.epi.ld_cin = (int32_t)mp; a.epi.bs_cin = mp * mp;
       a.epi.out_hi = Phi; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
       if (Plo) { a.epi.out_lo = Plo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp; }
-      mc_status st = launch_gemm_planned(w.poly, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * mm_ * nb);
+      mc_status st = launch_gemm_planned(w.poly, GEMM_POLY, g.split, a, s, ws, w.off_splitk,
+                                         2.0 * mm_ * mm_ * mm_ * nb);
       if (st) return st;
     }
     // Apply: X' = s0 P X, read as C[i][j] = sum_k P[i][k] X^T[j][k]
@@ -377,7 +388,7 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
       GemmArgs a{};
       a.M = (int32_t)mp; a.N = (int32_t)np; a.batch = nb;
       a.lda = (int32_t)mp; a.ldb = (int32_t)mp; a.bsa = mp * mp; a.bsb = np * mp;
-      const int kt = (int)(mp / 64);
+      const int kt = (int)(mp / kGemmBK);
       if (g.split) { a.nseg = 2; a.seg[0] = {Phi, xt_cur, kt}; a.seg[1] = {Plo, xt_cur, kt}; }
       else { a.nseg = 1; a.seg[0] = {Phi, xt_cur, kt}; }
       a.ktiles = w.kt_apply;
@@ -388,7 +399,8 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
       a.epi.out_hi = X; a.epi.ld_hi = (int32_t)np; a.epi.bs_hi = mp * np;
       a.epi.out_t = xt_nxt; a.epi.ld_t = (int32_t)mp; a.epi.bs_t = np * mp;
       (void)last;
-      mc_status st = launch_gemm_planned(w.apply, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * nn_ * nb);
+      mc_status st = launch_gemm_planned(w.apply, GEMM_APPLY, false, a, s, ws, w.off_splitk,
+                                         2.0 * mm_ * mm_ * nn_ * nb);
       if (st) return st;
     }
   }

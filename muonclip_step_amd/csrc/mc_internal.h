@@ -24,10 +24,12 @@ __host__ __device__ inline float bf16_to_f32(uint16_t h) {
 
 // One K segment of C = sum_s A_s B_s^T; both operands are bf16 row-major with
 // the contraction index contiguous ("NT" form).
+constexpr int kGemmBK = 32;   // k per pipeline stage of the NS GEMM
+
 struct GemmSeg {
   const uint16_t* a;
   const uint16_t* b;
-  int32_t ktiles;       // K_s / 64
+  int32_t ktiles;       // K_s / kGemmBK
 };
 
 // Epilogue: v = alpha * scale[b]^pow * acc + beta * cin[i][j] + diag * (i==j),
@@ -62,8 +64,16 @@ struct GemmArgs {
 };
 
 enum GemmTile { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2 };
+// which Newton-Schulz product a launch computes; fixes the epilogue:
+//   GRAM  A = s^2 X X^T      -> fp32 A, bf16 A_hi (+ A_lo)   (symmetric tiles)
+//   POLY  P = a I + b A + c A A -> bf16 P_hi (+ P_lo)          (symmetric tiles)
+//   APPLY X' = s P X          -> bf16 X' and its transpose
+enum GemmKind { GEMM_GRAM = 0, GEMM_POLY = 1, GEMM_APPLY = 2 };
 int gemm_tile_dim(GemmTile t);
-hipError_t launch_ns_gemm(GemmTile tile, const GemmArgs& a, hipStream_t s);
+// workgroups per matrix and split (symmetric products count upper tiles only)
+int gemm_tile_count(const GemmArgs& a, GemmKind kind);
+// split_pair: the product's result is also stored as a residual bf16 (lo) part
+hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const GemmArgs& a, hipStream_t s);
 hipError_t launch_splitk_reduce(const GemmArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- elementwise

@@ -7,21 +7,26 @@
 // A twice, and P X reads P and the transposed copy X^T that the previous
 // apply wrote. One kernel therefore serves all three, batched over the
 // matrices of one shape group (grid = tiles x splits x batch, mapped
-// XCD-major so the tiles of one matrix share an XCD's L2).
+// XCD-major so the tiles of one matrix share an XCD's L2). The two symmetric
+// products (X X^T and A A) compute only the tiles on and above the diagonal
+// and store each off-diagonal tile a second time, transposed.
 //
 // gfx950 design: v_mfma_f32_32x32x16_bf16 with fp32 accumulation; a block of
-// 2x2 waves owns a BMxBN tile, each wave a (BM/2)x(BN/2) sub-tile; BK = 64 k
-// per stage; A and B stages are double-buffered in LDS (128 KB at 256x256)
-// with an XOR swizzle of the 16-byte chunks so both the coalesced stores and
-// the MFMA-fragment reads are bank-conflict free; the next stage's global
-// loads are in flight while the current stage runs on the matrix cores.
+// 2x2 waves owns a BMxBN tile, each wave a (BM/2)x(BN/2) sub-tile. K advances
+// in 32-wide stages held in a 4-slot LDS ring that direct-to-LDS loads
+// (global_load_lds_dwordx4) fill three stages ahead, so no register staging
+// is needed; one barrier per stage publishes the next stage; the MFMA
+// fragments of each 16-k step are read from LDS while the previous step's
+// MFMAs run. The epilogue is specialised at compile time per use and stores
+// straight from the accumulator registers.
 #include "mc_internal.h"
 
 namespace mc {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
 
 int gemm_tile_dim(GemmTile t) { return t == TILE_256 ? 256 : (t == TILE_128 ? 128 : 64); }
 
@@ -52,172 +57,262 @@ __device__ __attribute__((always_inline)) inline float batch_scale(const GemmEpi
   return e.scale_pow == 1 ? s : s * s;
 }
 
-template <int BM, int BN>
-__global__ void __launch_bounds__(256, 1) ns_gemm_kernel(const GemmArgs p) {
-  constexpr int NT = 256, BK = 64;
+// Chunk swizzle of a 64-byte LDS row (four 16-byte chunks): row r stores
+// logical chunk c at c ^ swz(r). With rows grouped four to a 256-byte bank
+// window, the four rows that share bank positions get four different chunk
+// slots; the SQ_LDS_BANK_CONFLICT counter reads zero for the fragment reads
+// of this kernel with this mapping on gfx950.
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+
+// Calls f(acc[I / FN][I % FN], I / FN, I % FN) for I = I0 .. N-1 with every
+// index a compile-time constant (keeps the accumulators in registers).
+template <int I0, int N, int FN>
+struct FragVisit {
+  template <typename A, typename F>
+  __device__ __forceinline__ static void run(A& acc, F& f) {
+    f(acc[I0 / FN][I0 % FN], I0 / FN, I0 % FN);
+    FragVisit<I0 + 1, N, FN>::run(acc, f);
+  }
+};
+template <int N, int FN>
+struct FragVisit<N, N, FN> {
+  template <typename A, typename F>
+  __device__ __forceinline__ static void run(A&, F&) {}
+};
+
+// compile-time epilogue selection
+enum : int {
+  E_F32 = 1,      // fp32 store of v
+  E_HI = 2,       // bf16 store of v
+  E_LO = 4,       // bf16 store of v - bf16(v)
+  E_T = 8,        // bf16 store of v at the transposed position
+  E_CIN = 16,     // v += beta * cin[i][j]
+  E_DIAG = 32,    // v += diag on i == j
+  E_PART = 64,    // split-K: raw fp32 partial, no epilogue
+  E_SYM = 128,    // upper tiles only; off-diagonal tiles also stored mirrored
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at max)
+#define MC_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | 0x70 | 0xF00 | (((n) >> 4) << 14))
+
+template <int BM, int BN, int EPI>
+__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+ns_gemm_kernel(const GemmArgs p) {
+  constexpr int BK = 32, NSTAGE = 4;
   constexpr int WTM = BM / 2, WTN = BN / 2;       // 2 x 2 waves
   constexpr int FM = WTM / 32, FN = WTN / 32;     // 32x32 fragments per wave
-  constexpr int CA = BM * BK / 8, CB = BN * BK / 8;   // 16-byte chunks per stage
-  constexpr int PT = (CA + CB) / NT;
-  constexpr int PA = CA / NT;
-  static_assert((CA % NT) == 0 && (CB % NT) == 0, "tile/thread mismatch");
-  __shared__ u32x4_t lds[2][CA + CB];
+  constexpr int ROWB = BK * 2;                    // bytes per LDS row (64)
+  constexpr int STAGE = (BM + BN) * ROWB;         // bytes per stage
+  constexpr int IA = BM / 64, IB = BN / 64;       // DMA instructions per wave per stage (16 rows each)
+  static_assert(STAGE * NSTAGE <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) char lds[STAGE * NSTAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  const int tiles = p.tiles_m * p.tiles_n;
+  const int tiles = (EPI & E_SYM) ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
   const int total = tiles * p.splits * p.batch;
   const int L = xcd_remap(blockIdx.x, total);
   const int b = L / (tiles * p.splits);
   const int rem = L - b * tiles * p.splits;
   const int split = rem / tiles;
-  const int t = rem - split * tiles;
-  const int m0 = (t / p.tiles_n) * BM;
-  const int n0 = (t % p.tiles_n) * BN;
+  int t = rem - split * tiles;
+  int tm, tn;
+  if (EPI & E_SYM) {            // t-th tile of the upper triangle, row by row
+    tm = 0;
+    while (t >= p.tiles_m - tm) { t -= p.tiles_m - tm; ++tm; }
+    tn = tm + t;
+  } else {
+    tm = t / p.tiles_n;
+    tn = t - tm * p.tiles_n;
+  }
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
 
   const int kt_begin = split * p.kt_per_split;
   const int kt_end = min(p.ktiles, kt_begin + p.kt_per_split);
   const int nk = kt_end - kt_begin;
+
+  // Per-lane DMA source offsets (elements, without k): DMA instruction i of
+  // this wave fills tile rows 16*(wave*IA + i) .. +15; lane l lands at LDS
+  // slot l of that 1 KB block = row l/4, physical chunk l%4, so it fetches
+  // logical chunk (l%4) ^ swz(row). Rows past M / N re-read the last row;
+  // they only feed outputs that are never stored.
+  int64_t offA[IA], offB[IB];
+#pragma unroll
+  for (int i = 0; i < IA; ++i) {
+    const int r = 16 * (wave * IA + i) + (lane >> 2);
+    const int gr = min(m0 + r, p.M - 1);
+    offA[i] = (int64_t)gr * p.lda + (((lane & 3) ^ swz(r)) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < IB; ++i) {
+    const int r = 16 * (wave * IB + i) + (lane >> 2);
+    const int gr = min(n0 + r, p.N - 1);
+    offB[i] = (int64_t)gr * p.ldb + (((lane & 3) ^ swz(r)) * 8);
+  }
+
+  // segment bases and boundaries, read from the kernel arguments once so the
+  // loop issues no scalar loads (they would force full LDS-counter waits)
+  const int nseg = p.nseg;
+  const int kb0 = p.seg[0].ktiles, kb1 = p.seg[0].ktiles + (nseg > 1 ? p.seg[1].ktiles : 0);
+  const uint16_t* A0 = p.seg[0].a + (int64_t)b * p.bsa;
+  const uint16_t* B0 = p.seg[0].b + (int64_t)b * p.bsb;
+  const uint16_t* A1 = nseg > 1 ? p.seg[1].a + (int64_t)b * p.bsa : A0;
+  const uint16_t* B1 = nseg > 1 ? p.seg[1].b + (int64_t)b * p.bsb : B0;
+  const uint16_t* A2 = nseg > 2 ? p.seg[2].a + (int64_t)b * p.bsa : A1;
+  const uint16_t* B2 = nseg > 2 ? p.seg[2].b + (int64_t)b * p.bsb : B1;
+
+  // issue the DMA of k-stage kt_ (relative to kt_begin) into ring slot kt_ % NSTAGE
+#define MC_ISSUE(kt_)                                                                    \
+  {                                                                                      \
+    const int kg_ = kt_begin + (kt_);                                                    \
+    const uint16_t* A_ = A0;                                                             \
+    const uint16_t* B_ = B0;                                                             \
+    int kl_ = kg_;                                                                       \
+    if (kg_ >= kb1) { A_ = A2; B_ = B2; kl_ = kg_ - kb1; }                               \
+    else if (kg_ >= kb0) { A_ = A1; B_ = B1; kl_ = kg_ - kb0; }                          \
+    A_ += kl_ * BK;                                                                      \
+    B_ += kl_ * BK;                                                                      \
+    char* base_ = lds + ((kt_) % NSTAGE) * STAGE;                                        \
+    _Pragma("unroll") for (int i = 0; i < IA; ++i)                                       \
+      __builtin_amdgcn_global_load_lds((const void*)(A_ + offA[i]),                      \
+          (lds_void_t*)(base_ + (16 * (wave * IA + i)) * ROWB), 16, 0, 0);               \
+    _Pragma("unroll") for (int i = 0; i < IB; ++i)                                       \
+      __builtin_amdgcn_global_load_lds((const void*)(B_ + offB[i]),                      \
+          (lds_void_t*)(base_ + BM * ROWB + (16 * (wave * IB + i)) * ROWB), 16, 0, 0);   \
+  }
 
   f32x16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
+  bf16x8_t af[2][FM], bfr[2][FN];
 
-  u32x4_t st[PT];
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-
-  // global -> registers for k-tile kt (chunk q of a stage: row q/8, 16-byte
-  // column chunk q%8; rows past M or N load zeros)
-#define MC_GLOAD(kt_)                                                                    \
+  // fragment reads of k-step kk_ (16 k) of stage kt_ into register slot sl_
+#define MC_FRAG(kt_, kk_, sl_)                                                           \
   {                                                                                      \
-    int s_ = 0, kl_ = (kt_);                                                             \
-    if (p.nseg > 1 && kl_ >= p.seg[0].ktiles) {                                          \
-      kl_ -= p.seg[0].ktiles; s_ = 1;                                                    \
-      if (p.nseg > 2 && kl_ >= p.seg[1].ktiles) { kl_ -= p.seg[1].ktiles; s_ = 2; }      \
+    const char* base_ = lds + ((kt_) % NSTAGE) * STAGE;                                  \
+    const int c_ = (kk_) * 2 + (lane >> 5);                                              \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                     \
+      const int r_ = wm * WTM + i * 32 + (lane & 31);                                    \
+      af[(sl_)][i] = *(const bf16x8_t*)(base_ + r_ * ROWB + ((c_ ^ swz(r_)) << 4));      \
     }                                                                                    \
-    const uint16_t* A_ = (s_ == 0 ? p.seg[0].a : (s_ == 1 ? p.seg[1].a : p.seg[2].a)) +  \
-                         (int64_t)b * p.bsa;                                             \
-    const uint16_t* B_ = (s_ == 0 ? p.seg[0].b : (s_ == 1 ? p.seg[1].b : p.seg[2].b)) +  \
-                         (int64_t)b * p.bsb;                                             \
-    const int k0_ = kl_ * BK;                                                            \
-    _Pragma("unroll") for (int i = 0; i < PT; ++i) {                                     \
-      if (i < PA) {                                                                      \
-        const int q = tid + i * NT, r = q >> 3, c = q & 7, gr = m0 + r;                  \
-        const int rr = gr < p.M ? gr : p.M - 1;                                          \
-        u32x4_t v_ = *(const u32x4_t*)(A_ + (int64_t)rr * p.lda + k0_ + c * 8);              \
-        st[i] = gr < p.M ? v_ : zero;                                                    \
-      } else {                                                                           \
-        const int q = tid + (i - PA) * NT, r = q >> 3, c = q & 7, gr = n0 + r;           \
-        const int rr = gr < p.N ? gr : p.N - 1;                                          \
-        u32x4_t v_ = *(const u32x4_t*)(B_ + (int64_t)rr * p.ldb + k0_ + c * 8);              \
-        st[i] = gr < p.N ? v_ : zero;                                                    \
-      }                                                                                  \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                     \
+      const int r_ = wn * WTN + j * 32 + (lane & 31);                                    \
+      bfr[(sl_)][j] = *(const bf16x8_t*)(base_ + BM * ROWB + r_ * ROWB + ((c_ ^ swz(r_)) << 4)); \
     }                                                                                    \
   }
-  // registers -> LDS stage buf, 16-byte chunk c of row r stored at chunk c ^ (r & 7)
-#define MC_LSTORE(buf_)                                                                  \
+#define MC_MMA(sl_)                                                                      \
   {                                                                                      \
-    _Pragma("unroll") for (int i = 0; i < PT; ++i) {                                     \
-      if (i < PA) {                                                                      \
-        const int q = tid + i * NT, r = q >> 3, c = q & 7;                               \
-        lds[(buf_)][r * 8 + (c ^ (r & 7))] = st[i];                                      \
-      } else {                                                                           \
-        const int q = tid + (i - PA) * NT, r = q >> 3, c = q & 7;                        \
-        lds[(buf_)][CA + r * 8 + (c ^ (r & 7))] = st[i];                                 \
-      }                                                                                  \
-    }                                                                                    \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i)                                       \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                     \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[(sl_)][i], bfr[(sl_)][j], \
+                                                            acc[i][j], 0, 0, 0);         \
   }
 
+  // Pipeline: stages are fetched 3 ahead into a 4-slot LDS ring by DMA; one
+  // barrier per stage, placed between the stage's two k-steps, publishes the
+  // next stage and retires the slot the new DMA overwrites; the fragments of
+  // each k-step are read while the previous k-step's MFMAs run.
   if (nk > 0) {
-    MC_GLOAD(kt_begin);
-    MC_LSTORE(0);
-    __syncthreads();
-    for (int it = 0; it < nk; ++it) {
-      const int cur = it & 1;
-      if (it + 1 < nk) MC_GLOAD(kt_begin + it + 1);
-      const u32x4_t* La = lds[cur];
-      const u32x4_t* Lb = lds[cur] + CA;
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        bf16x8_t af[FM], bfr[FN];
-        const int c = kk * 2 + (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int r = wm * WTM + i * 32 + (lane & 31);
-          af[i] = __builtin_bit_cast(bf16x8_t, La[r * 8 + (c ^ (r & 7))]);
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int r = wn * WTN + j * 32 + (lane & 31);
-          bfr[j] = __builtin_bit_cast(bf16x8_t, Lb[r * 8 + (c ^ (r & 7))]);
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    const int pre = min(NSTAGE - 1, nk);
+    for (int s = 0; s < pre; ++s) MC_ISSUE(s);
+    if (pre == 3) MC_WAIT_VMCNT(2 * (IA + IB));
+    else if (pre == 2) MC_WAIT_VMCNT(IA + IB);
+    else MC_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    MC_FRAG(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      MC_FRAG(kt, 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      MC_MMA(0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < nk) {
+        if (kt + 2 < nk) MC_WAIT_VMCNT(IA + IB);
+        else MC_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_barrier();
+        if (kt + 3 < nk) MC_ISSUE(kt + 3);
       }
-      if (it + 1 < nk) MC_LSTORE(cur ^ 1);
-      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      // k-step 0 of the next stage (visible after the barrier); after the last
+      // stage this reads a stale ring slot whose values are never used, which
+      // keeps the LDS counter waits exact
+      MC_FRAG(kt + 1, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      MC_MMA(1);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-#undef MC_GLOAD
-#undef MC_LSTORE
+  MC_WAIT_VMCNT(0);
+#undef MC_MMA
+#undef MC_FRAG
+#undef MC_ISSUE
 
-  // Epilogue, one 32-row fragment band of every wave at a time, staged through
-  // LDS (free after the last barrier) so that every store is coalesced: the
-  // accumulator layout of the 32x32 MFMA puts row 8*(r/4) + 4*(l/32) + r%4,
-  // column l%32 of a fragment in register r of lane l.
-  constexpr int RLD = WTN + 4;                       // padded row of a wave's band
-  float* band = reinterpret_cast<float*>(&lds[0][0]) + wave * (32 * RLD);
-  const float sc = batch_scale(p.epi, b);
-  float* part = p.splits > 1 ? p.partial + ((int64_t)split * p.batch + b) * (int64_t)p.M * p.N : nullptr;
+  // Epilogue straight from the accumulators: register 4g+q of lane l holds
+  // row 8g + 4(l/32) + q, column l%32 of its 32x32 fragment, i.e. each lane
+  // owns runs of four consecutive rows at one column. Row-major stores are
+  // 64/128-byte segments per half-wave; transposed stores write the four
+  // rows as one 8- or 16-byte vector.
+  const float sc = (EPI & E_PART) ? 1.0f : batch_scale(p.epi, b);
+  const float alpha = p.epi.alpha * sc, beta = p.epi.beta, diag = p.epi.diag;
+  const bool mirror = (EPI & E_SYM) && tm != tn;
+  const int64_t mn = (int64_t)p.M * p.N;
+  float* part = (EPI & E_PART) ? p.partial + ((int64_t)split * p.batch + b) * mn : nullptr;
+  const float* cin = (EPI & E_CIN) ? p.epi.cin + (int64_t)b * p.epi.bs_cin : nullptr;
+  float* of32 = (EPI & E_F32) ? p.epi.out_f32 + (int64_t)b * p.epi.bs_f32 : nullptr;
+  uint16_t* ohi = (EPI & E_HI) ? p.epi.out_hi + (int64_t)b * p.epi.bs_hi : nullptr;
+  uint16_t* olo = (EPI & E_LO) ? p.epi.out_lo + (int64_t)b * p.epi.bs_lo : nullptr;
+  uint16_t* ot = (EPI & E_T) ? p.epi.out_t + (int64_t)b * p.epi.bs_t : nullptr;
+  // one 32x32 fragment per call; fragments are visited in a fully unrolled
+  // recursion so every accumulator index is a compile-time constant
+  auto frag_out = [&](const f32x16_t& a, int fi, int fj) __attribute__((always_inline)) {
+    const int gj = n0 + wn * WTN + fj * 32 + (lane & 31);
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+    for (int g = 0; g < 4; ++g) {
+      const int gi = m0 + wm * WTM + fi * 32 + 8 * g + 4 * (lane >> 5);   // rows gi..gi+3
+      if (gi < p.M && gj < p.N) {
+        float v[4] = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+        if (EPI & E_PART) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+          for (int q = 0; q < 4; ++q) part[(int64_t)(gi + q) * p.N + gj] = v[q];
+        } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        band[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * RLD + j * 32 + (lane & 31)] = acc[i][j][r];
-    __syncthreads();
-    const int gi0 = m0 + wm * WTM + i * 32;
-    const int gj0 = n0 + wn * WTN;
-    // row-major pass: consecutive lanes take consecutive columns
-    for (int e = lane; e < 32 * WTN; e += 64) {
-      const int rr = e / WTN, cc = e - rr * WTN;
-      const int gi = gi0 + rr, gj = gj0 + cc;
-      if (gi >= p.M || gj >= p.N) continue;
-      const float a = band[rr * RLD + cc];
-      if (part) { part[(int64_t)gi * p.N + gj] = a; continue; }
-      const GemmEpi& E = p.epi;
-      float v = E.alpha * sc * a;
-      if (E.cin) v += E.beta * E.cin[(int64_t)b * E.bs_cin + (int64_t)gi * E.ld_cin + gj];
-      if (gi == gj) v += E.diag;
-      if (E.out_f32) E.out_f32[(int64_t)b * E.bs_f32 + (int64_t)gi * E.ld_f32 + gj] = v;
-      if (E.out_hi || E.out_lo) {
-        const uint16_t h = f32_to_bf16(v);
-        if (E.out_hi) E.out_hi[(int64_t)b * E.bs_hi + (int64_t)gi * E.ld_hi + gj] = h;
-        if (E.out_lo) E.out_lo[(int64_t)b * E.bs_lo + (int64_t)gi * E.ld_lo + gj] = f32_to_bf16(v - bf16_to_f32(h));
+          for (int q = 0; q < 4; ++q) {
+            v[q] *= alpha;
+            if (EPI & E_CIN) v[q] += beta * cin[(int64_t)(gi + q) * p.epi.ld_cin + gj];
+            if ((EPI & E_DIAG) && gi + q == gj) v[q] += diag;
+          }
+          if (EPI & E_F32) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) of32[(int64_t)(gi + q) * p.epi.ld_f32 + gj] = v[q];
+            if (mirror) *(f32x4_t*)(of32 + (int64_t)gj * p.epi.ld_f32 + gi) = f32x4_t{v[0], v[1], v[2], v[3]};
+          }
+          uint16_t h[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) h[q] = f32_to_bf16(v[q]);
+          if (EPI & E_HI) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ohi[(int64_t)(gi + q) * p.epi.ld_hi + gj] = h[q];
+            if (mirror) *(u16x4_t*)(ohi + (int64_t)gj * p.epi.ld_hi + gi) = u16x4_t{h[0], h[1], h[2], h[3]};
+          }
+          if (EPI & E_LO) {
+            uint16_t l[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) l[q] = f32_to_bf16(v[q] - bf16_to_f32(h[q]));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) olo[(int64_t)(gi + q) * p.epi.ld_lo + gj] = l[q];
+            if (mirror) *(u16x4_t*)(olo + (int64_t)gj * p.epi.ld_lo + gi) = u16x4_t{l[0], l[1], l[2], l[3]};
+          }
+          if (EPI & E_T) *(u16x4_t*)(ot + (int64_t)gj * p.epi.ld_t + gi) = u16x4_t{h[0], h[1], h[2], h[3]};
+        }
       }
     }
-    // transposed pass: consecutive lanes take consecutive rows of the band
-    if (!part && p.epi.out_t) {
-      const GemmEpi& E = p.epi;
-      for (int e = lane; e < 32 * WTN; e += 64) {
-        const int cc = e >> 5, rr = e & 31;
-        const int gi = gi0 + rr, gj = gj0 + cc;
-        if (gi >= p.M || gj >= p.N) continue;
-        float v = E.alpha * sc * band[rr * RLD + cc];
-        if (E.cin) v += E.beta * E.cin[(int64_t)b * E.bs_cin + (int64_t)gi * E.ld_cin + gj];
-        if (gi == gj) v += E.diag;
-        E.out_t[(int64_t)b * E.bs_t + (int64_t)gj * E.ld_t + gi] = f32_to_bf16(v);
-      }
-    }
-    __syncthreads();
-  }
+  };
+  FragVisit<0, FM * FN, FN>::run(acc, frag_out);
 }
 
 // Deterministic split-K finish: fixed-order sum of the partial tiles, then the
@@ -236,13 +331,33 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs p) {
   }
 }
 
-hipError_t launch_ns_gemm(GemmTile tile, const GemmArgs& a, hipStream_t s) {
-  const int total = a.tiles_m * a.tiles_n * a.splits * a.batch;
-  if (total <= 0) return hipSuccess;
+template <int EPI>
+static void launch_epi(GemmTile tile, const GemmArgs& a, int total, hipStream_t s) {
   switch (tile) {
-    case TILE_256: ns_gemm_kernel<256, 256><<<total, 256, 0, s>>>(a); break;
-    case TILE_128: ns_gemm_kernel<128, 128><<<total, 256, 0, s>>>(a); break;
-    default:       ns_gemm_kernel<64, 64><<<total, 256, 0, s>>>(a); break;
+    case TILE_256: ns_gemm_kernel<256, 256, EPI><<<total, 256, 0, s>>>(a); break;
+    case TILE_128: ns_gemm_kernel<128, 128, EPI><<<total, 256, 0, s>>>(a); break;
+    default:       ns_gemm_kernel<64, 64, EPI><<<total, 256, 0, s>>>(a); break;
+  }
+}
+
+int gemm_tile_count(const GemmArgs& a, GemmKind kind) {
+  const bool sym = a.splits == 1 && (kind == GEMM_GRAM || kind == GEMM_POLY);
+  return sym ? a.tiles_m * (a.tiles_m + 1) / 2 : a.tiles_m * a.tiles_n;
+}
+
+hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const GemmArgs& a, hipStream_t s) {
+  const int total = gemm_tile_count(a, kind) * a.splits * a.batch;
+  if (total <= 0) return hipSuccess;
+  if (a.splits > 1) {
+    launch_epi<E_PART>(tile, a, total, s);
+  } else if (kind == GEMM_GRAM) {
+    if (split_pair) launch_epi<E_SYM | E_F32 | E_HI | E_LO>(tile, a, total, s);
+    else launch_epi<E_SYM | E_F32 | E_HI>(tile, a, total, s);
+  } else if (kind == GEMM_POLY) {
+    if (split_pair) launch_epi<E_SYM | E_CIN | E_DIAG | E_HI | E_LO>(tile, a, total, s);
+    else launch_epi<E_SYM | E_CIN | E_DIAG | E_HI>(tile, a, total, s);
+  } else {
+    launch_epi<E_HI | E_T>(tile, a, total, s);
   }
   return hipGetLastError();
 }
