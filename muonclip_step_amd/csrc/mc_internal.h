@@ -24,7 +24,7 @@ __host__ __device__ inline float bf16_to_f32(uint16_t h) {
 
 // One K segment of C = sum_s A_s B_s^T; both operands are bf16 row-major with
 // the contraction index contiguous ("NT" form).
-constexpr int kGemmBK = 32;   // k per pipeline stage of the NS GEMM
+constexpr int kGemmBK = 64;   // k per pipeline stage of the NS GEMM
 
 struct GemmSeg {
   const uint16_t* a;

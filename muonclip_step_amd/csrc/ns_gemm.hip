@@ -57,12 +57,13 @@ __device__ __attribute__((always_inline)) inline float batch_scale(const GemmEpi
   return e.scale_pow == 1 ? s : s * s;
 }
 
-// Chunk swizzle of a 64-byte LDS row (four 16-byte chunks): row r stores
-// logical chunk c at c ^ swz(r). With rows grouped four to a 256-byte bank
-// window, the four rows that share bank positions get four different chunk
-// slots; the SQ_LDS_BANK_CONFLICT counter reads zero for the fragment reads
-// of this kernel with this mapping on gfx950.
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+// Chunk swizzle of a 128-byte LDS row (eight 16-byte chunks): row r stores
+// logical chunk c at c ^ swz(r). Chosen from the SQ_LDS_BANK_CONFLICT counter
+// of this kernel's fragment reads on gfx950 (which the swizzle drives to zero).
+#ifndef MC_SWZ128
+#define MC_SWZ128(r) (((r) >> 1) & 7)
+#endif
+__device__ __forceinline__ int swz(int r) { return MC_SWZ128(r); }
 
 // Calls f(acc[I / FN][I % FN], I / FN, I % FN) for I = I0 .. N-1 with every
 // index a compile-time constant (keeps the accumulators in registers).
@@ -97,16 +98,20 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at max)
 #define MC_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | 0x70 | 0xF00 | (((n) >> 4) << 14))
 
-template <int BM, int BN, int EPI>
+template <int BM, int BN, int NSTAGE, int EPI>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 ns_gemm_kernel(const GemmArgs p) {
-  constexpr int BK = 32, NSTAGE = 4;
+  constexpr int BK = kGemmBK;                     // 64: one 128-byte row segment per operand row
+  constexpr int KK = BK / 16;                     // MFMA k-steps per stage
   constexpr int WTM = BM / 2, WTN = BN / 2;       // 2 x 2 waves
   constexpr int FM = WTM / 32, FN = WTN / 32;     // 32x32 fragments per wave
-  constexpr int ROWB = BK * 2;                    // bytes per LDS row (64)
+  constexpr int ROWB = BK * 2;                    // bytes per LDS row (128)
+  constexpr int CPR = ROWB / 16;                  // 16-byte chunks per row (8)
+  constexpr int RPI = 64 / CPR;                   // rows per DMA instruction (8)
   constexpr int STAGE = (BM + BN) * ROWB;         // bytes per stage
-  constexpr int IA = BM / 64, IB = BN / 64;       // DMA instructions per wave per stage (16 rows each)
+  constexpr int IA = BM / 4 / RPI, IB = BN / 4 / RPI;   // DMA instructions per wave per stage
   static_assert(STAGE * NSTAGE <= 160 * 1024, "LDS");
+  static_assert((KK % 2) == 0, "two fragment slots");
   __shared__ __attribute__((aligned(1024))) char lds[STAGE * NSTAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -136,22 +141,24 @@ ns_gemm_kernel(const GemmArgs p) {
   const int nk = kt_end - kt_begin;
 
   // Per-lane DMA source offsets (elements, without k): DMA instruction i of
-  // this wave fills tile rows 16*(wave*IA + i) .. +15; lane l lands at LDS
-  // slot l of that 1 KB block = row l/4, physical chunk l%4, so it fetches
-  // logical chunk (l%4) ^ swz(row). Rows past M / N re-read the last row;
+  // this wave fills tile rows RPI*(wave*IA + i) .. +RPI-1; lane l lands at LDS
+  // slot l of that 1 KB block = row l/CPR, physical chunk l%CPR, so it fetches
+  // logical chunk (l%CPR) ^ swz(row). Rows past M / N re-read the last row;
   // they only feed outputs that are never stored.
-  int64_t offA[IA], offB[IB];
+  // (32-bit: a row offset is below rows * ld < 2^31 for every matrix this
+  // library accepts; batch offsets are applied to the base pointers)
+  int offA[IA], offB[IB];
 #pragma unroll
   for (int i = 0; i < IA; ++i) {
-    const int r = 16 * (wave * IA + i) + (lane >> 2);
+    const int r = RPI * (wave * IA + i) + lane / CPR;
     const int gr = min(m0 + r, p.M - 1);
-    offA[i] = (int64_t)gr * p.lda + (((lane & 3) ^ swz(r)) * 8);
+    offA[i] = gr * p.lda + (((lane % CPR) ^ swz(r)) * 8);
   }
 #pragma unroll
   for (int i = 0; i < IB; ++i) {
-    const int r = 16 * (wave * IB + i) + (lane >> 2);
+    const int r = RPI * (wave * IB + i) + lane / CPR;
     const int gr = min(n0 + r, p.N - 1);
-    offB[i] = (int64_t)gr * p.ldb + (((lane & 3) ^ swz(r)) * 8);
+    offB[i] = gr * p.ldb + (((lane % CPR) ^ swz(r)) * 8);
   }
 
   // segment bases and boundaries, read from the kernel arguments once so the
@@ -179,10 +186,10 @@ ns_gemm_kernel(const GemmArgs p) {
     char* base_ = lds + ((kt_) % NSTAGE) * STAGE;                                        \
     _Pragma("unroll") for (int i = 0; i < IA; ++i)                                       \
       __builtin_amdgcn_global_load_lds((const void*)(A_ + offA[i]),                      \
-          (lds_void_t*)(base_ + (16 * (wave * IA + i)) * ROWB), 16, 0, 0);               \
+          (lds_void_t*)(base_ + (RPI * (wave * IA + i)) * ROWB), 16, 0, 0);              \
     _Pragma("unroll") for (int i = 0; i < IB; ++i)                                       \
       __builtin_amdgcn_global_load_lds((const void*)(B_ + offB[i]),                      \
-          (lds_void_t*)(base_ + BM * ROWB + (16 * (wave * IB + i)) * ROWB), 16, 0, 0);   \
+          (lds_void_t*)(base_ + BM * ROWB + (RPI * (wave * IB + i)) * ROWB), 16, 0, 0);  \
   }
 
   f32x16_t acc[FM][FN];
@@ -192,20 +199,30 @@ ns_gemm_kernel(const GemmArgs p) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
   bf16x8_t af[2][FM], bfr[2][FN];
 
-  // fragment reads of k-step kk_ (16 k) of stage kt_ into register slot sl_
+  // Fragment reads of k-step kk_ (16 k) of stage kt_ into register slot sl_.
+  // They are issued as inline ds_read_b128 so the compiler does not track
+  // them: its LDS-counter analysis is conservative across the loop back-edge
+  // and would wait for every outstanding read before each MFMA block. The
+  // loop instead waits explicitly (MC_WAIT_LGKM) for exactly the older batch;
+  // no other LDS-counter operation is in flight inside the loop.
+  const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds);
 #define MC_FRAG(kt_, kk_, sl_)                                                           \
   {                                                                                      \
-    const char* base_ = lds + ((kt_) % NSTAGE) * STAGE;                                  \
+    const uint32_t base_ = lds_base + ((kt_) % NSTAGE) * STAGE;                          \
     const int c_ = (kk_) * 2 + (lane >> 5);                                              \
     _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                     \
       const int r_ = wm * WTM + i * 32 + (lane & 31);                                    \
-      af[(sl_)][i] = *(const bf16x8_t*)(base_ + r_ * ROWB + ((c_ ^ swz(r_)) << 4));      \
+      const uint32_t ad_ = base_ + r_ * ROWB + ((c_ ^ swz(r_)) << 4);                    \
+      asm volatile("ds_read_b128 %0, %1" : "=v"(af[(sl_)][i]) : "v"(ad_));              \
     }                                                                                    \
     _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                     \
       const int r_ = wn * WTN + j * 32 + (lane & 31);                                    \
-      bfr[(sl_)][j] = *(const bf16x8_t*)(base_ + BM * ROWB + r_ * ROWB + ((c_ ^ swz(r_)) << 4)); \
+      const uint32_t ad_ = base_ + BM * ROWB + r_ * ROWB + ((c_ ^ swz(r_)) << 4);        \
+      asm volatile("ds_read_b128 %0, %1" : "=v"(bfr[(sl_)][j]) : "v"(ad_));             \
     }                                                                                    \
   }
+  // wait until at most n_ fragment reads are outstanding
+#define MC_WAIT_LGKM(n_) asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(n_))
 #define MC_MMA(sl_)                                                                      \
   {                                                                                      \
     _Pragma("unroll") for (int i = 0; i < FM; ++i)                                       \
@@ -214,43 +231,106 @@ ns_gemm_kernel(const GemmArgs p) {
                                                             acc[i][j], 0, 0, 0);         \
   }
 
-  // Pipeline: stages are fetched 3 ahead into a 4-slot LDS ring by DMA; one
-  // barrier per stage, placed between the stage's two k-steps, publishes the
-  // next stage and retires the slot the new DMA overwrites; the fragments of
-  // each k-step are read while the previous k-step's MFMAs run.
+  // One k-step, interleaved: MFMA m of register slot sl_, then fragment read
+  // m of the next k-step (stage rkt_, k-step rkk_, into slot rsl_; if rd_),
+  // then DMA instruction m of stage dkt_ (if dma_). Spreading the memory
+  // instructions between MFMAs keeps the in-order issue from stalling the
+  // matrix core behind a burst of loads.
+  constexpr int NSTEP = (FM * FN > FM + FN ? FM * FN : FM + FN) > IA + IB
+                            ? (FM * FN > FM + FN ? FM * FN : FM + FN) : IA + IB;
+#define MC_STEP(sl_, rd_, rkt_, rkk_, rsl_, dma_, dkt_)                                  \
+  {                                                                                      \
+    const uint32_t rb_ = lds_base + ((rkt_) % NSTAGE) * STAGE;                           \
+    const int rc_ = (rkk_) * 2 + (lane >> 5);                                            \
+    const int dkg_ = kt_begin + (dkt_);                                                  \
+    const uint16_t* dA_ = A0;                                                            \
+    const uint16_t* dB_ = B0;                                                            \
+    int dkl_ = dkg_;                                                                     \
+    if (dkg_ >= kb1) { dA_ = A2; dB_ = B2; dkl_ = dkg_ - kb1; }                          \
+    else if (dkg_ >= kb0) { dA_ = A1; dB_ = B1; dkl_ = dkg_ - kb0; }                     \
+    dA_ += dkl_ * BK;                                                                    \
+    dB_ += dkl_ * BK;                                                                    \
+    char* db_ = lds + ((dkt_) % NSTAGE) * STAGE;                                         \
+    _Pragma("unroll") for (int m = 0; m < NSTEP; ++m) {                                  \
+      if (m < FM * FN)                                                                   \
+        acc[m / FN][m % FN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                   \
+            af[(sl_)][m / FN], bfr[(sl_)][m % FN], acc[m / FN][m % FN], 0, 0, 0);        \
+      __builtin_amdgcn_sched_barrier(0);                                                 \
+      if ((rd_) && m < FM) {                                                             \
+        const int r_ = wm * WTM + m * 32 + (lane & 31);                                  \
+        const uint32_t ad_ = rb_ + r_ * ROWB + ((rc_ ^ swz(r_)) << 4);                   \
+        asm volatile("ds_read_b128 %0, %1" : "=v"(af[(rsl_)][m < FM ? m : 0]) : "v"(ad_)); \
+      } else if ((rd_) && m < FM + FN) {                                                 \
+        const int j_ = m - FM;                                                           \
+        const int r_ = wn * WTN + j_ * 32 + (lane & 31);                                 \
+        const uint32_t ad_ = rb_ + BM * ROWB + r_ * ROWB + ((rc_ ^ swz(r_)) << 4);       \
+        asm volatile("ds_read_b128 %0, %1" : "=v"(bfr[(rsl_)][j_ < FN ? j_ : 0]) : "v"(ad_)); \
+      }                                                                                  \
+      if ((dma_) && m < IA) {                                                            \
+        __builtin_amdgcn_global_load_lds((const void*)(dA_ + offA[m < IA ? m : 0]),      \
+            (lds_void_t*)(db_ + (RPI * (wave * IA + m)) * ROWB), 16, 0, 0);              \
+      } else if ((dma_) && m < IA + IB) {                                                \
+        const int i_ = m - IA;                                                           \
+        __builtin_amdgcn_global_load_lds((const void*)(dB_ + offB[i_ < IB ? i_ : 0]),    \
+            (lds_void_t*)(db_ + BM * ROWB + (RPI * (wave * IB + i_)) * ROWB), 16, 0, 0); \
+      }                                                                                  \
+      __builtin_amdgcn_sched_barrier(0);                                                 \
+    }                                                                                    \
+  }
+
+  // Pipeline over an NSTAGE-slot LDS ring: the prologue fetches stages
+  // 0..NSTAGE-1; stage kt lives in slot kt % NSTAGE. Within a stage the
+  // fragments of k-step kk+1 are read while the MFMAs of k-step kk run (two
+  // register slots). Before the last k-step of stage kt every wave has all of
+  // stage kt's fragments in registers; the block then waits for stage kt+1
+  // to land, synchronises once (publishing stage kt+1 and retiring slot
+  // kt % NSTAGE), refills that slot with stage kt+NSTAGE, and reads the first
+  // fragments of stage kt+1 under the last k-step's MFMAs.
+#define MC_WAIT_STAGES(n_)                                                               \
+  {                                                                                      \
+    if ((n_) >= 3) MC_WAIT_VMCNT(3 * (IA + IB));                                         \
+    else if ((n_) == 2) MC_WAIT_VMCNT(2 * (IA + IB));                                    \
+    else if ((n_) == 1) MC_WAIT_VMCNT(IA + IB);                                          \
+    else MC_WAIT_VMCNT(0);                                                               \
+  }
   if (nk > 0) {
-    const int pre = min(NSTAGE - 1, nk);
+    const int pre = min(NSTAGE, nk);
     for (int s = 0; s < pre; ++s) MC_ISSUE(s);
-    if (pre == 3) MC_WAIT_VMCNT(2 * (IA + IB));
-    else if (pre == 2) MC_WAIT_VMCNT(IA + IB);
-    else MC_WAIT_VMCNT(0);
+    MC_WAIT_STAGES(pre - 1);            // stage 0 landed; the rest may stay in flight
     __builtin_amdgcn_s_barrier();
     MC_FRAG(0, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
-      MC_FRAG(kt, 1, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      MC_MMA(0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kt + 1 < nk) {
-        if (kt + 2 < nk) MC_WAIT_VMCNT(IA + IB);
-        else MC_WAIT_VMCNT(0);
-        __builtin_amdgcn_s_barrier();
-        if (kt + 3 < nk) MC_ISSUE(kt + 3);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        MC_WAIT_LGKM(0);                // this k-step's fragments landed
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk + 1 < KK) {
+          MC_STEP(kk & 1, true, kt, kk + 1, (kk + 1) & 1, false, kt);
+        } else {
+          // all of stage kt is in registers: its slot can be refilled
+          const bool more = kt + 1 < nk;
+          if (more) {
+            // stage kt+1 landed; issued stages kt+2 .. min(kt+NSTAGE-1, nk-1) may stay in flight
+            MC_WAIT_STAGES(min(kt + NSTAGE - 1, nk - 1) - (kt + 1));
+            __builtin_amdgcn_s_barrier();
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          // first fragments of stage kt+1 (after the last stage: a stale slot,
+          // values unused) and, when there is one, the DMA of stage kt+NSTAGE
+          MC_STEP(kk & 1, true, kt + 1, 0, 0, more && kt + NSTAGE < nk, kt + NSTAGE);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      // k-step 0 of the next stage (visible after the barrier); after the last
-      // stage this reads a stale ring slot whose values are never used, which
-      // keeps the LDS counter waits exact
-      MC_FRAG(kt + 1, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      MC_MMA(1);
-      __builtin_amdgcn_sched_barrier(0);
     }
+    MC_WAIT_LGKM(0);
   }
+#undef MC_WAIT_STAGES
   MC_WAIT_VMCNT(0);
 #undef MC_MMA
 #undef MC_FRAG
 #undef MC_ISSUE
+#undef MC_WAIT_LGKM
+#undef MC_STEP
 
   // Epilogue straight from the accumulators: register 4g+q of lane l holds
   // row 8g + 4(l/32) + q, column l%32 of its 32x32 fragment, i.e. each lane
@@ -334,9 +414,9 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs p) {
 template <int EPI>
 static void launch_epi(GemmTile tile, const GemmArgs& a, int total, hipStream_t s) {
   switch (tile) {
-    case TILE_256: ns_gemm_kernel<256, 256, EPI><<<total, 256, 0, s>>>(a); break;
-    case TILE_128: ns_gemm_kernel<128, 128, EPI><<<total, 256, 0, s>>>(a); break;
-    default:       ns_gemm_kernel<64, 64, EPI><<<total, 256, 0, s>>>(a); break;
+    case TILE_256: ns_gemm_kernel<256, 256, 2, EPI><<<total, 256, 0, s>>>(a); break;
+    case TILE_128: ns_gemm_kernel<128, 128, 2, EPI><<<total, 256, 0, s>>>(a); break;
+    default:       ns_gemm_kernel<64, 64, 2, EPI><<<total, 256, 0, s>>>(a); break;
   }
 }
 
