@@ -41,7 +41,50 @@ def parse():
     ap.add_argument("--experts", type=int, default=385, help="expert count for workloads 4/5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-s", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain streaming copy of MIB MiB (read + write) five times, "
+                         "to calibrate the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ns_gemm_traffic_mha_layer.txt")
+GEMM_SOURCE = os.path.join(ROOT, "muonclip_step_amd", "csrc", "ns_gemm.hip")
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    with open(GEMM_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per ns_gemm launch from the committed rocprofv3 counter runs,
+    or None when they were taken on another workload or another kernel source."""
+    if workload != "mha_layer" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("ns_gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib: int):
+    """A plain streaming kernel of known size: reads and writes mib MiB."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": 5}), flush=True)
 
 
 def ns_flops(rows, cols, steps):
@@ -142,6 +185,10 @@ def main():
         sys.exit(2)
     import torch
 
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
     import muonclip_step_amd as mc
     import workloads as wl
 
@@ -235,7 +282,7 @@ def main():
         "kernels_ms_per_step": {k: round(v["ms"], 4) for k, v in per_step.items()},
         "roofline": {"bound": "mfma", "kernel": "ns_gemm", "achieved": round(gemm_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(cfg.name),
                      "launches_per_step": per_step.get("ns_gemm", {}).get("launches"),
                      "avg_launch_us": round(g["ms"] / max(1, g["launches"]) * 1e3, 2)},
         "cpu_baseline": cpu,
