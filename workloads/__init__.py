@@ -20,7 +20,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-KIND_W, KIND_G, KIND_M, KIND_X = 0, 1, 2, 3
+KIND_W, KIND_G, KIND_M, KIND_X, KIND_S = 0, 1, 2, 3, 4
 
 # Hyper-parameters of the step, as the configurations use them.
 DEFAULT_HPARAMS = dict(lr=2e-4, mu=0.95, weight_decay=0.1, rms_scale=0.2,
@@ -279,6 +279,16 @@ def draw_attention_inputs(cfg: Config, weights: dict):
     kv_b = weights["kv_b"].reshape(H, 256, 512)[:, :128, :].reshape(H * 128, 512)
     k_c = quantize_bf16(_matmul_f32(c_kv, kv_b.T)).reshape(a.B, a.T, H, 128)
     return q, k_c, k_r
+
+
+def draw_smax(cfg: Config, n_over: int = 4) -> np.ndarray:
+    """A per-head max-logit vector standing in for a forward pass (float32):
+    heads below n_over lie in (1.1, 4) x tau, the rest in (0.1, 0.95) x tau."""
+    a = cfg.attn
+    u = stream(cfg.seed, tensor_id(len(cfg.matrices), KIND_S)).uniform(size=a.H)
+    s = cfg.tau * (0.1 + 0.85 * u)
+    s[:n_over] = cfg.tau * (1.1 + 2.9 * u[:n_over])
+    return quantize_f32(s)
 
 
 def elements(cfg: Config) -> int:
