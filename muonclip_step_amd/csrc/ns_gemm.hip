@@ -13,12 +13,16 @@
 //
 // gfx950 design: v_mfma_f32_32x32x16_bf16 with fp32 accumulation; a block of
 // 2x2 waves owns a BMxBN tile, each wave a (BM/2)x(BN/2) sub-tile. K advances
-// in 32-wide stages held in a 4-slot LDS ring that direct-to-LDS loads
-// (global_load_lds_dwordx4) fill three stages ahead, so no register staging
-// is needed; one barrier per stage publishes the next stage; the MFMA
-// fragments of each 16-k step are read from LDS while the previous step's
-// MFMAs run. The epilogue is specialised at compile time per use and stores
-// straight from the accumulator registers.
+// in 64-wide stages (one 128-byte row segment per operand row) held in a
+// two-slot LDS ring that direct-to-LDS loads (global_load_lds_dwordx4) fill,
+// so no register staging is needed. One barrier per stage retires a slot;
+// the loads of the stage after next go out in two halves, under the last
+// k-step of one stage and the first k-step of the next, each load placed
+// between two MFMAs, and every memory instruction of the steady-state loop
+// is unconditional (the last stage is peeled). The MFMA fragments of each
+// 16-k step are read from LDS while the previous step's MFMAs run. The
+// epilogue is specialised at compile time per use and stores straight from
+// the accumulator registers.
 #include "mc_internal.h"
 
 namespace mc {
@@ -114,7 +118,8 @@ ns_gemm_kernel(const GemmArgs p) {
   static_assert((KK % 2) == 0, "two fragment slots");
   __shared__ __attribute__((aligned(1024))) char lds[STAGE * NSTAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS targets stay scalar
   const int wm = wave >> 1, wn = wave & 1;
 
   const int tiles = (EPI & E_SYM) ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
@@ -172,24 +177,31 @@ ns_gemm_kernel(const GemmArgs p) {
   const uint16_t* A2 = nseg > 2 ? p.seg[2].a + (int64_t)b * p.bsa : A1;
   const uint16_t* B2 = nseg > 2 ? p.seg[2].b + (int64_t)b * p.bsb : B1;
 
-  // issue the DMA of k-stage kt_ (relative to kt_begin) into ring slot kt_ % NSTAGE
-#define MC_ISSUE(kt_)                                                                    \
+  // Source pointers of k-stage st_ (relative to kt_begin): the segment that
+  // holds it and the k offset inside that segment.
+#define MC_STAGE_SRC(st_, dA_, dB_)                                                      \
+  const uint16_t* dA_ = A0;                                                              \
+  const uint16_t* dB_ = B0;                                                              \
   {                                                                                      \
-    const int kg_ = kt_begin + (kt_);                                                    \
-    const uint16_t* A_ = A0;                                                             \
-    const uint16_t* B_ = B0;                                                             \
+    const int kg_ = kt_begin + (st_);                                                    \
     int kl_ = kg_;                                                                       \
-    if (kg_ >= kb1) { A_ = A2; B_ = B2; kl_ = kg_ - kb1; }                               \
-    else if (kg_ >= kb0) { A_ = A1; B_ = B1; kl_ = kg_ - kb0; }                          \
-    A_ += kl_ * BK;                                                                      \
-    B_ += kl_ * BK;                                                                      \
-    char* base_ = lds + ((kt_) % NSTAGE) * STAGE;                                        \
-    _Pragma("unroll") for (int i = 0; i < IA; ++i)                                       \
-      __builtin_amdgcn_global_load_lds((const void*)(A_ + offA[i]),                      \
-          (lds_void_t*)(base_ + (RPI * (wave * IA + i)) * ROWB), 16, 0, 0);              \
-    _Pragma("unroll") for (int i = 0; i < IB; ++i)                                       \
-      __builtin_amdgcn_global_load_lds((const void*)(B_ + offB[i]),                      \
-          (lds_void_t*)(base_ + BM * ROWB + (RPI * (wave * IB + i)) * ROWB), 16, 0, 0);  \
+    if (kg_ >= kb1) { dA_ = A2; dB_ = B2; kl_ = kg_ - kb1; }                             \
+    else if (kg_ >= kb0) { dA_ = A1; dB_ = B1; kl_ = kg_ - kb0; }                        \
+    dA_ += kl_ * BK;                                                                     \
+    dB_ += kl_ * BK;                                                                     \
+  }
+  // DMA instruction j_ (compile-time) of a stage: j_ < IA fill A rows, the
+  // rest B rows; db_ is the stage's LDS slot
+#define MC_DMA(j_, dA_, dB_, db_)                                                        \
+  {                                                                                      \
+    if ((j_) < IA) {                                                                     \
+      __builtin_amdgcn_global_load_lds((const void*)(dA_ + offA[(j_) < IA ? (j_) : 0]),  \
+          (lds_void_t*)(db_ + (RPI * (wave * IA + (j_))) * ROWB), 16, 0, 0);             \
+    } else {                                                                             \
+      const int i_ = (j_) - IA >= 0 && (j_) - IA < IB ? (j_) - IA : 0;                   \
+      __builtin_amdgcn_global_load_lds((const void*)(dB_ + offB[i_]),                    \
+          (lds_void_t*)(db_ + BM * ROWB + (RPI * (wave * IB + i_)) * ROWB), 16, 0, 0);   \
+    }                                                                                    \
   }
 
   f32x16_t acc[FM][FN];
@@ -203,8 +215,11 @@ ns_gemm_kernel(const GemmArgs p) {
   // They are issued as inline ds_read_b128 so the compiler does not track
   // them: its LDS-counter analysis is conservative across the loop back-edge
   // and would wait for every outstanding read before each MFMA block. The
-  // loop instead waits explicitly (MC_WAIT_LGKM) for exactly the older batch;
-  // no other LDS-counter operation is in flight inside the loop.
+  // compiler therefore also takes their destination registers as written
+  // when the asm issues: every k-step ends with an explicit wait
+  // (MC_WAIT_LGKM(0)) for the reads it issued, so no read is in flight at a
+  // block boundary, where register allocation may copy those registers.
+  // No other LDS-counter operation is in flight inside the loop.
   const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds);
 #define MC_FRAG(kt_, kk_, sl_)                                                           \
   {                                                                                      \
@@ -223,34 +238,23 @@ ns_gemm_kernel(const GemmArgs p) {
   }
   // wait until at most n_ fragment reads are outstanding
 #define MC_WAIT_LGKM(n_) asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(n_))
-#define MC_MMA(sl_)                                                                      \
-  {                                                                                      \
-    _Pragma("unroll") for (int i = 0; i < FM; ++i)                                       \
-      _Pragma("unroll") for (int j = 0; j < FN; ++j)                                     \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[(sl_)][i], bfr[(sl_)][j], \
-                                                            acc[i][j], 0, 0, 0);         \
-  }
-
   // One k-step, interleaved: MFMA m of register slot sl_, then fragment read
   // m of the next k-step (stage rkt_, k-step rkk_, into slot rsl_; if rd_),
-  // then DMA instruction m of stage dkt_ (if dma_). Spreading the memory
-  // instructions between MFMAs keeps the in-order issue from stalling the
-  // matrix core behind a burst of loads.
+  // then, spaced evenly over the MFMAs, DMA instructions d0_ .. d1_-1 of
+  // stage dsrc_ into the ring slot of stage dkt_ (if dma_). Spreading the
+  // memory instructions between MFMAs keeps the in-order issue from stalling
+  // the matrix core behind a burst of loads. Every flag and count is a
+  // compile-time constant at each use, so no branch enters the MFMA stream.
   constexpr int NSTEP = (FM * FN > FM + FN ? FM * FN : FM + FN) > IA + IB
                             ? (FM * FN > FM + FN ? FM * FN : FM + FN) : IA + IB;
-#define MC_STEP(sl_, rd_, rkt_, rkk_, rsl_, dma_, dkt_)                                  \
+#define MC_STEP(sl_, rd_, rkt_, rkk_, rsl_, dma_, dsrc_, dkt_, d0_, d1_)                 \
   {                                                                                      \
     const uint32_t rb_ = lds_base + ((rkt_) % NSTAGE) * STAGE;                           \
     const int rc_ = (rkk_) * 2 + (lane >> 5);                                            \
-    const int dkg_ = kt_begin + (dkt_);                                                  \
-    const uint16_t* dA_ = A0;                                                            \
-    const uint16_t* dB_ = B0;                                                            \
-    int dkl_ = dkg_;                                                                     \
-    if (dkg_ >= kb1) { dA_ = A2; dB_ = B2; dkl_ = dkg_ - kb1; }                          \
-    else if (dkg_ >= kb0) { dA_ = A1; dB_ = B1; dkl_ = dkg_ - kb0; }                     \
-    dA_ += dkl_ * BK;                                                                    \
-    dB_ += dkl_ * BK;                                                                    \
+    MC_STAGE_SRC(dsrc_, dA_, dB_)                                                        \
     char* db_ = lds + ((dkt_) % NSTAGE) * STAGE;                                         \
+    const int dn_ = (d1_) - (d0_);                                                       \
+    const int ds_ = NSTEP / (dn_ > 0 ? dn_ : 1) > 0 ? NSTEP / (dn_ > 0 ? dn_ : 1) : 1;     \
     _Pragma("unroll") for (int m = 0; m < NSTEP; ++m) {                                  \
       if (m < FM * FN)                                                                   \
         acc[m / FN][m % FN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                   \
@@ -266,69 +270,78 @@ ns_gemm_kernel(const GemmArgs p) {
         const uint32_t ad_ = rb_ + BM * ROWB + r_ * ROWB + ((rc_ ^ swz(r_)) << 4);       \
         asm volatile("ds_read_b128 %0, %1" : "=v"(bfr[(rsl_)][j_ < FN ? j_ : 0]) : "v"(ad_)); \
       }                                                                                  \
-      if ((dma_) && m < IA) {                                                            \
-        __builtin_amdgcn_global_load_lds((const void*)(dA_ + offA[m < IA ? m : 0]),      \
-            (lds_void_t*)(db_ + (RPI * (wave * IA + m)) * ROWB), 16, 0, 0);              \
-      } else if ((dma_) && m < IA + IB) {                                                \
-        const int i_ = m - IA;                                                           \
-        __builtin_amdgcn_global_load_lds((const void*)(dB_ + offB[i_ < IB ? i_ : 0]),    \
-            (lds_void_t*)(db_ + BM * ROWB + (RPI * (wave * IB + i_)) * ROWB), 16, 0, 0); \
-      }                                                                                  \
+      if ((dma_) && dn_ > 0 && m % ds_ == 0 && (d0_) + m / ds_ < (d1_))                  \
+        MC_DMA((d0_) + m / ds_, dA_, dB_, db_);                                          \
       __builtin_amdgcn_sched_barrier(0);                                                 \
     }                                                                                    \
   }
 
-  // Pipeline over an NSTAGE-slot LDS ring: the prologue fetches stages
-  // 0..NSTAGE-1; stage kt lives in slot kt % NSTAGE. Within a stage the
-  // fragments of k-step kk+1 are read while the MFMAs of k-step kk run (two
-  // register slots). Before the last k-step of stage kt every wave has all of
-  // stage kt's fragments in registers; the block then waits for stage kt+1
-  // to land, synchronises once (publishing stage kt+1 and retiring slot
-  // kt % NSTAGE), refills that slot with stage kt+NSTAGE, and reads the first
-  // fragments of stage kt+1 under the last k-step's MFMAs.
-#define MC_WAIT_STAGES(n_)                                                               \
-  {                                                                                      \
-    if ((n_) >= 3) MC_WAIT_VMCNT(3 * (IA + IB));                                         \
-    else if ((n_) == 2) MC_WAIT_VMCNT(2 * (IA + IB));                                    \
-    else if ((n_) == 1) MC_WAIT_VMCNT(IA + IB);                                          \
-    else MC_WAIT_VMCNT(0);                                                               \
-  }
+  // Pipeline over the two-slot ring; stage s lives in slot s % 2. Its loads
+  // go out in two halves: [0, DH) under the last k-step of stage s-2, right
+  // after the barrier that frees slot s % 2, and [DH, ND) under the first
+  // k-step of stage s-1. Before the last k-step of stage kt every wave holds
+  // all of stage kt's fragments in registers; the block then waits for
+  // stage kt+1 to land, synchronises once (publishing stage kt+1 and
+  // retiring slot kt % 2), and reads the first fragments of stage kt+1 under
+  // the last k-step's MFMAs.
+  static_assert(NSTAGE == 2, "the issue schedule assumes a two-slot ring");
+  constexpr int ND = IA + IB, DH = ND / 2;
   if (nk > 0) {
-    const int pre = min(NSTAGE, nk);
-    for (int s = 0; s < pre; ++s) MC_ISSUE(s);
-    MC_WAIT_STAGES(pre - 1);            // stage 0 landed; the rest may stay in flight
+    {   // prologue: all of stage 0, the first half of stage 1
+      MC_STAGE_SRC(0, sA_, sB_)
+#pragma unroll
+      for (int j = 0; j < ND; ++j) MC_DMA(j, sA_, sB_, lds);
+    }
+    if (nk > 1) {
+      MC_STAGE_SRC(1, sA_, sB_)
+#pragma unroll
+      for (int j = 0; j < DH; ++j) MC_DMA(j, sA_, sB_, lds + STAGE);
+      MC_WAIT_VMCNT(DH);                // stage 0 landed
+    } else {
+      MC_WAIT_VMCNT(0);
+    }
     __builtin_amdgcn_s_barrier();
     MC_FRAG(0, 0, 0);
-    for (int kt = 0; kt < nk; ++kt) {
+    MC_WAIT_LGKM(0);
+    // stages 0 .. nk-2. After the barrier that retires stage kt, the first
+    // half of stage kt+2 goes into the freed slot; for kt+2 == nk it
+    // re-reads stage nk-1 into that slot, which is never read again.
+    for (int kt = 0; kt < nk - 1; ++kt) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        MC_WAIT_LGKM(0);                // this k-step's fragments landed
-        __builtin_amdgcn_sched_barrier(0);
-        if (kk + 1 < KK) {
-          MC_STEP(kk & 1, true, kt, kk + 1, (kk + 1) & 1, false, kt);
+        if (kk == 0) {
+          MC_STEP(kk & 1, true, kt, kk + 1, (kk + 1) & 1, true, kt + 1, kt + 1, DH, ND);
+        } else if (kk + 1 < KK) {
+          MC_STEP(kk & 1, true, kt, kk + 1, (kk + 1) & 1, false, kt, kt, 0, 0);
         } else {
-          // all of stage kt is in registers: its slot can be refilled
-          const bool more = kt + 1 < nk;
-          if (more) {
-            // stage kt+1 landed; issued stages kt+2 .. min(kt+NSTAGE-1, nk-1) may stay in flight
-            MC_WAIT_STAGES(min(kt + NSTAGE - 1, nk - 1) - (kt + 1));
-            __builtin_amdgcn_s_barrier();
-          }
+          MC_WAIT_VMCNT(0);             // stage kt+1 landed (this wave's part)
+          __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_sched_barrier(0);
-          // first fragments of stage kt+1 (after the last stage: a stale slot,
-          // values unused) and, when there is one, the DMA of stage kt+NSTAGE
-          MC_STEP(kk & 1, true, kt + 1, 0, 0, more && kt + NSTAGE < nk, kt + NSTAGE);
+          const int src = min(kt + 2, nk - 1);
+          MC_STEP(kk & 1, true, kt + 1, 0, 0, true, src, kt + 2, 0, DH);
         }
+        MC_WAIT_LGKM(0);                // the next k-step's fragments landed
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    MC_WAIT_LGKM(0);
+    {   // last stage: no loads, no barrier
+      const int kt = nk - 1;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 1 < KK) {
+          MC_STEP(kk & 1, true, kt, kk + 1, (kk + 1) & 1, false, kt, kt, 0, 0);
+        } else {
+          MC_STEP(kk & 1, false, kt, 0, 0, false, kt, kt, 0, 0);
+        }
+        MC_WAIT_LGKM(0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
-#undef MC_WAIT_STAGES
   MC_WAIT_VMCNT(0);
-#undef MC_MMA
 #undef MC_FRAG
-#undef MC_ISSUE
+#undef MC_STAGE_SRC
+#undef MC_DMA
 #undef MC_WAIT_LGKM
 #undef MC_STEP
 
@@ -339,6 +352,7 @@ ns_gemm_kernel(const GemmArgs p) {
   // rows as one 8- or 16-byte vector.
   const float sc = (EPI & E_PART) ? 1.0f : batch_scale(p.epi, b);
   const float alpha = p.epi.alpha * sc, beta = p.epi.beta, diag = p.epi.diag;
+  static_assert(!(EPI & E_CIN) || (EPI & E_SYM), "cin is read transposed: symmetric products only");
   const bool mirror = (EPI & E_SYM) && tm != tn;
   const int64_t mn = (int64_t)p.M * p.N;
   float* part = (EPI & E_PART) ? p.partial + ((int64_t)split * p.batch + b) * mn : nullptr;
@@ -351,6 +365,19 @@ ns_gemm_kernel(const GemmArgs p) {
   // recursion so every accumulator index is a compile-time constant
   auto frag_out = [&](const f32x16_t& a, int fi, int fj) __attribute__((always_inline)) {
     const int gj = n0 + wn * WTN + fj * 32 + (lane & 31);
+    // cin is the symmetric A of the Gram step: rows gi..gi+3 at column gj
+    // are read as one 16-byte vector of row gj, issued for all four row
+    // groups before any is used (rows clamped in range; values of clamped
+    // rows are never stored)
+    f32x4_t c4[4];
+    if (EPI & E_CIN) {
+      const int cj = min(gj, p.N - 1);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ci = min(m0 + wm * WTM + fi * 32 + 8 * g + 4 * (lane >> 5), p.M - 4);
+        c4[g] = *(const f32x4_t*)(cin + (int64_t)cj * p.epi.ld_cin + ci);
+      }
+    }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int gi = m0 + wm * WTM + fi * 32 + 8 * g + 4 * (lane >> 5);   // rows gi..gi+3
@@ -363,7 +390,7 @@ ns_gemm_kernel(const GemmArgs p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             v[q] *= alpha;
-            if (EPI & E_CIN) v[q] += beta * cin[(int64_t)(gi + q) * p.epi.ld_cin + gj];
+            if (EPI & E_CIN) v[q] += beta * c4[g][q];
             if ((EPI & E_DIAG) && gi + q == gj) v[q] += diag;
           }
           if (EPI & E_F32) {
@@ -428,6 +455,13 @@ int gemm_tile_count(const GemmArgs& a, GemmKind kind) {
 hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const GemmArgs& a, hipStream_t s) {
   const int total = gemm_tile_count(a, kind) * a.splits * a.batch;
   if (total <= 0) return hipSuccess;
+  // the epilogue moves four consecutive elements per lane: extents, leading
+  // dimensions and batch strides must be multiples of 4 elements
+  const GemmEpi& e = a.epi;
+  auto bad = [](const void* ptr, int64_t ld, int64_t bs) { return ptr && ((ld & 3) || (bs & 3)); };
+  if ((a.M & 3) || (a.N & 3) || bad(e.cin, e.ld_cin, e.bs_cin) || bad(e.out_f32, e.ld_f32, e.bs_f32) ||
+      bad(e.out_hi, e.ld_hi, e.bs_hi) || bad(e.out_lo, e.ld_lo, e.bs_lo) || bad(e.out_t, e.ld_t, e.bs_t))
+    return hipErrorInvalidValue;
   if (a.splits > 1) {
     launch_epi<E_PART>(tile, a, total, s);
   } else if (kind == GEMM_GRAM) {
