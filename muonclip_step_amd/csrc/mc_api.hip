@@ -5,16 +5,17 @@
 // wave, on the caller's stream:
 //   momentum_kernel   M <- mu M + G, norm partials, bf16 X0 in both layouts
 //   norm_finalize     s = 1 / (||M||_F + eps)
-//   5 x { Gram  A = s0^2 X X^T          -> A (fp32), A_hi (+ A_lo if m < 1024)
+//   5 x { Gram  A = s0^2 X X^T          -> A as a bf16 pair A_hi + A_lo
 //         Poly  P = a I + b A + c A A   -> P_hi (+ P_lo if m < 1024)
 //         Apply X' = s0 P X             -> X', X'^T  (last step: O) }
 //   update_kernel     W <- clip_row ((1 - lr wd) W - lr rms sqrt(max) O)
 // (s0 = s on the first step, 1 after). The apply is the quintic step of the
 // Notes on Muon blog, "Newton-Schulz", written as X' = (aI + bA + cA^2) X.
-// Operands are bf16, accumulation and every epilogue fp32; for m < 1024 the
-// Gram matrix and the polynomial enter their products as hi + lo bf16 pairs
-// (3 and 2 MFMA passes), which keeps those small-m shapes well inside the
-// 2e-2 relative Frobenius bound.
+// Operands are bf16, accumulation and every epilogue fp32; the Poly epilogue
+// reads b A from the pair A_hi + A_lo (about 16 significant bits). For
+// m < 1024 the Gram matrix and the polynomial also enter their products as
+// hi + lo bf16 pairs (3 and 2 MFMA passes), which keeps those small-m shapes
+// well inside the 2e-2 relative Frobenius bound.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -196,7 +197,8 @@ struct GemmPlan { GemmTile tile; int tiles_m, tiles_n, splits, kt_per_split; siz
 // at least two full waves of workgroups, else 128x128 (64x64 below 128 rows);
 // K is split only when the tiles alone cannot fill the chip, keeping every
 // split at least 8 k-stages long. Symmetric products count upper tiles only.
-GemmPlan plan_gemm(int64_t M, int64_t N, int ktiles, int batch, bool sym, bool reads_cin = false) {
+GemmPlan plan_gemm(int64_t M, int64_t N, int ktiles, int batch, bool sym, bool reads_cin = false,
+                   bool pair_out = false) {
   GemmPlan p{};
   auto count = [&](int d) {
     const int tm = (int)((M + d - 1) / d), tn = (int)((N + d - 1) / d);
@@ -208,7 +210,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int ktiles, int batch, bool sym, bool r
   // co-resident 128 tiles, overlapping one's epilogue with the other's loop,
   // stay ahead until the 256 tiles fill the chip twice
   const int need256 = reads_cin ? 2 * kCUs : kCUs / 2;
-  if (M >= 256 && N >= 256 && count(256) >= need256) p.tile = TILE_256;
+  // (the 256 tile of the Poly step with a hi/lo output pair needs more
+  // registers than a wave has, so that case stays on 128 tiles)
+  if (M >= 256 && N >= 256 && count(256) >= need256 && !(reads_cin && pair_out)) p.tile = TILE_256;
   else if (M >= 128 && N >= 128) p.tile = TILE_128;
   else p.tile = TILE_64;
   const int d = gemm_tile_dim(p.tile);
@@ -230,7 +234,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int ktiles, int batch, bool sym, bool r
 
 struct WavePlan {
   int nb;
-  size_t off_x, off_xt0, off_xt1, off_a32, off_ahi, off_alo, off_phi, off_plo, off_part, off_scale, off_splitk;
+  size_t off_x, off_xt0, off_xt1, off_ahi, off_alo, off_phi, off_plo, off_part, off_scale, off_splitk;
   size_t bytes;
   int64_t mom_blocks;          // momentum blocks per matrix
   GemmPlan gram, poly, apply;
@@ -246,9 +250,8 @@ WavePlan plan_wave(const Group& g, int nb) {
   w.off_x = take(nb * mp * np * 2);
   w.off_xt0 = take(nb * np * mp * 2);
   w.off_xt1 = take(nb * np * mp * 2);
-  w.off_a32 = take(nb * mp * mp * 4);
   w.off_ahi = take(nb * mp * mp * 2);
-  w.off_alo = g.split ? take(nb * mp * mp * 2) : 0;
+  w.off_alo = take(nb * mp * mp * 2);
   w.off_phi = take(nb * mp * mp * 2);
   w.off_plo = g.split ? take(nb * mp * mp * 2) : 0;
   w.mom_blocks = (int64_t)(mp / 64) * (int64_t)(np / 64);
@@ -258,7 +261,7 @@ WavePlan plan_wave(const Group& g, int nb) {
   w.kt_poly = (int)(mp / kGemmBK) * (g.split ? 3 : 1);
   w.kt_apply = (int)(mp / kGemmBK) * (g.split ? 2 : 1);
   w.gram = plan_gemm(g.mp, g.mp, w.kt_gram, nb, true);
-  w.poly = plan_gemm(g.mp, g.mp, w.kt_poly, nb, true, true);
+  w.poly = plan_gemm(g.mp, g.mp, w.kt_poly, nb, true, true, g.split);
   w.apply = plan_gemm(g.mp, g.np, w.kt_apply, nb, false);
   const size_t sk = std::max(w.gram.partial_bytes, std::max(w.poly.partial_bytes, w.apply.partial_bytes));
   w.off_splitk = sk ? take(sk) : 0;
@@ -303,9 +306,8 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
   const int64_t mp = g.mp, np = g.np;
   uint16_t* X = (uint16_t*)(ws + w.off_x);
   uint16_t* XT[2] = {(uint16_t*)(ws + w.off_xt0), (uint16_t*)(ws + w.off_xt1)};
-  float* A32 = (float*)(ws + w.off_a32);
   uint16_t* Ahi = (uint16_t*)(ws + w.off_ahi);
-  uint16_t* Alo = g.split ? (uint16_t*)(ws + w.off_alo) : nullptr;
+  uint16_t* Alo = (uint16_t*)(ws + w.off_alo);
   uint16_t* Phi = (uint16_t*)(ws + w.off_phi);
   uint16_t* Plo = g.split ? (uint16_t*)(ws + w.off_plo) : nullptr;
   float* part = (float*)(ws + w.off_part);
@@ -354,16 +356,15 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
     const bool first = it == 0, last = it == hp.ns_steps - 1;
     uint16_t* xt_cur = XT[it & 1];
     uint16_t* xt_nxt = XT[(it + 1) & 1];
-    // Gram: A = s0^2 X X^T
+    // Gram: A = s0^2 X X^T, stored as a bf16 pair A_hi + A_lo
     {
       GemmArgs a{};
       a.M = (int32_t)mp; a.N = (int32_t)mp; a.batch = nb;
       a.lda = (int32_t)np; a.ldb = (int32_t)np; a.bsa = mp * np; a.bsb = mp * np;
       a.nseg = 1; a.seg[0] = {X, X, w.kt_gram}; a.ktiles = w.kt_gram;
       a.epi.alpha = 1.0f; a.epi.scale_pow = first ? 2 : 0; a.epi.scale = scale;
-      a.epi.out_f32 = A32; a.epi.ld_f32 = (int32_t)mp; a.epi.bs_f32 = mp * mp;
       a.epi.out_hi = Ahi; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
-      if (Alo) { a.epi.out_lo = Alo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp; }
+      a.epi.out_lo = Alo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp;
       mc_status st = launch_gemm_planned(w.gram, GEMM_GRAM, g.split, a, s, ws, w.off_splitk,
                                          2.0 * mm_ * mm_ * nn_ * nb);
       if (st) return st;
@@ -382,7 +383,7 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
       }
       a.ktiles = w.kt_poly;
       a.epi.alpha = hp.ns_c; a.epi.beta = hp.ns_b; a.epi.diag = hp.ns_a;
-      a.epi.cin = A32; a.epi.ld_cin = (int32_t)mp; a.epi.bs_cin = mp * mp;
+      a.epi.cin_hi = Ahi; a.epi.cin_lo = Alo; a.epi.ld_cin = (int32_t)mp; a.epi.bs_cin = mp * mp;
       a.epi.out_hi = Phi; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
       if (Plo) { a.epi.out_lo = Plo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp; }
       mc_status st = launch_gemm_planned(w.poly, GEMM_POLY, g.split, a, s, ws, w.off_splitk,

@@ -9,12 +9,16 @@ namespace mc {
 
 // ---------------------------------------------------------------- bf16 bits
 
-// fp32 -> bf16 with round-to-nearest-even (NaN kept quiet).
-__host__ __device__ inline uint16_t f32_to_bf16(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// fp32 -> bf16 with round-to-nearest-even: gfx950's v_cvt_pk_bf16_f32 (NaN
+// stays a quiet NaN). Device code only.
+typedef __bf16 mc_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float mc_f32x2_t __attribute__((ext_vector_type(2)));
+__device__ inline uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// two values packed into one dword, a in the low half
+__device__ inline uint32_t f32x2_to_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((mc_f32x2_t){a, b}, mc_bf16x2_t));
 }
 __host__ __device__ inline float bf16_to_f32(uint16_t h) {
   return __builtin_bit_cast(float, (uint32_t)h << 16);
@@ -32,18 +36,18 @@ struct GemmSeg {
   int32_t ktiles;       // K_s / kGemmBK
 };
 
-// Epilogue: v = alpha * scale[b]^pow * acc + beta * cin[i][j] + diag * (i==j),
-// then any of: fp32 store, bf16 store (hi), bf16 residual store (lo = v - hi),
-// bf16 store of the transpose. Every pointer is the batch-0 base; bs_* are the
+// Epilogue: v = alpha * scale[b]^pow * acc + beta * (cin_hi + cin_lo)[i][j]
+// + diag * (i==j), then any of: bf16 store (hi), bf16 residual store
+// (lo = v - hi), bf16 store of the transpose. cin is a bf16 hi + lo pair
+// (about 16 significant bits). Every pointer is the batch-0 base; bs_* are the
 // per-batch strides in elements.
 struct GemmEpi {
   float alpha;
   int32_t scale_pow;
   const float* scale;
   float beta;
-  const float* cin; int32_t ld_cin; int64_t bs_cin;
+  const uint16_t* cin_hi; const uint16_t* cin_lo; int32_t ld_cin; int64_t bs_cin;
   float diag;
-  float* out_f32; int32_t ld_f32; int64_t bs_f32;
   uint16_t* out_hi; int32_t ld_hi; int64_t bs_hi;
   uint16_t* out_lo; int32_t ld_lo; int64_t bs_lo;
   uint16_t* out_t; int32_t ld_t; int64_t bs_t;
@@ -65,8 +69,8 @@ struct GemmArgs {
 
 enum GemmTile { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2 };
 // which Newton-Schulz product a launch computes; fixes the epilogue:
-//   GRAM  A = s^2 X X^T      -> fp32 A, bf16 A_hi (+ A_lo)   (symmetric tiles)
-//   POLY  P = a I + b A + c A A -> bf16 P_hi (+ P_lo)          (symmetric tiles)
+//   GRAM  A = s^2 X X^T      -> bf16 A_hi + A_lo           (symmetric tiles)
+//   POLY  P = a I + b A + c A A -> bf16 P_hi (+ P_lo)        (symmetric tiles)
 //   APPLY X' = s P X          -> bf16 X' and its transpose
 enum GemmKind { GEMM_GRAM = 0, GEMM_POLY = 1, GEMM_APPLY = 2 };
 int gemm_tile_dim(GemmTile t);

@@ -44,15 +44,15 @@ __device__ inline int xcd_remap(int L, int total) {
 
 __device__ __attribute__((always_inline)) inline void epilogue_store(const GemmEpi& e, int b, int i, int j, float acc, float sc) {
   float v = e.alpha * sc * acc;
-  if (e.cin) v += e.beta * e.cin[(int64_t)b * e.bs_cin + (int64_t)i * e.ld_cin + j];
-  if (i == j) v += e.diag;
-  if (e.out_f32) e.out_f32[(int64_t)b * e.bs_f32 + (int64_t)i * e.ld_f32 + j] = v;
-  if (e.out_hi || e.out_lo || e.out_t) {
-    const uint16_t h = f32_to_bf16(v);
-    if (e.out_hi) e.out_hi[(int64_t)b * e.bs_hi + (int64_t)i * e.ld_hi + j] = h;
-    if (e.out_lo) e.out_lo[(int64_t)b * e.bs_lo + (int64_t)i * e.ld_lo + j] = f32_to_bf16(v - bf16_to_f32(h));
-    if (e.out_t) e.out_t[(int64_t)b * e.bs_t + (int64_t)j * e.ld_t + i] = h;
+  if (e.cin_hi) {
+    const int64_t o = (int64_t)b * e.bs_cin + (int64_t)i * e.ld_cin + j;
+    v += e.beta * (bf16_to_f32(e.cin_hi[o]) + bf16_to_f32(e.cin_lo[o]));
   }
+  if (i == j) v += e.diag;
+  const uint16_t h = f32_to_bf16(v);
+  if (e.out_hi) e.out_hi[(int64_t)b * e.bs_hi + (int64_t)i * e.ld_hi + j] = h;
+  if (e.out_lo) e.out_lo[(int64_t)b * e.bs_lo + (int64_t)i * e.ld_lo + j] = f32_to_bf16(v - bf16_to_f32(h));
+  if (e.out_t) e.out_t[(int64_t)b * e.bs_t + (int64_t)j * e.ld_t + i] = h;
 }
 
 __device__ __attribute__((always_inline)) inline float batch_scale(const GemmEpi& e, int b) {
@@ -87,11 +87,10 @@ struct FragVisit<N, N, FN> {
 
 // compile-time epilogue selection
 enum : int {
-  E_F32 = 1,      // fp32 store of v
   E_HI = 2,       // bf16 store of v
   E_LO = 4,       // bf16 store of v - bf16(v)
   E_T = 8,        // bf16 store of v at the transposed position
-  E_CIN = 16,     // v += beta * cin[i][j]
+  E_CIN = 16,     // v += beta * (cin_hi + cin_lo)[i][j]
   E_DIAG = 32,    // v += diag on i == j
   E_PART = 64,    // split-K: raw fp32 partial, no epilogue
   E_SYM = 128,    // upper tiles only; off-diagonal tiles also stored mirrored
@@ -99,6 +98,8 @@ enum : int {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// wait for every outstanding LDS operation of this wave
+#define MC_WAIT_LGKM_ALL() asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory")
 // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at max)
 #define MC_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | 0x70 | 0xF00 | (((n) >> 4) << 14))
 
@@ -114,9 +115,11 @@ ns_gemm_kernel(const GemmArgs p) {
   constexpr int RPI = 64 / CPR;                   // rows per DMA instruction (8)
   constexpr int STAGE = (BM + BN) * ROWB;         // bytes per stage
   constexpr int IA = BM / 4 / RPI, IB = BN / 4 / RPI;   // DMA instructions per wave per stage
-  static_assert(STAGE * NSTAGE <= 160 * 1024, "LDS");
+  constexpr int TP = WTM * 2 + 16;                // epilogue staging: bytes per T row
+  constexpr int LDS_BYTES = STAGE * NSTAGE > 4 * WTN * TP ? STAGE * NSTAGE : 4 * WTN * TP;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert((KK % 2) == 0, "two fragment slots");
-  __shared__ __attribute__((aligned(1024))) char lds[STAGE * NSTAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS targets stay scalar
@@ -345,81 +348,140 @@ ns_gemm_kernel(const GemmArgs p) {
 #undef MC_WAIT_LGKM
 #undef MC_STEP
 
-  // Epilogue straight from the accumulators: register 4g+q of lane l holds
-  // row 8g + 4(l/32) + q, column l%32 of its 32x32 fragment, i.e. each lane
-  // owns runs of four consecutive rows at one column. Row-major stores are
-  // 64/128-byte segments per half-wave; transposed stores write the four
-  // rows as one 8- or 16-byte vector.
+  // Epilogue. Register 4g+q of lane l holds row 8g + 4(l/32) + q, column
+  // l%32 of its 32x32 fragment: runs of four consecutive rows at one column.
+  // bf16 results are staged through LDS so that every global store moves 16
+  // bytes per lane: each wave writes its sub-tile transposed (T[j][i], the
+  // four rows as one 8-byte write) into a private region of the freed ring,
+  // then reads T rows (8 consecutive i at one j) for the transposed or
+  // mirrored store, and reads T with the gfx950 transposing LDS read
+  // (ds_read_b64_tr_b16: lane t of a 16-lane group receives element b of
+  // the lanes 4q + t/4, q = 0..3) to get 8 consecutive j at one i for the
+  // row-major store. M and N are multiples of 32; stores test bounds per lane.
   const float sc = (EPI & E_PART) ? 1.0f : batch_scale(p.epi, b);
   const float alpha = p.epi.alpha * sc, beta = p.epi.beta, diag = p.epi.diag;
   static_assert(!(EPI & E_CIN) || (EPI & E_SYM), "cin is read transposed: symmetric products only");
   const bool mirror = (EPI & E_SYM) && tm != tn;
-  const int64_t mn = (int64_t)p.M * p.N;
-  float* part = (EPI & E_PART) ? p.partial + ((int64_t)split * p.batch + b) * mn : nullptr;
-  const float* cin = (EPI & E_CIN) ? p.epi.cin + (int64_t)b * p.epi.bs_cin : nullptr;
-  float* of32 = (EPI & E_F32) ? p.epi.out_f32 + (int64_t)b * p.epi.bs_f32 : nullptr;
+  const int wi0 = m0 + wm * WTM, wj0 = n0 + wn * WTN;          // wave sub-tile origin
+  const int li = 4 * (lane >> 5), lj = lane & 31;
+
+  if (EPI & E_PART) {   // split-K: raw fp32 partials, row-major
+    float* part = p.partial + ((int64_t)split * p.batch + b) * ((int64_t)p.M * p.N);
+    const uint32_t r0 = (uint32_t)((wi0 + li) * p.N + wj0 + lj);
+    auto frag_part = [&](const f32x16_t& a, int fi, int fj) __attribute__((always_inline)) {
+      if (wi0 + fi * 32 >= p.M || wj0 + fj * 32 >= p.N) return;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) part[r0 + (uint32_t)((fi * 32 + 8 * g + q) * p.N + fj * 32)] = a[4 * g + q];
+    };
+    FragVisit<0, FM * FN, FN>::run(acc, frag_part);
+    return;
+  }
+
+  const int ld_hi = (EPI & E_HI) ? p.epi.ld_hi : 0, ld_lo = (EPI & E_LO) ? p.epi.ld_lo : 0;
+  const int ld_t = (EPI & E_T) ? p.epi.ld_t : 0, ld_cin = (EPI & E_CIN) ? p.epi.ld_cin : 0;
+  const uint16_t* cin_hi = (EPI & E_CIN) ? p.epi.cin_hi + (int64_t)b * p.epi.bs_cin : nullptr;
+  const uint16_t* cin_lo = (EPI & E_CIN) ? p.epi.cin_lo + (int64_t)b * p.epi.bs_cin : nullptr;
   uint16_t* ohi = (EPI & E_HI) ? p.epi.out_hi + (int64_t)b * p.epi.bs_hi : nullptr;
   uint16_t* olo = (EPI & E_LO) ? p.epi.out_lo + (int64_t)b * p.epi.bs_lo : nullptr;
   uint16_t* ot = (EPI & E_T) ? p.epi.out_t + (int64_t)b * p.epi.bs_t : nullptr;
-  // one 32x32 fragment per call; fragments are visited in a fully unrolled
-  // recursion so every accumulator index is a compile-time constant
-  auto frag_out = [&](const f32x16_t& a, int fi, int fj) __attribute__((always_inline)) {
-    const int gj = n0 + wn * WTN + fj * 32 + (lane & 31);
-    // cin is the symmetric A of the Gram step: rows gi..gi+3 at column gj
-    // are read as one 16-byte vector of row gj, issued for all four row
-    // groups before any is used (rows clamped in range; values of clamped
-    // rows are never stored)
-    f32x4_t c4[4];
-    if (EPI & E_CIN) {
-      const int cj = min(gj, p.N - 1);
+  const uint32_t t_cin = (uint32_t)((wj0 + lj) * ld_cin + wi0 + li);
+
+  // private staging region of this wave: T[WTN][WTM] bf16, row pitch TP
+  // bytes (16 bytes of padding keep the 8-byte writes of 16 lanes on
+  // distinct banks)
+  char* tw = lds + wave * (WTN * TP);
+  __builtin_amdgcn_s_barrier();          // every wave is done with the ring
+
+  // write pass: v (or its bf16 residual when lo_pass) into T
+  auto stage = [&](bool lo_pass) __attribute__((always_inline)) {
+    auto frag_stage = [&](const f32x16_t& a, int fi, int fj) __attribute__((always_inline)) {
+      uint2 c_hi[4], c_lo[4];
+      if (EPI & E_CIN) {   // rows r..r+3 at column c of the symmetric A, read as row c
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int ci = min(m0 + wm * WTM + fi * 32 + 8 * g + 4 * (lane >> 5), p.M - 4);
-        c4[g] = *(const f32x4_t*)(cin + (int64_t)cj * p.epi.ld_cin + ci);
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int gi = m0 + wm * WTM + fi * 32 + 8 * g + 4 * (lane >> 5);   // rows gi..gi+3
-      if (gi < p.M && gj < p.N) {
-        float v[4] = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-        if (EPI & E_PART) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) part[(int64_t)(gi + q) * p.N + gj] = v[q];
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            v[q] *= alpha;
-            if (EPI & E_CIN) v[q] += beta * c4[g][q];
-            if ((EPI & E_DIAG) && gi + q == gj) v[q] += diag;
-          }
-          if (EPI & E_F32) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) of32[(int64_t)(gi + q) * p.epi.ld_f32 + gj] = v[q];
-            if (mirror) *(f32x4_t*)(of32 + (int64_t)gj * p.epi.ld_f32 + gi) = f32x4_t{v[0], v[1], v[2], v[3]};
-          }
-          uint16_t h[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) h[q] = f32_to_bf16(v[q]);
-          if (EPI & E_HI) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) ohi[(int64_t)(gi + q) * p.epi.ld_hi + gj] = h[q];
-            if (mirror) *(u16x4_t*)(ohi + (int64_t)gj * p.epi.ld_hi + gi) = u16x4_t{h[0], h[1], h[2], h[3]};
-          }
-          if (EPI & E_LO) {
-            uint16_t l[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) l[q] = f32_to_bf16(v[q] - bf16_to_f32(h[q]));
-#pragma unroll
-            for (int q = 0; q < 4; ++q) olo[(int64_t)(gi + q) * p.epi.ld_lo + gj] = l[q];
-            if (mirror) *(u16x4_t*)(olo + (int64_t)gj * p.epi.ld_lo + gi) = u16x4_t{l[0], l[1], l[2], l[3]};
-          }
-          if (EPI & E_T) *(u16x4_t*)(ot + (int64_t)gj * p.epi.ld_t + gi) = u16x4_t{h[0], h[1], h[2], h[3]};
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t o = t_cin + (uint32_t)(fj * 32 * ld_cin + fi * 32 + 8 * g);
+          c_hi[g] = *(const uint2*)(cin_hi + o);
+          c_lo[g] = *(const uint2*)(cin_lo + o);
         }
       }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ur = fi * 32 + 8 * g + li;           // wave-local row of q = 0
+        const int uc = fj * 32 + lj;                   // wave-local column
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[q] = a[4 * g + q] * alpha;
+          if (EPI & E_CIN) {
+            const uint32_t wh = q < 2 ? c_hi[g].x : c_hi[g].y, wl = q < 2 ? c_lo[g].x : c_lo[g].y;
+            const float ch = bf16_to_f32((uint16_t)((q & 1) ? wh >> 16 : wh));
+            const float cl = bf16_to_f32((uint16_t)((q & 1) ? wl >> 16 : wl));
+            v[q] += beta * (ch + cl);
+          }
+          if ((EPI & E_DIAG) && wi0 + ur + q == wj0 + uc) v[q] += diag;
+        }
+        uint32_t w01 = f32x2_to_bf16x2(v[0], v[1]), w23 = f32x2_to_bf16x2(v[2], v[3]);
+        if (lo_pass) {
+          w01 = f32x2_to_bf16x2(v[0] - bf16_to_f32((uint16_t)w01), v[1] - bf16_to_f32((uint16_t)(w01 >> 16)));
+          w23 = f32x2_to_bf16x2(v[2] - bf16_to_f32((uint16_t)w23), v[3] - bf16_to_f32((uint16_t)(w23 >> 16)));
+        }
+        *(uint2*)(tw + uc * TP + ur * 2) = make_uint2(w01, w23);
+      }
+    };
+    FragVisit<0, FM * FN, FN>::run(acc, frag_stage);
+  };
+  // row-major store of T^T: lane t of group gr reads rows i0+t, columns
+  // j0..j0+7 (two transposing reads) and stores them as one 16-byte vector
+  auto store_direct = [&](uint16_t* dst, int ld) __attribute__((always_inline)) {
+    const int t = lane & 15, gr = lane >> 4;
+    const int sq = t >> 2, sa = t & 3;               // this lane's source row / column block
+#pragma unroll
+    for (int jb = 0; jb < WTN / 32; ++jb)
+#pragma unroll
+      for (int ib = 0; ib < WTM / 16; ++ib) {
+        const int i0 = ib * 16, j0 = jb * 32 + gr * 8;
+        typedef short v4i16 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+        const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(tw + (j0 + sq) * TP + (i0 + 4 * sa) * 2));
+        const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(tw + (j0 + 4 + sq) * TP + (i0 + 4 * sa) * 2));
+        const int gi = wi0 + i0 + t, gj = wj0 + j0;
+        if (gi < p.M && gj < p.N) {
+          uint4 o;
+          o.x = (uint32_t)(uint16_t)x0[0] | ((uint32_t)(uint16_t)x0[1] << 16);
+          o.y = (uint32_t)(uint16_t)x0[2] | ((uint32_t)(uint16_t)x0[3] << 16);
+          o.z = (uint32_t)(uint16_t)x1[0] | ((uint32_t)(uint16_t)x1[1] << 16);
+          o.w = (uint32_t)(uint16_t)x1[2] | ((uint32_t)(uint16_t)x1[3] << 16);
+          *(uint4*)(dst + (uint32_t)(gi * ld + gj)) = o;
+        }
+      }
+  };
+  // transposed store: T rows (8 consecutive i at one j) as 16-byte vectors
+  auto store_trans = [&](uint16_t* dst, int ld) __attribute__((always_inline)) {
+    constexpr int CH = WTM / 8, RPS = 64 / CH;       // chunks per T row, T rows per pass
+    const int ch = lane % CH, rr = lane / CH;
+#pragma unroll
+    for (int it = 0; it < WTN / RPS; ++it) {
+      const int jr = it * RPS + rr;
+      const uint4 o = *(const uint4*)(tw + jr * TP + ch * 16);
+      const int gj = wj0 + jr, gi = wi0 + ch * 8;
+      if (gj < p.N && gi < p.M) *(uint4*)(dst + (uint32_t)(gj * ld + gi)) = o;
     }
   };
-  FragVisit<0, FM * FN, FN>::run(acc, frag_out);
+
+  stage(false);
+  if (EPI & E_HI) store_direct(ohi, ld_hi);
+  if (EPI & E_T) store_trans(ot, ld_t);
+  else if ((EPI & E_HI) && mirror) store_trans(ohi, ld_hi);
+  if (EPI & E_LO) {
+    MC_WAIT_LGKM_ALL();
+    stage(true);
+    store_direct(olo, ld_lo);
+    if (mirror) store_trans(olo, ld_lo);
+  }
 }
 
 // Deterministic split-K finish: fixed-order sum of the partial tiles, then the
@@ -455,18 +517,20 @@ int gemm_tile_count(const GemmArgs& a, GemmKind kind) {
 hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const GemmArgs& a, hipStream_t s) {
   const int total = gemm_tile_count(a, kind) * a.splits * a.batch;
   if (total <= 0) return hipSuccess;
-  // the epilogue moves four consecutive elements per lane: extents, leading
-  // dimensions and batch strides must be multiples of 4 elements
+  // the epilogue works on 32x32 fragments and moves 16-byte vectors:
+  // extents must be multiples of 32; leading dimensions and batch strides
+  // multiples of 8 elements and bases 16-byte aligned
   const GemmEpi& e = a.epi;
-  auto bad = [](const void* ptr, int64_t ld, int64_t bs) { return ptr && ((ld & 3) || (bs & 3)); };
-  if ((a.M & 3) || (a.N & 3) || bad(e.cin, e.ld_cin, e.bs_cin) || bad(e.out_f32, e.ld_f32, e.bs_f32) ||
+  auto bad = [](const void* ptr, int64_t ld, int64_t bs) {
+    return ptr && ((ld & 7) || (bs & 7) || ((uintptr_t)ptr & 15));
+  };
+  if ((a.M & 31) || (a.N & 31) || bad(e.cin_hi, e.ld_cin, e.bs_cin) || bad(e.cin_lo, e.ld_cin, e.bs_cin) ||
       bad(e.out_hi, e.ld_hi, e.bs_hi) || bad(e.out_lo, e.ld_lo, e.bs_lo) || bad(e.out_t, e.ld_t, e.bs_t))
     return hipErrorInvalidValue;
   if (a.splits > 1) {
     launch_epi<E_PART>(tile, a, total, s);
   } else if (kind == GEMM_GRAM) {
-    if (split_pair) launch_epi<E_SYM | E_F32 | E_HI | E_LO>(tile, a, total, s);
-    else launch_epi<E_SYM | E_F32 | E_HI>(tile, a, total, s);
+    launch_epi<E_SYM | E_HI | E_LO>(tile, a, total, s);
   } else if (kind == GEMM_POLY) {
     if (split_pair) launch_epi<E_SYM | E_CIN | E_DIAG | E_HI | E_LO>(tile, a, total, s);
     else launch_epi<E_SYM | E_CIN | E_DIAG | E_HI>(tile, a, total, s);
