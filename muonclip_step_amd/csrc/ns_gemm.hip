@@ -34,6 +34,13 @@ typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
 
 int gemm_tile_dim(GemmTile t) { return t == TILE_256 ? 256 : (t == TILE_128 ? 128 : 64); }
 
+// Tile order of the non-symmetric products: consecutive tiles walk down
+// kGroupRows tile rows before moving one tile column right, so the 32
+// workgroups an XCD runs at once cover a 4 x 8 block of tiles and share their
+// operand rows in that XCD's L2 (a row-major order would share only one A
+// block across 32 different B blocks).
+constexpr int kGroupRows = 4;
+
 // Bijective remap of the linear workgroup id so that consecutive ids of the
 // logical order land on one XCD (hardware deals workgroups round-robin over 8).
 __device__ inline int xcd_remap(int L, int total) {
@@ -137,9 +144,12 @@ ns_gemm_kernel(const GemmArgs p) {
     tm = 0;
     while (t >= p.tiles_m - tm) { t -= p.tiles_m - tm; ++tm; }
     tn = tm + t;
-  } else {
-    tm = t / p.tiles_n;
-    tn = t - tm * p.tiles_n;
+  } else {                      // groups of kGroupRows tile rows, column by column inside a group
+    const int grp = t / (kGroupRows * p.tiles_n);
+    const int rows = min(kGroupRows, p.tiles_m - grp * kGroupRows);
+    const int local = t - grp * kGroupRows * p.tiles_n;
+    tn = local / rows;
+    tm = grp * kGroupRows + (local - tn * rows);
   }
   const int m0 = tm * BM;
   const int n0 = tn * BN;
