@@ -101,6 +101,8 @@ enum : int {
   E_DIAG = 32,    // v += diag on i == j
   E_PART = 64,    // split-K: raw fp32 partial, no epilogue
   E_SYM = 128,    // upper tiles only; off-diagonal tiles also stored mirrored
+  E_LOMIR = 256,  // the lo part is read only transposed (by the Poly epilogue):
+                  // off-diagonal tiles store it mirrored only
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -489,7 +491,7 @@ ns_gemm_kernel(const GemmArgs p) {
   if (EPI & E_LO) {
     MC_WAIT_LGKM_ALL();
     stage(true);
-    store_direct(olo, ld_lo);
+    if (!(EPI & E_LOMIR) || !mirror) store_direct(olo, ld_lo);
     if (mirror) store_trans(olo, ld_lo);
   }
 }
@@ -540,7 +542,9 @@ hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const G
   if (a.splits > 1) {
     launch_epi<E_PART>(tile, a, total, s);
   } else if (kind == GEMM_GRAM) {
-    launch_epi<E_SYM | E_HI | E_LO>(tile, a, total, s);
+    // without operand pairs A_lo only feeds the Poly epilogue's transposed read
+    if (split_pair) launch_epi<E_SYM | E_HI | E_LO>(tile, a, total, s);
+    else launch_epi<E_SYM | E_HI | E_LO | E_LOMIR>(tile, a, total, s);
   } else if (kind == GEMM_POLY) {
     if (split_pair) launch_epi<E_SYM | E_CIN | E_DIAG | E_HI | E_LO>(tile, a, total, s);
     else launch_epi<E_SYM | E_CIN | E_DIAG | E_HI>(tile, a, total, s);
