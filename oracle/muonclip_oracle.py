@@ -27,7 +27,7 @@ Sources, by page title and section:
               polynomial phi, U phi^N(S) V^T), "Coefficient Optimization", "Algorithm"
               (newtonschulz5: bf16 copy, Frobenius normalisation with eps=1e-7,
               transpose when rows > cols, 5 steps, (a,b,c) = (3.4445, -4.7750, 2.0315))
-              and "Analysis" (2(2nm^2+m^3) FLOPs per step).
+              and "Analysis" (2(2nm^2+m^3) FLOPs per step; Nesterov-style momentum).
 
 Readings where the pages are silent or garbled (each is listed in the design doc):
   * Algorithm 1's body is absent on every page; the step is assembled from the
@@ -40,6 +40,11 @@ Readings where the pages are silent or garbled (each is listed in the design doc):
     mirroring the guard in the essay's MHA code sample.
   * d in 1/sqrt(d) is the per-head q.k dimension (the essay's code divides by
     q.size(-1)); NaN logits are ignored by the max (IEEE maxNum).
+  * Nesterov-style momentum (the Muon blog notes say only that Muon uses it):
+    the buffer update is unchanged and the matrix orthogonalised is the
+    look-ahead G_t + mu M_t.
+  * Global clip ([K2-cn] 2.1, the naive variant): gamma from the largest
+    S_max^h of the layer, NaN heads ignored by that max.
 """
 
 from __future__ import annotations
@@ -108,6 +113,13 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 def momentum(m_prev: np.ndarray, g: np.ndarray, mu: float) -> np.ndarray:
     """M_t = mu * M_{t-1} + G_t  ([Moonlight] "Background"; M_0 = 0)."""
     return mu * np.asarray(m_prev, np.float64) + np.asarray(g, np.float64)
+
+
+def nesterov_direction(m_new: np.ndarray, g: np.ndarray, mu: float) -> np.ndarray:
+    """The matrix a Nesterov-style Muon step orthogonalises: the look-ahead
+    G_t + mu M_t of the plain buffer M_t = mu M_{t-1} + G_t ([Muon-blog]
+    "Analysis": Nesterov-style momentum is used instead of plain SGD momentum)."""
+    return np.asarray(g, np.float64) + mu * np.asarray(m_new, np.float64)
 
 
 def newton_schulz(m: np.ndarray, steps: int = NS_STEPS, a: float = NS_A,
@@ -219,6 +231,17 @@ def clip_factor(s_max: np.ndarray, tau: float) -> np.ndarray:
     return g
 
 
+def clip_factor_global(s_max_layer: np.ndarray, tau: float) -> float:
+    """The naive all-head variant ([K2-cn] 2.1): gamma = min(1, tau / S_max)
+    with S_max the largest S_max^h of the layer; W_q is then scaled by
+    gamma**alpha and W_k by gamma**(1 - alpha) (alpha = 1/2 typically). NaN
+    heads are ignored by the max; gamma is 1 when that max is not positive."""
+    s = np.asarray(s_max_layer, np.float64)
+    s = s[~np.isnan(s)]
+    top = float(s.max()) if s.size else float("nan")
+    return float(clip_factor(np.array([top]), tau)[0])
+
+
 def qk_clip_rows(w: np.ndarray, gamma: np.ndarray, period: int, segments) -> np.ndarray:
     """Scale the head-specific row blocks of a projection weight [out, in].
 
@@ -243,18 +266,22 @@ def qk_clip_rows(w: np.ndarray, gamma: np.ndarray, period: int, segments) -> np.
 def muonclip_step_matrix(w, g, m, *, lr, mu, weight_decay, rms_scale=0.2,
                          ns_steps=NS_STEPS, ns_a=NS_A, ns_b=NS_B, ns_c=NS_C,
                          ns_eps=NS_EPS, gamma=None, period=0, segments=(),
-                         w_dtype="bf16"):
+                         w_dtype="bf16", nesterov=False):
     """One MuonClip update of one 2-D parameter, in the pages' order:
     momentum -> Newton-Schulz -> RMS matching -> decoupled decay/update ->
     post-update QK-Clip of the head row blocks (gamma from this step's
-    forward, computed on the pre-update weights).
+    forward, computed on the pre-update weights). With nesterov the
+    orthogonalised matrix is the look-ahead G + mu M_t (nesterov_direction);
+    gamma is per head (clip_factor) or one value repeated over the heads
+    (clip_factor_global).
 
     Returns (w_new rounded once to w_dtype as fp64 values, m_new as fp32,
     the fp64 Newton-Schulz output O).
     """
     rows, cols = np.shape(w)
     m_new = momentum(m, g, mu)
-    o = newton_schulz(m_new, ns_steps, ns_a, ns_b, ns_c, ns_eps)
+    d = nesterov_direction(m_new, g, mu) if nesterov else m_new
+    o = newton_schulz(d, ns_steps, ns_a, ns_b, ns_c, ns_eps)
     u = rms_matched(o, rows, cols, rms_scale)
     w_new = decoupled_update(w, u, lr, weight_decay)
     if gamma is not None and segments:

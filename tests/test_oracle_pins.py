@@ -313,3 +313,76 @@ def test_ns_flops_formula():
     # Notes on Muon blog, "Analysis": 2(2nm^2 + m^3) per step, m <= n
     assert oracle.ns_flops(2048, 7168, 1) == 2 * (2 * 7168 * 2048 ** 2 + 2048 ** 3)
     assert oracle.ns_flops(7168, 2048, 5) == oracle.ns_flops(2048, 7168, 5)
+
+
+# ---------------------------------------------------------------- variants
+
+def test_nesterov_direction_is_the_lookahead_of_plain_momentum():
+    # Nesterov momentum in Sutskever's look-ahead form: the direction at step t
+    # is M_t + mu (M_t - M_{t-1}) of the plain buffer sequence; built here from
+    # two plain momentum steps, never from the oracle's direction formula
+    rng = np.random.default_rng(21)
+    mu = 0.95
+    g1, g2 = rng.standard_normal((2, 6, 9))
+    m0 = rng.standard_normal((6, 9))
+    m1 = oracle.momentum(m0, g1, mu)
+    m2 = oracle.momentum(m1, g2, mu)
+    lookahead = m2 + mu * (m2 - m1)
+    assert np.allclose(oracle.nesterov_direction(m2, g2, mu), lookahead, rtol=0, atol=1e-12)
+    # mu = 0: no momentum at all, the direction is the gradient
+    assert np.array_equal(oracle.nesterov_direction(oracle.momentum(m0, g1, 0.0), g1, 0.0), g1)
+
+
+def test_nesterov_cold_start_orthogonalises_the_gradient():
+    # M_0 = 0: the look-ahead is (1 + mu) G, and Newton-Schulz is scale
+    # invariant up to eps, so the update equals a plain step on G alone
+    rng = np.random.default_rng(22)
+    w = rng.standard_normal((12, 20))
+    g = rng.standard_normal((12, 20))
+    kw = dict(lr=0.01, mu=0.9, weight_decay=0.1, w_dtype="f64")
+    _, _, o_nest = oracle.muonclip_step_matrix(w, g, np.zeros_like(g), nesterov=True, **kw)
+    want = closed_form_ns(g * 1.9)
+    assert np.linalg.norm(o_nest - want) <= 1e-12 * np.linalg.norm(want)
+    # and with a warm buffer the two variants differ
+    m = rng.standard_normal((12, 20))
+    _, _, o_plain = oracle.muonclip_step_matrix(w, g, m, nesterov=False, **kw)
+    _, _, o_n2 = oracle.muonclip_step_matrix(w, g, m, nesterov=True, **kw)
+    assert np.linalg.norm(o_plain - o_n2) > 1e-3
+
+
+@pytest.mark.parametrize("alpha", [0.5, 0.3])
+def test_global_clip_scales_every_logit_by_gamma(alpha):
+    # the naive variant (K2 report 2.1): W_q by gamma^alpha, W_k by
+    # gamma^(1-alpha) on every head; each logit q.k is bilinear in (W_q, W_k),
+    # so every head's max logit scales by exactly gamma and the layer max lands
+    # on tau. Logits are recomputed here with plain einsum, not the oracle.
+    rng = np.random.default_rng(23)
+    H, dm, dh, T, tau = 3, 12, 4, 9, 5.0
+    x = rng.standard_normal((1, T, dm))
+    wq = rng.standard_normal((H * dh, dm)) * 2.0
+    wk = rng.standard_normal((H * dh, dm)) * 2.0
+
+    def head_max(wq_, wk_):
+        q = np.einsum("btd,od->bto", x, wq_).reshape(1, T, H, dh)
+        k = np.einsum("btd,od->bto", x, wk_).reshape(1, T, H, dh)
+        lg = np.einsum("bihf,bjhf->hij", q, k) / math.sqrt(dh)
+        return lg.reshape(H, -1).max(axis=1)
+
+    before = head_max(wq, wk)
+    gam = oracle.clip_factor_global(before, tau)
+    assert gam < 1.0 and abs(gam - tau / before.max()) < 1e-15
+    g_all = np.full(H, gam)
+    wq2 = oracle.qk_clip_rows(wq, g_all, dh, ((0, dh, alpha),))
+    wk2 = oracle.qk_clip_rows(wk, g_all, dh, ((0, dh, 1.0 - alpha),))
+    after = head_max(wq2, wk2)
+    assert np.allclose(after, before * gam, rtol=1e-12)
+    assert abs(after.max() - tau) < 1e-9
+
+
+def test_global_clip_special_cases():
+    # one head: the global rule is the per-head rule
+    for s in (250.0, 40.0, -3.0, 0.0, math.inf):
+        assert oracle.clip_factor_global(np.array([s]), 100.0) == oracle.clip_factor(np.array([s]), 100.0)[0]
+    # NaN heads are ignored by the max; all-NaN gives gamma = 1
+    assert oracle.clip_factor_global(np.array([np.nan, 400.0, 20.0]), 100.0) == 0.25
+    assert oracle.clip_factor_global(np.array([np.nan, np.nan]), 100.0) == 1.0
