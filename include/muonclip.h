@@ -98,11 +98,24 @@ typedef struct {
 
 /* Hyper-parameters (fp32). Defaults from mc_default_hparams: lr 2e-4,
  * mu 0.95, weight_decay 0.1, rms_scale 0.2, tau 100, Newton-Schulz
- * (a, b, c) = (3.4445, -4.7750, 2.0315), eps 1e-7, 5 steps. */
+ * (a, b, c) = (3.4445, -4.7750, 2.0315), eps 1e-7, 5 steps, plain momentum,
+ * per-head clip.
+ *   nesterov     0: Newton-Schulz orthogonalises the momentum M_t (Notes on
+ *                Moonlight, "Background"); 1: it orthogonalises the look-ahead
+ *                G_t + mu M_t (Nesterov-style momentum, Notes on Muon blog,
+ *                "Analysis"). The stored momentum is M_t either way.
+ *   clip_global  0: per-head gamma_h = min(1, tau / S_max^h) (K2 report 2.1);
+ *                1: the report's naive variant, one gamma = min(1, tau / max_h
+ *                S_max^h) for every head of a layer (slot); the segment
+ *                exponents then carry the balance alpha (W_q alpha, W_k
+ *                1 - alpha; alpha = 0.5 gives 0.5 on both). gamma_out receives
+ *                that gamma for every head. NaN heads are ignored by the max. */
 typedef struct {
   float lr, mu, weight_decay, rms_scale, tau;
   float ns_a, ns_b, ns_c, ns_eps;
   int32_t ns_steps;   /* 1..16 */
+  int32_t nesterov;   /* 0 or 1 */
+  int32_t clip_global;/* 0 or 1 */
 } mc_hparams;
 
 /* (host) Fill *hp with the defaults above. */
@@ -155,8 +168,9 @@ mc_status max_logits_per_head(const void *q, const void *k, const void *k_shared
 /* QK-Clip alone on existing weights (the clip part of muonclip_step without
  * the Muon update): for every matrix with clip_slot >= 0, rows in its
  * segments are scaled by gamma_h ** expo, gamma from s_max[slots][heads] and
- * tau; rows whose factor is exactly 1 are not touched (bit-identical). Uses
- * w, w_dtype, rows, cols, ld and the clip fields of each matrix.
+ * tau (per head; the all-head variant is muonclip_step's clip_global); rows
+ * whose factor is exactly 1 are not touched (bit-identical). Uses w, w_dtype,
+ * rows, cols, ld and the clip fields of each matrix.
  * gamma_out: optional fp32 [slots][heads]. */
 mc_status qk_clip_apply(const mc_matrix *mats /* host, n */, int32_t n, const float *s_max,
                         int32_t slots, int32_t heads, float tau, float *gamma_out, void *stream);

@@ -46,7 +46,7 @@ class Matrix(ctypes.Structure):
 class HParams(ctypes.Structure):
     _fields_ = [("lr", c_float), ("mu", c_float), ("weight_decay", c_float), ("rms_scale", c_float),
                 ("tau", c_float), ("ns_a", c_float), ("ns_b", c_float), ("ns_c", c_float),
-                ("ns_eps", c_float), ("ns_steps", c_int32)]
+                ("ns_eps", c_float), ("ns_steps", c_int32), ("nesterov", c_int32), ("clip_global", c_int32)]
 
 
 class ProfileEntry(ctypes.Structure):

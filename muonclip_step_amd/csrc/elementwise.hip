@@ -1,8 +1,9 @@
 // HBM-bound kernels of the MuonClip step (gfx950).
 //
 //  momentum_kernel   M <- mu M + G (Notes on Moonlight, "Background"), the
-//                    per-block sum of squares of the new M for its Frobenius
-//                    norm, and the bf16 copy of M in both orientations that the
+//                    per-block sum of squares of the new M (or of the Nesterov
+//                    look-ahead G + mu M, Notes on Muon blog, "Analysis") for
+//                    its Frobenius norm, and its bf16 copy in both orientations that the
 //                    Newton-Schulz GEMMs read (Notes on Muon blog, "Algorithm":
 //                    bf16 copy, normalisation, transpose when rows > cols). The
 //                    1/(||M||+eps) scale is not applied here; the first GEMM
@@ -13,7 +14,8 @@
 //                    "Scaling up Muon"), with the post-update QK-Clip row scale
 //                    s_row = gamma_h^expo (Kimi K2 essay, MHA equations and the
 //                    MLA table; gamma_h = min(1, tau / S_max^h)) fused in.
-//  gamma_kernel      gamma_h for every (layer, head).
+//  gamma_kernel      gamma_h for every (layer, head); with clip_global one
+//                    gamma per layer from its largest S_max (K2 report 2.1).
 //  clip_apply_kernel the QK-Clip rescale alone on an existing weight.
 //
 // Tiles are 64x64 elements per 256-thread block; each thread moves 4
@@ -32,14 +34,24 @@ __device__ inline float gamma_of(float s, float tau) {
   return s > 0.0f ? fminf(1.0f, tau / s) : 1.0f;
 }
 
-__device__ inline float row_clip_scale(const ClipRule& c, int row, const float* s_max, int heads, float tau) {
+// S_max that sets head h's gamma: its own, or with clip_global the largest
+// of its layer's heads (fmaxf ignores NaN heads; all NaN gives -inf -> gamma 1)
+__device__ inline float layer_s(const float* s_max, int slot, int h, int heads, int clip_global) {
+  if (!clip_global) return s_max[slot * heads + h];
+  float m = -INFINITY;
+  for (int k = 0; k < heads; ++k) m = fmaxf(m, s_max[slot * heads + k]);
+  return m;
+}
+
+__device__ inline float row_clip_scale(const ClipRule& c, int row, const float* s_max, int heads, float tau,
+                                       int clip_global) {
   if (c.slot < 0 || !s_max || c.nseg == 0) return 1.0f;
   const int h = row / c.period, o = row - h * c.period;
   float expo = 0.0f;
   if (c.nseg > 0 && o >= c.off[0] && o < c.off[0] + c.len[0]) expo = c.expo[0];
   else if (c.nseg > 1 && o >= c.off[1] && o < c.off[1] + c.len[1]) expo = c.expo[1];
   if (expo == 0.0f) return 1.0f;
-  const float g = gamma_of(s_max[c.slot * heads + h], tau);
+  const float g = gamma_of(layer_s(s_max, c.slot, h, heads, clip_global), tau);
   if (expo == 0.5f) return sqrtf(g);
   if (expo == 1.0f) return g;
   return powf(g, expo);
@@ -84,7 +96,8 @@ __global__ void __launch_bounds__(256) momentum_kernel(const MomArgs a) {
         nv[0] = fmaf(a.mu, mv[0], gv[0]); nv[1] = fmaf(a.mu, mv[1], gv[1]);
         nv[2] = fmaf(a.mu, mv[2], gv[2]); nv[3] = fmaf(a.mu, mv[3], gv[3]);
         *(f32x4_t*)(mm.m + base) = nv;
-        v[0] = nv[0]; v[1] = nv[1]; v[2] = nv[2]; v[3] = nv[3];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = a.nesterov ? fmaf(a.mu, nv[e], gv[e]) : nv[e];
       } else if (!mm.vec) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -92,7 +105,7 @@ __global__ void __launch_bounds__(256) momentum_kernel(const MomArgs a) {
             const float g = mm.g_bf16 ? bf16_to_f32(((const uint16_t*)mm.g)[base + e]) : ((const float*)mm.g)[base + e];
             const float n = fmaf(a.mu, mm.m[base + e], g);
             mm.m[base + e] = n;
-            v[e] = n;
+            v[e] = a.nesterov ? fmaf(a.mu, n, g) : n;
           }
         }
       }
@@ -170,7 +183,7 @@ __global__ void __launch_bounds__(256) update_kernel(const UpdArgs a) {
   for (int k = 0; k < 4; ++k) {
     const int row = tr * 64 + ry + 16 * k;
     if (row >= u.rows) break;
-    const float sc = row_clip_scale(u.clip, row, a.s_max, a.heads, a.tau);
+    const float sc = row_clip_scale(u.clip, row, a.s_max, a.heads, a.tau, a.clip_global);
     const int64_t wb = (int64_t)row * u.ld + col;
     const uint16_t* op = u.o + (int64_t)row * u.ld_o + col;
     if (u.vec) {
@@ -220,14 +233,16 @@ hipError_t launch_update(const UpdArgs& a, hipStream_t s) {
 
 // ---------------------------------------------------------------- gamma / clip
 
-__global__ void gamma_kernel(const float* s_max, float* gamma, int n, float tau) {
+__global__ void gamma_kernel(const float* s_max, float* gamma, int slots, int heads, float tau, int clip_global) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) gamma[i] = gamma_of(s_max[i], tau);
+  if (i < slots * heads) gamma[i] = gamma_of(layer_s(s_max, i / heads, i % heads, heads, clip_global), tau);
 }
 
-hipError_t launch_gamma(const float* s_max, float* gamma, int32_t n, float tau, hipStream_t s) {
+hipError_t launch_gamma(const float* s_max, float* gamma, int32_t slots, int32_t heads, float tau,
+                        int32_t clip_global, hipStream_t s) {
+  const int n = slots * heads;
   if (n <= 0) return hipSuccess;
-  gamma_kernel<<<(n + 255) / 256, 256, 0, s>>>(s_max, gamma, n, tau);
+  gamma_kernel<<<(n + 255) / 256, 256, 0, s>>>(s_max, gamma, slots, heads, tau, clip_global);
   return hipGetLastError();
 }
 
@@ -236,7 +251,7 @@ hipError_t launch_gamma(const float* s_max, float* gamma, int32_t n, float tau, 
 // bit-identical.
 __global__ void __launch_bounds__(256) clip_apply_kernel(const ClipApplyArgs a) {
   for (int row = blockIdx.y; row < a.rows; row += gridDim.y) {
-    const float sc = row_clip_scale(a.clip, row, a.s_max, a.heads, a.tau);
+    const float sc = row_clip_scale(a.clip, row, a.s_max, a.heads, a.tau, 0);
     if (sc == 1.0f) continue;
     const int c0 = blockIdx.x * 1024 + threadIdx.x;
     for (int e = 0; e < 4; ++e) {

@@ -110,6 +110,8 @@ mc_status check_hparams(const mc_hparams* hp) {
   if (hp->ns_steps < 1 || hp->ns_steps > 16) return fail(MC_ERR_HPARAM, "ns_steps must be in 1..16 (got %d)", hp->ns_steps);
   if (hp->ns_eps < 0.0f) return fail(MC_ERR_HPARAM, "ns_eps must be >= 0");
   if (hp->tau <= 0.0f) return fail(MC_ERR_HPARAM, "tau must be > 0");
+  if (hp->nesterov != 0 && hp->nesterov != 1) return fail(MC_ERR_HPARAM, "nesterov must be 0 or 1");
+  if (hp->clip_global != 0 && hp->clip_global != 1) return fail(MC_ERR_HPARAM, "clip_global must be 0 or 1");
   return MC_OK;
 }
 
@@ -316,7 +318,7 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
   // 1. momentum + norm partials + bf16 X0 in both orientations
   for (int b0 = 0; b0 < nb; b0 += kMaxBatchMats) {
     MomArgs a{};
-    a.mu = hp.mu;
+    a.mu = hp.mu; a.nesterov = hp.nesterov;
     int blocks = 0;
     double bytes = 0;
     for (int j = 0; j < kMaxBatchMats && b0 + j < nb; ++j) {
@@ -417,7 +419,7 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
   const float decay = (float)(1.0 - (double)hp.lr * (double)hp.weight_decay);
   for (int b0 = 0; b0 < nb; b0 += kMaxBatchMats) {
     UpdArgs a{};
-    a.decay = decay; a.s_max = s_max; a.heads = heads; a.tau = hp.tau;
+    a.decay = decay; a.s_max = s_max; a.heads = heads; a.tau = hp.tau; a.clip_global = hp.clip_global;
     int blocks = 0;
     double bytes = 0;
     for (int j = 0; j < kMaxBatchMats && b0 + j < nb; ++j) {
@@ -464,6 +466,7 @@ void mc_default_hparams(mc_hparams* hp) {
   if (!hp) return;
   hp->lr = 2e-4f; hp->mu = 0.95f; hp->weight_decay = 0.1f; hp->rms_scale = 0.2f; hp->tau = 100.0f;
   hp->ns_a = 3.4445f; hp->ns_b = -4.7750f; hp->ns_c = 2.0315f; hp->ns_eps = 1e-7f; hp->ns_steps = 5;
+  hp->nesterov = 0; hp->clip_global = 0;
 }
 
 const char* mc_last_error(void) { return g_err.c_str(); }
@@ -514,7 +517,7 @@ mc_status muonclip_step(const mc_matrix* mats, int32_t n, const mc_hparams* hp, 
   hipStream_t s = (hipStream_t)stream;
   if (gamma_out) {
     Prof pr(F_GAMMA, s, 0.0, 0.0);
-    hipError_t e = launch_gamma(s_max, gamma_out, slots * heads, hp->tau, s);
+    hipError_t e = launch_gamma(s_max, gamma_out, slots, heads, hp->tau, hp->clip_global, s);
     if (e != hipSuccess) return fail(MC_ERR_HIP, "gamma launch: %s", hipGetErrorString(e));
   }
   for (size_t gi = 0; gi < groups.size(); ++gi) {
@@ -601,7 +604,7 @@ mc_status qk_clip_apply(const mc_matrix* mats, int32_t n, const float* s_max, in
   hipStream_t s = (hipStream_t)stream;
   if (gamma_out) {
     Prof pr(F_GAMMA, s, 0.0, 0.0);
-    hipError_t e = launch_gamma(s_max, gamma_out, slots * heads, tau, s);
+    hipError_t e = launch_gamma(s_max, gamma_out, slots, heads, tau, 0, s);
     if (e != hipSuccess) return fail(MC_ERR_HIP, "gamma launch: %s", hipGetErrorString(e));
   }
   for (int i = 0; i < n; ++i) {

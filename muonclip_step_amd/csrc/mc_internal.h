@@ -96,7 +96,8 @@ struct MomMat {
   int32_t block_start;
   float* partial;                      // one fp32 per block of this matrix
 };
-struct MomArgs { int32_t nmat; float mu; int32_t total_blocks; MomMat mat[kMaxBatchMats]; };
+// nesterov: the norm and the bf16 copies are of G + mu M_t instead of M_t
+struct MomArgs { int32_t nmat; float mu; int32_t nesterov; int32_t total_blocks; MomMat mat[kMaxBatchMats]; };
 hipError_t launch_momentum(const MomArgs& a, hipStream_t s);
 
 // sum of per-block partials -> scale = 1 / (sqrt(sum) + eps), one matrix per block
@@ -120,15 +121,18 @@ struct UpdMat {
   ClipRule clip;
   int32_t tiles_c, block_start;
 };
+// clip_global: gamma of a layer from the largest S_max of its heads
 struct UpdArgs {
   int32_t nmat; int32_t total_blocks;
   float decay;
-  const float* s_max; int32_t heads; float tau;
+  const float* s_max; int32_t heads; float tau; int32_t clip_global;
   UpdMat mat[kMaxBatchMats];
 };
 hipError_t launch_update(const UpdArgs& a, hipStream_t s);
 
-hipError_t launch_gamma(const float* s_max, float* gamma, int32_t n, float tau, hipStream_t s);
+// gamma for [slots][heads]; clip_global: one value per slot from its largest S_max
+hipError_t launch_gamma(const float* s_max, float* gamma, int32_t slots, int32_t heads, float tau,
+                        int32_t clip_global, hipStream_t s);
 
 struct ClipApplyArgs {
   void* w; int32_t w_bf16;

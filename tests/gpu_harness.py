@@ -79,7 +79,7 @@ def oracle_step(state: State, hp, gamma=None):
         rms_scale=oracle.f32(hp.rms_scale), ns_steps=hp.ns_steps, ns_a=oracle.f32(hp.ns_a),
         ns_b=oracle.f32(hp.ns_b), ns_c=oracle.f32(hp.ns_c), ns_eps=oracle.f32(hp.ns_eps),
         gamma=gamma if s.clip_slot >= 0 else None, period=s.period, segments=s.segments,
-        w_dtype=s.w_dtype)
+        w_dtype=s.w_dtype, nesterov=bool(getattr(hp, "nesterov", 0)))
 
 
 def rel_fro(a, b) -> float:

@@ -36,6 +36,19 @@ def test_default_hparams():
     assert abs(hp.rms_scale - 0.2) < 1e-7 and hp.tau == 100.0 and hp.ns_steps == 5
     assert (round(hp.ns_a, 4), round(hp.ns_b, 4), round(hp.ns_c, 4)) == (3.4445, -4.775, 2.0315)
     assert abs(hp.ns_eps - 1e-7) < 1e-12
+    assert hp.nesterov == 0 and hp.clip_global == 0
+
+
+def test_hparams_struct_size_matches_the_library():
+    # mc_default_hparams writes the whole C struct: on a buffer one struct
+    # long plus a sentinel tail, the tail must stay untouched and the last
+    # fields must be written (so the binding's layout is the library's)
+    size = ctypes.sizeof(mc.HParams)
+    buf = (ctypes.c_uint8 * (size + 64))(*([0xAB] * (size + 64)))
+    mc.load().mc_default_hparams(ctypes.cast(buf, ctypes.POINTER(mc.HParams)))
+    assert bytes(buf[size:]) == b"\xab" * 64
+    hp = mc.HParams.from_buffer_copy(bytes(buf[:size]))
+    assert hp.ns_steps == 5 and hp.nesterov == 0 and hp.clip_global == 0
 
 
 def fake_matrix(rows, cols, ld=None, w_dtype=mc.MC_BF16, g_dtype=mc.MC_F32, clip_slot=-1, period=0, segs=()):
@@ -70,6 +83,8 @@ def test_step_rejects_bad_arguments():
     assert step_status([fake_matrix(64, 64)], hp=hp) == mc.MC_ERR_HPARAM
     hp = mc.hparams(lr=float("nan"))
     assert step_status([fake_matrix(64, 64)], hp=hp) == mc.MC_ERR_HPARAM
+    assert step_status([fake_matrix(64, 64)], hp=mc.hparams(nesterov=2)) == mc.MC_ERR_HPARAM
+    assert step_status([fake_matrix(64, 64)], hp=mc.hparams(clip_global=-1)) == mc.MC_ERR_HPARAM
     # workspace: NULL, misaligned, too small
     assert step_status([fake_matrix(64, 64)], ws=None) == mc.MC_ERR_WORKSPACE
     assert step_status([fake_matrix(64, 64)], ws=0x400010) == mc.MC_ERR_WORKSPACE

@@ -61,6 +61,54 @@ def test_config1_tiny_mha_full_step(lr):
         assert rel_fro(d_g, d_o) < 2e-2
 
 
+def test_nesterov_step_matches_oracle():
+    # Nesterov-style momentum: the stored buffer is mu M + G, the matrix
+    # orthogonalised is G + mu (mu M + G)
+    print("config 1, nesterov", flush=True)
+    cfg = wl.config(1)
+    states = load_config_states(cfg)
+    hp = hp_for(cfg, lr=0.02, nesterov=1)
+    mc.muonclip_step([s.desc() for s in states], hp)
+    torch.cuda.synchronize()
+    for s in states:
+        check_matrix(s, hp)
+    # the variant is visible: the plain step's O differs
+    plain = load_config_states(cfg, indices=[0])
+    hp0 = hp_for(cfg, lr=0.02)
+    mc.muonclip_step([plain[0].desc()], hp0)
+    torch.cuda.synchronize()
+    assert rel_fro(host64(plain[0].o), host64(states[0].o)) > 5e-2
+
+
+@pytest.mark.parametrize("alpha", [0.5, 0.3])
+def test_global_clip_step_matches_oracle(alpha):
+    # the all-head variant: one gamma from the largest S_max of the layer,
+    # W_q rows scaled by gamma^alpha and W_k rows by gamma^(1 - alpha)
+    import dataclasses
+    print("config 1, global clip, alpha", alpha, flush=True)
+    cfg = wl.config(1)
+    q, k, ks = wl.draw_attention_inputs(cfg, weights_of(cfg))
+    qd, kd, _ = qk_to_device(q, k, ks, "f32")
+    s_gpu = mc.max_logits_per_head(qd, kd, None, causal=False)
+    s_orc = smax_oracle(cfg, q, k, None)
+    g_glob = oracle.clip_factor_global(s_orc, cfg.tau)
+    assert g_glob < min(oracle.clip_factor(s_orc, cfg.tau)) * 1.0000001
+    states = load_config_states(cfg)
+    for s in states:
+        if s.spec.name == "wq":
+            s.spec = dataclasses.replace(s.spec, segments=((0, s.spec.period, alpha),))
+        elif s.spec.name == "wk":
+            s.spec = dataclasses.replace(s.spec, segments=((0, s.spec.period, 1.0 - alpha),))
+    hp = hp_for(cfg, lr=0.02, clip_global=1)
+    gamma = torch.empty(4, dtype=torch.float32, device="cuda")
+    mc.muonclip_step([s.desc() for s in states], hp, s_max=s_gpu, slots=1, heads=4, gamma_out=gamma)
+    torch.cuda.synchronize()
+    g_gpu = host64(gamma)
+    assert np.allclose(g_gpu, g_glob, rtol=1e-3, atol=0) and np.all(g_gpu == g_gpu[0])
+    for s in states:
+        check_matrix(s, hp, np.full(4, g_glob), gamma_gpu=g_gpu)
+
+
 def test_cold_start_momentum_is_gradient():
     cfg = wl.config(1)
     states = load_config_states(cfg, indices=[0], cold=True)
