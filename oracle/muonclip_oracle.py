@@ -45,6 +45,12 @@ Readings where the pages are silent or garbled (each is listed in the design doc):
     look-ahead G_t + mu M_t.
   * Global clip ([K2-cn] 2.1, the naive variant): gamma from the largest
     S_max^h of the layer, NaN heads ignored by that max.
+  * AdamW for the parameters Muon does not cover ([Muon-blog] "Limitation":
+    only 2-D parameters; the rest still need AdamW; [Moonlight] "Scaling up
+    Muon": Muon and AdamW share the learning rate and weight decay). The pages
+    give no AdamW formula: the textbook form with bias correction and the
+    same decoupled decay as the Muon update is used; beta1, beta2 and eps are
+    arguments.
 """
 
 from __future__ import annotations
@@ -293,6 +299,32 @@ def muonclip_step_matrix(w, g, m, *, lr, mu, weight_decay, rms_scale=0.2,
     else:                                   # "f64": unrounded, for pins
         w_out = w_new
     return w_out, m_new.astype(np.float32), o
+
+
+# ---------------------------------------------------------------------------
+# AdamW for the non-matrix parameters
+# ---------------------------------------------------------------------------
+
+def adamw_step(p, g, m, v, *, lr, beta1, beta2, eps, weight_decay, step, p_dtype="bf16"):
+    """One AdamW update of a parameter vector (reading in the module
+    docstring): m <- b1 m + (1 - b1) g; v <- b2 v + (1 - b2) g^2;
+    p <- p - lr (m / (1 - b1^t) / (sqrt(v / (1 - b2^t)) + eps) + lambda p).
+    Returns (p_new rounded once to p_dtype as fp64 values, m_new and v_new as
+    fp32 values)."""
+    p = np.asarray(p, np.float64)
+    g = np.asarray(g, np.float64)
+    m_new = beta1 * np.asarray(m, np.float64) + (1.0 - beta1) * g
+    v_new = beta2 * np.asarray(v, np.float64) + (1.0 - beta2) * g * g
+    m_hat = m_new / (1.0 - beta1 ** step)
+    v_hat = v_new / (1.0 - beta2 ** step)
+    p_new = p - lr * (m_hat / (np.sqrt(v_hat) + eps) + weight_decay * p)
+    if p_dtype == "bf16":
+        p_out = round_to_bf16(p_new)
+    elif p_dtype == "f32":
+        p_out = p_new.astype(np.float32).astype(np.float64)
+    else:
+        p_out = p_new
+    return p_out, m_new.astype(np.float32), v_new.astype(np.float32)
 
 
 def ns_flops(rows: int, cols: int, steps: int = NS_STEPS) -> float:

@@ -386,3 +386,52 @@ def test_global_clip_special_cases():
     # NaN heads are ignored by the max; all-NaN gives gamma = 1
     assert oracle.clip_factor_global(np.array([np.nan, 400.0, 20.0]), 100.0) == 0.25
     assert oracle.clip_factor_global(np.array([np.nan, np.nan]), 100.0) == 1.0
+
+
+# ---------------------------------------------------------------- AdamW
+
+def test_adamw_first_step_is_a_sign_step():
+    # t = 1 from zero moments: both bias corrections undo (1 - beta), so the
+    # step is g / (|g| + eps), i.e. the sign of g up to eps
+    rng = np.random.default_rng(31)
+    p, g = rng.standard_normal((2, 50))
+    z = np.zeros(50)
+    kw = dict(lr=0.01, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, step=1, p_dtype="f64")
+    p1, m1, v1 = oracle.adamw_step(p, g, z, z, **kw)
+    assert np.allclose(p1, p - 0.01 * g / (np.abs(g) + 1e-8), rtol=0, atol=1e-15)
+    assert np.allclose(m1, 0.1 * g, rtol=1e-6) and np.allclose(v1, 0.05 * g * g, rtol=1e-6)
+
+
+def test_adamw_constant_gradient_closed_form():
+    # a constant gradient keeps m_hat = g and v_hat = g^2 exactly at every
+    # step (the bias corrections are what make this so), so after t steps
+    # without decay p_t = p_0 - t lr g / (|g| + eps); with decay each step
+    # also multiplies by (1 - lr lambda): a scalar recurrence, not the oracle
+    g = np.array([0.5, -2.0, 3e-3])
+    p0 = np.array([1.0, -1.0, 0.25])
+    lr, eps, lam = 1e-3, 1e-8, 0.1
+    p, m, v = p0.copy(), np.zeros(3), np.zeros(3)
+    for t in range(1, 41):
+        p, m, v = oracle.adamw_step(p, g, m, v, lr=lr, beta1=0.9, beta2=0.95, eps=eps,
+                                    weight_decay=lam, step=t, p_dtype="f64")
+        m, v = m.astype(np.float64), v.astype(np.float64)
+    want = p0.copy()
+    for _ in range(40):
+        want = want * (1.0 - lr * lam) - lr * g / (np.abs(g) + eps)
+    # m and v pass through fp32 each step: their rounding (2^-24 relative,
+    # at most ~2^-22 on m_hat / sqrt(v_hat)) is the only slack, 40 steps of lr
+    assert np.allclose(p, want, rtol=0, atol=40 * lr * 2.0 ** -21)
+    # a dropped bias correction or decay term is off by far more
+    assert abs(want[0] - (p0[0] - 40 * lr * g[0] / (abs(g[0]) + eps))) > 1e-3
+
+
+def test_adamw_decay_only_and_rounding():
+    # zero gradient and zero moments: only the decoupled decay acts, and the
+    # bf16 result is one round-to-nearest-even of p (1 - lr lambda)
+    p = oracle.round_to_bf16(np.linspace(-3.0, 3.0, 101))
+    z = np.zeros_like(p)
+    p1, _, _ = oracle.adamw_step(p, z, z, z, lr=0.01, beta1=0.9, beta2=0.95, eps=1e-8,
+                                 weight_decay=0.1, step=3, p_dtype="bf16")
+    import torch
+    want = torch.tensor(p * (1.0 - 0.001), dtype=torch.float64).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(p1, want)
