@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--experts", type=int, default=385, help="expert count for workloads 4/5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-s", type=float, default=15.0)
+    ap.add_argument("--adamw", action="store_true",
+                    help="time the AdamW entry point (the parameters Muon does not cover) on a "
+                         "synthetic set: one 512M-element vector plus 64 norm-sized vectors of 7168")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain streaming copy of MIB MiB (read + write) five times, "
                          "to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -177,6 +180,61 @@ def cpu_baseline(cfg, budget_s):
                       f" scaled by B*H" if a else f"{done_mats} matrices, scaled by NS FLOPs"}
 
 
+def adamw_bench(args):
+    """AdamW over bf16 parameters with fp32 gradients and moments: 24 bytes
+    per element (read p, g, m, v; write p, m, v). Prints its own JSON line."""
+    import torch
+
+    import muonclip_step_amd as mc
+    mc.load()
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    sizes = [512 * 1024 * 1024] + [7168] * 64
+    keep, vecs = [], []
+    for n in sizes:
+        p = (torch.randn(n, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+        g = torch.randn(n, generator=gen, device=dev) * 1e-3
+        m = torch.zeros(n, device=dev)
+        v = torch.zeros(n, device=dev)
+        keep += [p, g, m, v]
+        vecs.append(mc.vector(p, g, m, v))
+    elems = sum(sizes)
+    torch.cuda.synchronize()
+    for t in range(1, args.warmup + 1):
+        mc.adamw_step(vecs, mc.adamw_hparams(step=t))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for t in range(args.warmup + 1, args.warmup + 1 + args.steps):
+        mc.adamw_step(vecs, mc.adamw_hparams(step=t))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = elems * 24.0 / (ms * 1e-3) / 1e9
+    # context: a plain device copy of 4 GiB (read + write) on the same GPU
+    src = torch.empty(1 << 30, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 4 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    print(json.dumps({"metric": "AdamW GB/s (non-matrix parameters)", "value": round(gbs, 1), "unit": "GB/s",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+                      "higher_is_better": True, "dtype": "f32", "data": "synthetic",
+                      "config": {"workload": "adamw", "elements": elems, "vectors": len(sizes),
+                                 "bytes_per_element": 24},
+                      "copy_gbs": round(copy_gbs, 1),
+                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -187,6 +245,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.adamw:
+        adamw_bench(args)
         return
 
     import muonclip_step_amd as mc

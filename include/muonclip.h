@@ -175,6 +175,43 @@ mc_status max_logits_per_head(const void *q, const void *k, const void *k_shared
 mc_status qk_clip_apply(const mc_matrix *mats /* host, n */, int32_t n, const float *s_max,
                         int32_t slots, int32_t heads, float tau, float *gamma_out, void *stream);
 
+/* ---- AdamW for the parameters Muon does not cover (Notes on Muon blog,
+ * "Limitation": Muon is for 2-D parameters, the rest keep AdamW; Notes on
+ * Moonlight, "Scaling up Muon": the two share lr and weight decay). The pages
+ * give no AdamW formula; the textbook form with bias correction is used:
+ *   m <- b1 m + (1 - b1) g,   v <- b2 v + (1 - b2) g^2,
+ *   p <- p - lr ( m / (1 - b1^t) / (sqrt(v / (1 - b2^t)) + eps) + weight_decay p ).
+ * One contiguous parameter vector (norm weights, biases, embeddings flattened):
+ *   p  param, p_dtype (MC_F32 or MC_BF16), updated in place
+ *   g  gradient, g_dtype (MC_F32 or MC_BF16), read only
+ *   m, v  fp32 first and second moments, updated in place (zero at t = 1)
+ *   n  elements (0 allowed: nothing is touched)                              */
+typedef struct {
+  void *p;
+  const void *g;
+  float *m, *v;
+  int64_t n;
+  int32_t p_dtype, g_dtype;
+} mc_vector;
+
+/* lr, weight_decay as for Muon (defaults 2e-4, 0.1); beta1 0.9, beta2 0.95,
+ * eps 1e-8 by default (not on the pages); step t >= 1 (1-based). */
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay;
+  int32_t step;
+} mc_adamw_hparams;
+
+/* (host) Fill *hp with the defaults above (step 1). */
+void mc_default_adamw_hparams(mc_adamw_hparams *hp);
+
+/* One AdamW step over n vectors (host array). Validates everything before
+ * the first launch (NULL pointers, dtypes, alignment of each pointer to its
+ * element size, 0 <= beta < 1, eps >= 0, finite values, step >= 1); enqueues
+ * one launch per 16 vectors on `stream`; allocates nothing. Vectors must not
+ * overlap each other. */
+mc_status adamw_step(const mc_vector *vecs /* host, n */, int32_t n, const mc_adamw_hparams *hp /* host */,
+                     void *stream);
+
 /* (host) Text of the last non-OK status returned on this thread. */
 const char *mc_last_error(void);
 

@@ -22,7 +22,7 @@ MC_F32, MC_BF16 = 0, 1
 
 EXPORTS = ("mc_default_hparams", "mc_workspace_size", "mc_workspace_min_size", "muonclip_step",
            "max_logits_per_head", "qk_clip_apply", "mc_last_error", "mc_version",
-           "mc_profile_enable", "mc_profile_read")
+           "mc_profile_enable", "mc_profile_read", "mc_default_adamw_hparams", "adamw_step")
 
 
 class MuonClipError(RuntimeError):
@@ -47,6 +47,16 @@ class HParams(ctypes.Structure):
     _fields_ = [("lr", c_float), ("mu", c_float), ("weight_decay", c_float), ("rms_scale", c_float),
                 ("tau", c_float), ("ns_a", c_float), ("ns_b", c_float), ("ns_c", c_float),
                 ("ns_eps", c_float), ("ns_steps", c_int32), ("nesterov", c_int32), ("clip_global", c_int32)]
+
+
+class Vector(ctypes.Structure):
+    _fields_ = [("p", c_void_p), ("g", c_void_p), ("m", c_void_p), ("v", c_void_p), ("n", c_int64),
+                ("p_dtype", c_int32), ("g_dtype", c_int32)]
+
+
+class AdamWHParams(ctypes.Structure):
+    _fields_ = [("lr", c_float), ("beta1", c_float), ("beta2", c_float), ("eps", c_float),
+                ("weight_decay", c_float), ("step", c_int32)]
 
 
 class ProfileEntry(ctypes.Structure):
@@ -89,6 +99,10 @@ def load():
     lib.mc_profile_enable.restype = c_int32
     lib.mc_profile_read.argtypes = [POINTER(ProfileEntry), c_int32]
     lib.mc_profile_read.restype = c_int32
+    lib.mc_default_adamw_hparams.argtypes = [POINTER(AdamWHParams)]
+    lib.mc_default_adamw_hparams.restype = None
+    lib.adamw_step.argtypes = [POINTER(Vector), c_int32, POINTER(AdamWHParams), c_void_p]
+    lib.adamw_step.restype = c_int32
     _lib = lib
     return lib
 
@@ -204,6 +218,36 @@ def max_logits_per_head(q, k, k_shared=None, causal: bool = True, scale: float |
 def qk_clip_apply(mats, s_max, slots: int, heads: int, tau: float, gamma_out=None, stream=None):
     arr, n = _array(mats)
     _check(load().qk_clip_apply(arr, n, _ptr(s_max), slots, heads, tau, _ptr(gamma_out), _stream(stream)))
+
+
+def adamw_hparams(**kw) -> AdamWHParams:
+    """Default AdamW hyper-parameters with keyword overrides."""
+    hp = AdamWHParams()
+    load().mc_default_adamw_hparams(ctypes.byref(hp))
+    for k, v in kw.items():
+        setattr(hp, k, v)
+    return hp
+
+
+def vector(p, g, m, v) -> Vector:
+    """Describe one non-matrix parameter: contiguous tensors of one size."""
+    for t in (p, g, m, v):
+        if not t.is_contiguous():
+            raise ValueError("AdamW tensors must be contiguous")
+    if not (p.numel() == g.numel() == m.numel() == v.numel()):
+        raise ValueError("p, g, m, v must have the same number of elements")
+    d = Vector()
+    d.p, d.g, d.m, d.v = p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr()
+    d.n = p.numel()
+    d.p_dtype, d.g_dtype = _dtype_code(p), _dtype_code(g)
+    return d
+
+
+def adamw_step(vecs, hp: AdamWHParams | None = None, stream=None):
+    """One AdamW step over `vecs` (list of Vector) on the current stream."""
+    hp = hp or adamw_hparams()
+    arr = (Vector * max(1, len(vecs)))(*vecs)
+    _check(load().adamw_step(arr, len(vecs), ctypes.byref(hp), _stream(stream)))
 
 
 def profile_enable(on: bool = True):

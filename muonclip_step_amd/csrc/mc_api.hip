@@ -57,11 +57,11 @@ constexpr int kSplitThreshold = 1024;   // m below this: hi/lo operand pairs
 
 enum Family {
   F_MOMENTUM = 0, F_NORM, F_GEMM, F_SPLITK, F_UPDATE, F_GAMMA, F_CLIP,
-  F_ML_INIT, F_ML, F_ML_FIN, F_COUNT
+  F_ML_INIT, F_ML, F_ML_FIN, F_ADAMW, F_COUNT
 };
 const char* kFamilyNames[F_COUNT] = {"momentum_norm", "norm_finalize", "ns_gemm", "splitk_reduce",
                                      "update_clip", "gamma", "clip_apply", "max_logits_init",
-                                     "max_logits", "max_logits_finalize"};
+                                     "max_logits", "max_logits_finalize", "adamw"};
 
 struct ProfRec { int fam; hipEvent_t a, b; double flops, bytes; };
 std::mutex g_prof_mu;
@@ -620,6 +620,79 @@ mc_status qk_clip_apply(const mc_matrix* mats, int32_t n, const float* s_max, in
     if (e != hipSuccess) return fail(MC_ERR_HIP, "clip_apply launch: %s", hipGetErrorString(e));
   }
   return MC_OK;
+}
+
+void mc_default_adamw_hparams(mc_adamw_hparams* hp) {
+  if (!hp) return;
+  hp->lr = 2e-4f; hp->beta1 = 0.9f; hp->beta2 = 0.95f; hp->eps = 1e-8f; hp->weight_decay = 0.1f; hp->step = 1;
+}
+
+mc_status adamw_step(const mc_vector* vecs, int32_t n, const mc_adamw_hparams* hp, void* stream) {
+  if (!hp) return fail(MC_ERR_NULL, "hparams is NULL");
+  const float v[] = {hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay};
+  for (float x : v)
+    if (!isfinite(x)) return fail(MC_ERR_HPARAM, "AdamW hyper-parameters must be finite");
+  if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+    return fail(MC_ERR_HPARAM, "beta1 and beta2 must be in [0, 1)");
+  if (hp->eps < 0.0f) return fail(MC_ERR_HPARAM, "eps must be >= 0");
+  if (hp->step < 1) return fail(MC_ERR_HPARAM, "step must be >= 1 (got %d)", hp->step);
+  if (n < 0) return fail(MC_ERR_SHAPE, "n < 0");
+  if (n > 0 && !vecs) return fail(MC_ERR_NULL, "vecs is NULL");
+  for (int i = 0; i < n; ++i) {
+    const mc_vector& d = vecs[i];
+    if (d.n < 0) return fail(MC_ERR_SHAPE, "vector %d: n < 0", i);
+    if (d.n == 0) continue;
+    if (d.n > ((int64_t)1 << 40)) return fail(MC_ERR_SHAPE, "vector %d: n above 2^40", i);
+    if (!d.p || !d.g || !d.m || !d.v) return fail(MC_ERR_NULL, "vector %d: p, g, m or v is NULL", i);
+    if (!dtype_ok(d.p_dtype) || !dtype_ok(d.g_dtype)) return fail(MC_ERR_DTYPE, "vector %d: dtype", i);
+    if (!aligned(d.p, dtype_size(d.p_dtype)) || !aligned(d.g, dtype_size(d.g_dtype)) || !aligned(d.m, 4) ||
+        !aligned(d.v, 4))
+      return fail(MC_ERR_ALIGN, "vector %d: misaligned pointer", i);
+  }
+  // bias corrections in double, then fp32 like every other hyper-parameter
+  const double c1 = 1.0 / (1.0 - pow((double)hp->beta1, (double)hp->step));
+  const double c2 = 1.0 / (1.0 - pow((double)hp->beta2, (double)hp->step));
+  hipStream_t s = (hipStream_t)stream;
+  AdamArgs a{};
+  auto flush = [&]() -> mc_status {
+    if (a.nvec == 0) return MC_OK;
+    double bytes = 0;
+    for (int k = 0; k < a.nvec; ++k)
+      bytes += (double)a.vec[k].n * (2.0 * (a.vec[k].p_bf16 ? 2 : 4) + (a.vec[k].g_bf16 ? 2 : 4) + 16.0);
+    Prof pr(F_ADAMW, s, 0.0, bytes);
+    hipError_t e = launch_adamw(a, s);
+    if (e != hipSuccess) return fail(MC_ERR_HIP, "adamw launch: %s", hipGetErrorString(e));
+    a.nvec = 0; a.total_blocks = 0;
+    return MC_OK;
+  };
+  a.lr = hp->lr; a.beta1 = hp->beta1; a.beta2 = hp->beta2;
+  a.one_m_beta1 = 1.0f - hp->beta1; a.one_m_beta2 = 1.0f - hp->beta2; a.eps = hp->eps;
+  a.decay = (float)(1.0 - (double)hp->lr * (double)hp->weight_decay);
+  a.c1 = (float)c1; a.c2 = (float)c2;
+  for (int i = 0; i < n; ++i) {
+    const mc_vector& d = vecs[i];
+    if (d.n == 0) continue;
+    // a vector whose blocks would overflow one launch's grid index is split
+    for (int64_t off = 0; off < d.n;) {
+      const int64_t room = ((int64_t)1 << 30) - a.total_blocks;
+      const int64_t chunk = std::min<int64_t>(d.n - off, room * 4096);
+      if (a.nvec == kMaxBatchVecs || chunk <= 0) {
+        mc_status st = flush();
+        if (st) return st;
+        continue;
+      }
+      AdamVec& v2 = a.vec[a.nvec++];
+      const size_t pe = dtype_size(d.p_dtype), ge = dtype_size(d.g_dtype);
+      v2.p = (char*)d.p + off * pe; v2.g = (const char*)d.g + off * ge;
+      v2.m = d.m + off; v2.v = d.v + off; v2.n = chunk;
+      v2.p_bf16 = d.p_dtype == MC_BF16; v2.g_bf16 = d.g_dtype == MC_BF16;
+      v2.vec = aligned(v2.p, 4 * pe) && aligned(v2.g, 4 * ge) && aligned(v2.m, 16) && aligned(v2.v, 16);
+      v2.block_start = a.total_blocks;
+      a.total_blocks += (int32_t)adamw_blocks(chunk);
+      off += chunk;
+    }
+  }
+  return flush();
 }
 
 mc_status mc_profile_enable(int32_t on) {

@@ -143,6 +143,24 @@ struct ClipApplyArgs {
 };
 hipError_t launch_clip_apply(const ClipApplyArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------- AdamW
+
+constexpr int kMaxBatchVecs = 16;
+struct AdamVec {
+  void* p; const void* g; float* m; float* v;
+  int64_t n;
+  int32_t p_bf16, g_bf16, vec;         // vec: 16-byte fp32 / 8-byte bf16 accesses allowed
+  int32_t block_start;
+};
+// decay = 1 - lr wd, c1 = 1 / (1 - beta1^t), c2 = 1 / (1 - beta2^t)
+struct AdamArgs {
+  int32_t nvec, total_blocks;
+  float lr, beta1, beta2, one_m_beta1, one_m_beta2, eps, decay, c1, c2;
+  AdamVec vec[kMaxBatchVecs];
+};
+int64_t adamw_blocks(int64_t n);   // blocks one vector of n elements needs
+hipError_t launch_adamw(const AdamArgs& a, hipStream_t s);
+
 // ---------------------------------------------------------------- max logits
 
 struct MaxLogitArgs {

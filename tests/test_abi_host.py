@@ -18,7 +18,7 @@ def declared_functions():
     names = set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text))
     keywords = {"if", "sizeof", "defined", "return"}
     return sorted(n for n in names if n not in keywords and (n.startswith("mc_") or n in (
-        "muonclip_step", "max_logits_per_head", "qk_clip_apply")))
+        "muonclip_step", "max_logits_per_head", "qk_clip_apply", "adamw_step")))
 
 
 def test_library_exports_every_declared_function():
@@ -161,3 +161,32 @@ def test_oracle_and_product_are_independent():
             assert "muonclip_step_amd" not in txt and "libmuonclip" not in txt
     ws = open(os.path.join(root, "workloads", "__init__.py")).read()
     assert "import oracle" not in ws and "muonclip_step_amd" not in ws
+
+
+def test_adamw_defaults_and_rejections():
+    hp = mc.adamw_hparams()
+    assert abs(hp.lr - 2e-4) < 1e-10 and abs(hp.beta1 - 0.9) < 1e-7 and abs(hp.beta2 - 0.95) < 1e-7
+    assert abs(hp.eps - 1e-8) < 1e-14 and abs(hp.weight_decay - 0.1) < 1e-7 and hp.step == 1
+    lib = mc.load()
+
+    def status(vecs, **kw):
+        arr = (mc.Vector * max(1, len(vecs)))(*vecs)
+        return lib.adamw_step(arr, len(vecs), ctypes.byref(mc.adamw_hparams(**kw)), None)
+
+    def vec(n=16, p=0x100000, g=0x200000, m=0x300000, v=0x400000, pd=mc.MC_BF16, gd=mc.MC_F32):
+        d = mc.Vector()
+        d.p, d.g, d.m, d.v, d.n, d.p_dtype, d.g_dtype = p, g, m, v, n, pd, gd
+        return d
+
+    assert status([]) == mc.MC_OK
+    assert status([vec(n=0, p=None)]) == mc.MC_OK            # empty vectors are never touched
+    assert status([vec(p=None)]) == mc.MC_ERR_NULL
+    assert status([vec(n=-1)]) == mc.MC_ERR_SHAPE
+    assert status([vec(pd=5)]) == mc.MC_ERR_DTYPE
+    assert status([vec(m=0x300002)]) == mc.MC_ERR_ALIGN
+    assert status([vec(p=0x100001)]) == mc.MC_ERR_ALIGN
+    assert status([vec()], step=0) == mc.MC_ERR_HPARAM
+    assert status([vec()], beta1=1.0) == mc.MC_ERR_HPARAM
+    assert status([vec()], beta2=-0.1) == mc.MC_ERR_HPARAM
+    assert status([vec()], eps=-1e-8) == mc.MC_ERR_HPARAM
+    assert status([vec()], lr=float("inf")) == mc.MC_ERR_HPARAM
