@@ -3,9 +3,10 @@
 //  momentum_kernel   M <- mu M + G (Notes on Moonlight, "Background"), the
 //                    per-block sum of squares of the new M (or of the Nesterov
 //                    look-ahead G + mu M, Notes on Muon blog, "Analysis") for
-//                    its Frobenius norm, and its bf16 copy in both orientations that the
-//                    Newton-Schulz GEMMs read (Notes on Muon blog, "Algorithm":
-//                    bf16 copy, normalisation, transpose when rows > cols). The
+//                    its Frobenius norm, and its bf16 copy in the [min][max]
+//                    orientation the Newton-Schulz GEMMs read (Notes on Muon
+//                    blog, "Algorithm": bf16 copy, normalisation, transpose
+//                    when rows > cols; a 64x64 LDS tile transposes). The
 //                    1/(||M||+eps) scale is not applied here; the first GEMM
 //                    epilogues fold it in.
 //  norm_finalize     fixed-order fp64 sum of the partials -> scale per matrix.
@@ -118,13 +119,14 @@ __global__ void __launch_bounds__(256) momentum_kernel(const MomArgs a) {
       tile[lr][cx * 4 + e] = h[e];
     }
     // stored orientation (zeros in the padding)
-    *(u16x4_t*)(mm.x_orig + (int64_t)row * mm.ld_orig + col) = h;
+    if (mm.x_orig) *(u16x4_t*)(mm.x_orig + (int64_t)row * mm.ld_orig + col) = h;
   }
   // block sum of squares (fixed order)
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
   if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
   if (tid == 0) mm.partial[local] = (red[0] + red[1]) + (red[2] + red[3]);
+  if (!mm.x_tr) return;
   // transposed orientation: output row tc*64 + jj, 16 consecutive elements
   const int jj = tid >> 2, i0 = (tid & 3) * 16;
   uint16_t o[16];
@@ -172,12 +174,26 @@ hipError_t launch_norm_finalize(const float* partial, int32_t parts, int64_t str
 // ---------------------------------------------------------------- update
 
 __global__ void __launch_bounds__(256) update_kernel(const UpdArgs a) {
+  __shared__ uint16_t ot[64][66];
   const int j = find_mat(a.mat, a.nmat, blockIdx.x);
   const UpdMat& u = a.mat[j];
   const int local = blockIdx.x - u.block_start;
   const int tr = local / u.tiles_c, tc = local - tr * u.tiles_c;
   const int tid = threadIdx.x, cx = tid & 15, ry = tid >> 4;
   const int col = tc * 64 + cx * 4;
+  if (u.o_trans) {
+    // O is stored [cols][rows] (a tall matrix iterates on its transpose):
+    // stage the 64x64 tile through LDS. The buffer is padded to multiples of
+    // 64 in both directions, so the whole tile is in bounds.
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int oc = tc * 64 + ry + 16 * k;        // W column = O row
+      const u16x4_t v = *(const u16x4_t*)(u.o + (int64_t)oc * u.ld_o + tr * 64 + cx * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ot[ry + 16 * k][cx * 4 + e] = v[e];
+    }
+    __syncthreads();
+  }
   if (col >= u.cols) return;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -186,8 +202,17 @@ __global__ void __launch_bounds__(256) update_kernel(const UpdArgs a) {
     const float sc = row_clip_scale(u.clip, row, a.s_max, a.heads, a.tau, a.clip_global);
     const int64_t wb = (int64_t)row * u.ld + col;
     const uint16_t* op = u.o + (int64_t)row * u.ld_o + col;
+    u16x4_t ov;
+    if (u.o_trans) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[e] = ot[cx * 4 + e][ry + 16 * k];
+    } else if (u.vec) {
+      ov = *(const u16x4_t*)op;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[e] = col + e < u.cols ? op[e] : (uint16_t)0;
+    }
     if (u.vec) {
-      const u16x4_t ov = *(const u16x4_t*)op;
       float o[4] = {bf16_to_f32(ov[0]), bf16_to_f32(ov[1]), bf16_to_f32(ov[2]), bf16_to_f32(ov[3])};
       if (u.o_out) *(u16x4_t*)(u.o_out + (int64_t)row * u.cols + col) = ov;
       if (u.w_bf16) {
@@ -210,7 +235,7 @@ __global__ void __launch_bounds__(256) update_kernel(const UpdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (col + e >= u.cols) break;
-        const uint16_t ob = op[e];
+        const uint16_t ob = ov[e];
         const float o = bf16_to_f32(ob);
         if (u.o_out) u.o_out[(int64_t)row * u.cols + col + e] = ob;
         if (u.w_bf16) {

@@ -3,11 +3,11 @@
 // muonclip_step: matrices are grouped by (m, n) = (min, max) of their shape;
 // each group runs in waves of as many matrices as the workspace holds. Per
 // wave, on the caller's stream:
-//   momentum_kernel   M <- mu M + G, norm partials, bf16 X0 in both layouts
+//   momentum_kernel   M <- mu M + G, norm partials, bf16 X0 ([m][n]: M or M^T)
 //   norm_finalize     s = 1 / (||M||_F + eps)
 //   5 x { Gram  A = s0^2 X X^T          -> A as a bf16 pair A_hi + A_lo
 //         Poly  P = a I + b A + c A A   -> P_hi (+ P_lo if m < 1024)
-//         Apply X' = s0 P X             -> X', X'^T  (last step: O) }
+//         Apply X' = s0 P X             -> X' (ping-pong; last step: O) }
 //   update_kernel     W <- clip_row ((1 - lr wd) W - lr rms sqrt(max) O)
 // (s0 = s on the first step, 1 after). The apply is the quintic step of the
 // Notes on Muon blog, "Newton-Schulz", written as X' = (aI + bA + cA^2) X.
@@ -236,7 +236,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int ktiles, int batch, bool sym, bool r
 
 struct WavePlan {
   int nb;
-  size_t off_x, off_xt0, off_xt1, off_ahi, off_alo, off_phi, off_plo, off_part, off_scale, off_splitk;
+  size_t off_x0, off_x1, off_ahi, off_alo, off_phi, off_plo, off_part, off_scale, off_splitk;
   size_t bytes;
   int64_t mom_blocks;          // momentum blocks per matrix
   GemmPlan gram, poly, apply;
@@ -249,9 +249,8 @@ WavePlan plan_wave(const Group& g, int nb) {
   const size_t mp = (size_t)g.mp, np = (size_t)g.np;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
-  w.off_x = take(nb * mp * np * 2);
-  w.off_xt0 = take(nb * np * mp * 2);
-  w.off_xt1 = take(nb * np * mp * 2);
+  w.off_x0 = take(nb * mp * np * 2);
+  w.off_x1 = take(nb * mp * np * 2);
   w.off_ahi = take(nb * mp * mp * 2);
   w.off_alo = take(nb * mp * mp * 2);
   w.off_phi = take(nb * mp * mp * 2);
@@ -306,8 +305,8 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
                    const float* s_max, int32_t heads, char* ws, hipStream_t s) {
   const WavePlan w = plan_wave(g, nb);
   const int64_t mp = g.mp, np = g.np;
-  uint16_t* X = (uint16_t*)(ws + w.off_x);
-  uint16_t* XT[2] = {(uint16_t*)(ws + w.off_xt0), (uint16_t*)(ws + w.off_xt1)};
+  // X ping-pong: iteration it reads X[it % 2] and writes X[(it + 1) % 2]
+  uint16_t* X[2] = {(uint16_t*)(ws + w.off_x0), (uint16_t*)(ws + w.off_x1)};
   uint16_t* Ahi = (uint16_t*)(ws + w.off_ahi);
   uint16_t* Alo = (uint16_t*)(ws + w.off_alo);
   uint16_t* Phi = (uint16_t*)(ws + w.off_phi);
@@ -315,7 +314,7 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
   float* part = (float*)(ws + w.off_part);
   float* scale = (float*)(ws + w.off_scale);
 
-  // 1. momentum + norm partials + bf16 X0 in both orientations
+  // 1. momentum + norm partials + bf16 X0 = M (wide) or M^T (tall), [mp][np]
   for (int b0 = 0; b0 < nb; b0 += kMaxBatchMats) {
     MomArgs a{};
     a.mu = hp.mu; a.nesterov = hp.nesterov;
@@ -330,16 +329,15 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
       mm.rows = (int32_t)m.rows; mm.cols = (int32_t)m.cols;
       mm.g_bf16 = m.g_dtype == MC_BF16;
       mm.vec = (m.cols % 4 == 0) && (m.ld % 4 == 0) && aligned(m.m, 16) && aligned(m.g, 4 * dtype_size(m.g_dtype));
-      uint16_t* xs = X + (size_t)slot * mp * np;
-      uint16_t* xts = XT[0] + (size_t)slot * np * mp;
-      mm.x_orig = wide ? xs : xts; mm.ld_orig = (int32_t)(wide ? np : mp);
-      mm.x_tr = wide ? xts : xs;   mm.ld_tr = (int32_t)(wide ? mp : np);
+      uint16_t* xs = X[0] + (size_t)slot * mp * np;
+      mm.x_orig = wide ? xs : nullptr; mm.ld_orig = (int32_t)np;
+      mm.x_tr = wide ? nullptr : xs;   mm.ld_tr = (int32_t)np;
       mm.rp = (int32_t)(wide ? mp : np); mm.cp = (int32_t)(wide ? np : mp);
       mm.tiles_c = mm.cp / 64;
       mm.block_start = blocks;
       mm.partial = part + (size_t)slot * w.mom_blocks;
       blocks += (mm.rp / 64) * mm.tiles_c;
-      bytes += (double)m.rows * m.cols * (dtype_size(m.g_dtype) + 8);
+      bytes += (double)m.rows * m.cols * (dtype_size(m.g_dtype) + 8);   // read G, M; write M
     }
     a.total_blocks = blocks;
     Prof pr(F_MOMENTUM, s, 0.0, bytes);
@@ -355,15 +353,15 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
   // 2. Newton-Schulz iterations
   const double mm_ = (double)g.m, nn_ = (double)g.n;
   for (int it = 0; it < hp.ns_steps; ++it) {
-    const bool first = it == 0, last = it == hp.ns_steps - 1;
-    uint16_t* xt_cur = XT[it & 1];
-    uint16_t* xt_nxt = XT[(it + 1) & 1];
+    const bool first = it == 0;
+    uint16_t* x_cur = X[it & 1];
+    uint16_t* x_nxt = X[(it + 1) & 1];
     // Gram: A = s0^2 X X^T, stored as a bf16 pair A_hi + A_lo
     {
       GemmArgs a{};
       a.M = (int32_t)mp; a.N = (int32_t)mp; a.batch = nb;
       a.lda = (int32_t)np; a.ldb = (int32_t)np; a.bsa = mp * np; a.bsb = mp * np;
-      a.nseg = 1; a.seg[0] = {X, X, w.kt_gram}; a.ktiles = w.kt_gram;
+      a.nseg = 1; a.seg[0] = {x_cur, x_cur, w.kt_gram}; a.ktiles = w.kt_gram;
       a.epi.alpha = 1.0f; a.epi.scale_pow = first ? 2 : 0; a.epi.scale = scale;
       a.epi.out_hi = Ahi; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
       a.epi.out_lo = Alo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp;
@@ -392,22 +390,17 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
                                          2.0 * mm_ * mm_ * mm_ * nb);
       if (st) return st;
     }
-    // Apply: X' = s0 P X, read as C[i][j] = sum_k P[i][k] X^T[j][k]
+    // Apply: X' = s0 P X, C[i][j] = sum_k P[i][k] X[k][j] with X read as [k][n]
     {
       GemmArgs a{};
       a.M = (int32_t)mp; a.N = (int32_t)np; a.batch = nb;
-      a.lda = (int32_t)mp; a.ldb = (int32_t)mp; a.bsa = mp * mp; a.bsb = np * mp;
+      a.lda = (int32_t)mp; a.ldb = (int32_t)np; a.bsa = mp * mp; a.bsb = mp * np;
       const int kt = (int)(mp / kGemmBK);
-      if (g.split) { a.nseg = 2; a.seg[0] = {Phi, xt_cur, kt}; a.seg[1] = {Plo, xt_cur, kt}; }
-      else { a.nseg = 1; a.seg[0] = {Phi, xt_cur, kt}; }
+      if (g.split) { a.nseg = 2; a.seg[0] = {Phi, x_cur, kt}; a.seg[1] = {Plo, x_cur, kt}; }
+      else { a.nseg = 1; a.seg[0] = {Phi, x_cur, kt}; }
       a.ktiles = w.kt_apply;
       a.epi.alpha = 1.0f; a.epi.scale_pow = first ? 1 : 0; a.epi.scale = scale;
-      // both layouts every step: the next Gram reads X, the next apply X^T;
-      // after the last step O is read from whichever matches the matrix's
-      // own orientation (one group can mix [m][n] and [n][m] matrices)
-      a.epi.out_hi = X; a.epi.ld_hi = (int32_t)np; a.epi.bs_hi = mp * np;
-      a.epi.out_t = xt_nxt; a.epi.ld_t = (int32_t)mp; a.epi.bs_t = np * mp;
-      (void)last;
+      a.epi.out_hi = x_nxt; a.epi.ld_hi = (int32_t)np; a.epi.bs_hi = mp * np;
       mc_status st = launch_gemm_planned(w.apply, GEMM_APPLY, false, a, s, ws, w.off_splitk,
                                          2.0 * mm_ * mm_ * nn_ * nb);
       if (st) return st;
@@ -415,7 +408,7 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
   }
 
   // 3. update + decay + QK-Clip rows
-  uint16_t* xt_final = XT[hp.ns_steps & 1];
+  uint16_t* x_final = X[hp.ns_steps & 1];   // O in [m][n]: W itself (wide) or W^T (tall)
   const float decay = (float)(1.0 - (double)hp.lr * (double)hp.weight_decay);
   for (int b0 = 0; b0 < nb; b0 += kMaxBatchMats) {
     UpdArgs a{};
@@ -431,8 +424,9 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
       u.rows = (int32_t)m.rows; u.cols = (int32_t)m.cols;
       u.vec = (m.cols % 4 == 0) && (m.ld % 4 == 0) && aligned(m.w, 4 * dtype_size(m.w_dtype)) &&
               (!m.o_out || aligned(m.o_out, 8));
-      u.o = wide ? X + (size_t)slot * mp * np : xt_final + (size_t)slot * np * mp;
-      u.ld_o = (int32_t)(wide ? np : mp);
+      u.o = x_final + (size_t)slot * mp * np;
+      u.ld_o = (int32_t)np;
+      u.o_trans = wide ? 0 : 1;
       u.o_out = (uint16_t*)m.o_out;
       u.lr_rms = (float)((double)hp.lr * (double)hp.rms_scale * sqrt((double)std::max(m.rows, m.cols)));
       u.clip = clip_rule(m, s_max != nullptr);

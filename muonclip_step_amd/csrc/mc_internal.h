@@ -26,8 +26,8 @@ __host__ __device__ inline float bf16_to_f32(uint16_t h) {
 
 // ---------------------------------------------------------------- NS GEMM
 
-// One K segment of C = sum_s A_s B_s^T; both operands are bf16 row-major with
-// the contraction index contiguous ("NT" form).
+// One K segment of C = sum_s A_s B_s: A bf16 row-major [M][K]; B bf16 either
+// [N][K] ("NT", the Gram and Poly products) or [K][N] (the apply).
 constexpr int kGemmBK = 64;   // k per pipeline stage of the NS GEMM
 
 struct GemmSeg {
@@ -38,7 +38,7 @@ struct GemmSeg {
 
 // Epilogue: v = alpha * scale[b]^pow * acc + beta * (cin_hi + cin_lo)[i][j]
 // + diag * (i==j), then any of: bf16 store (hi), bf16 residual store
-// (lo = v - hi), bf16 store of the transpose. cin is a bf16 hi + lo pair
+// (lo = v - hi). cin is a bf16 hi + lo pair
 // (about 16 significant bits). Every pointer is the batch-0 base; bs_* are the
 // per-batch strides in elements.
 struct GemmEpi {
@@ -50,7 +50,6 @@ struct GemmEpi {
   float diag;
   uint16_t* out_hi; int32_t ld_hi; int64_t bs_hi;
   uint16_t* out_lo; int32_t ld_lo; int64_t bs_lo;
-  uint16_t* out_t; int32_t ld_t; int64_t bs_t;
 };
 
 struct GemmArgs {
@@ -71,7 +70,7 @@ enum GemmTile { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2 };
 // which Newton-Schulz product a launch computes; fixes the epilogue:
 //   GRAM  A = s^2 X X^T      -> bf16 A_hi + A_lo           (symmetric tiles)
 //   POLY  P = a I + b A + c A A -> bf16 P_hi (+ P_lo)        (symmetric tiles)
-//   APPLY X' = s P X          -> bf16 X' and its transpose
+//   APPLY X' = s P X          -> bf16 X' (B = X read as [k][n])
 enum GemmKind { GEMM_GRAM = 0, GEMM_POLY = 1, GEMM_APPLY = 2 };
 int gemm_tile_dim(GemmTile t);
 // workgroups per matrix and split (symmetric products count upper tiles only)
@@ -84,13 +83,13 @@ hipError_t launch_splitk_reduce(const GemmArgs& a, hipStream_t s);
 
 constexpr int kMaxBatchMats = 8;
 
-// momentum update + sum of squares + bf16 copies in both orientations
+// momentum update + sum of squares + bf16 copy in one orientation
 struct MomMat {
   const void* g; float* m;
   int64_t ld;
   int32_t rows, cols, g_bf16, vec;
-  uint16_t* x_orig; int32_t ld_orig;   // [rp][cp], the stored orientation
-  uint16_t* x_tr;   int32_t ld_tr;     // [cp][rp]
+  uint16_t* x_orig; int32_t ld_orig;   // [rp][cp], the stored orientation, or NULL
+  uint16_t* x_tr;   int32_t ld_tr;     // [cp][rp], or NULL
   int32_t rp, cp;                      // padded extents, multiples of 64
   int32_t tiles_c;                     // cp / 64
   int32_t block_start;
@@ -116,6 +115,7 @@ struct UpdMat {
   int64_t ld;
   int32_t rows, cols;
   const uint16_t* o; int32_t ld_o;
+  int32_t o_trans;                     // O is stored transposed: element (r, c) at o[c * ld_o + r]
   uint16_t* o_out;                     // optional copy of O, [rows][cols] contiguous
   float lr_rms;
   ClipRule clip;

@@ -1,28 +1,28 @@
 // bf16 MFMA GEMM for the Newton-Schulz chains of the MuonClip step.
 //
 // Every product of the quintic iteration (Notes on Muon blog, "Newton-Schulz"
-// and "Algorithm": A = X X^T, A A, and the P X apply) is written in the "NT"
-// form C[i][j] = sum_k A[i][k] B[j][k] with both operands row-major and the
-// contraction index contiguous: X X^T reads X twice, A A reads the symmetric
-// A twice, and P X reads P and the transposed copy X^T that the previous
-// apply wrote. One kernel therefore serves all three, batched over the
-// matrices of one shape group (grid = tiles x splits x batch, mapped
-// XCD-major so the tiles of one matrix share an XCD's L2). The two symmetric
-// products (X X^T and A A) compute only the tiles on and above the diagonal
+// and "Algorithm": A = X X^T, A A, and the P X apply) is C[i][j] = sum_k
+// A[i][k] B[k][j] with A row-major and k contiguous. X X^T and the symmetric
+// A A read their B operand as rows of the same row-major matrix ("NT" form:
+// B[k][j] = X[j][k]); the apply P X reads B = X in its own row-major [k][n]
+// layout and forms the MFMA B fragments with gfx950's transposing LDS read,
+// so no transposed copy of X is ever written. One kernel serves all three,
+// batched over the matrices of one shape group (grid = tiles x splits x
+// batch, mapped XCD-major so the tiles of one matrix share an XCD's L2). The
+// two symmetric products compute only the tiles on and above the diagonal
 // and store each off-diagonal tile a second time, transposed.
 //
 // gfx950 design: v_mfma_f32_32x32x16_bf16 with fp32 accumulation; a block of
 // 2x2 waves owns a BMxBN tile, each wave a (BM/2)x(BN/2) sub-tile. K advances
-// in 64-wide stages (one 128-byte row segment per operand row) held in a
-// two-slot LDS ring that direct-to-LDS loads (global_load_lds_dwordx4) fill,
-// so no register staging is needed. One barrier per stage retires a slot;
-// the loads of the stage after next go out in two halves, under the last
-// k-step of one stage and the first k-step of the next, each load placed
-// between two MFMAs, and every memory instruction of the steady-state loop
-// is unconditional (the last stage is peeled). The MFMA fragments of each
-// 16-k step are read from LDS while the previous step's MFMAs run. The
-// epilogue is specialised at compile time per use and stores straight from
-// the accumulator registers.
+// in 64-wide stages held in a two-slot LDS ring that direct-to-LDS loads
+// (global_load_lds_dwordx4) fill, so no register staging is needed. One
+// barrier per stage retires a slot; the loads of the stage after next go out
+// in two halves, under the last k-step of one stage and the first k-step of
+// the next, each load placed between two MFMAs, and every memory instruction
+// of the steady-state loop is unconditional (the last stage is peeled). The
+// MFMA fragments of each 16-k step are read from LDS while the previous
+// step's MFMAs run. The epilogue is specialised at compile time per use and
+// stages each wave's results through LDS for 16-byte stores.
 #include "mc_internal.h"
 
 namespace mc {
@@ -59,7 +59,6 @@ __device__ __attribute__((always_inline)) inline void epilogue_store(const GemmE
   const uint16_t h = f32_to_bf16(v);
   if (e.out_hi) e.out_hi[(int64_t)b * e.bs_hi + (int64_t)i * e.ld_hi + j] = h;
   if (e.out_lo) e.out_lo[(int64_t)b * e.bs_lo + (int64_t)i * e.ld_lo + j] = f32_to_bf16(v - bf16_to_f32(h));
-  if (e.out_t) e.out_t[(int64_t)b * e.bs_t + (int64_t)j * e.ld_t + i] = h;
 }
 
 __device__ __attribute__((always_inline)) inline float batch_scale(const GemmEpi& e, int b) {
@@ -96,7 +95,6 @@ struct FragVisit<N, N, FN> {
 enum : int {
   E_HI = 2,       // bf16 store of v
   E_LO = 4,       // bf16 store of v - bf16(v)
-  E_T = 8,        // bf16 store of v at the transposed position
   E_CIN = 16,     // v += beta * (cin_hi + cin_lo)[i][j]
   E_DIAG = 32,    // v += diag on i == j
   E_PART = 64,    // split-K: raw fp32 partial, no epilogue
@@ -112,9 +110,18 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at max)
 #define MC_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | 0x70 | 0xF00 | (((n) >> 4) << 14))
 
-template <int BM, int BN, int NSTAGE, int EPI>
+template <int BM, int BN, int NSTAGE, int EPI, int NNB = 0>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 ns_gemm_kernel(const GemmArgs p) {
+  // NNB: the B operand is stored [k][n] (n contiguous) and staged in LDS the
+  // same way, BN columns per k-row; its fragments are read with
+  // ds_read_b64_tr_b16, whose 16-lane groups read four k-rows of 32 bytes.
+  // The 16-byte chunks of k-row r are XOR-swizzled so those four rows land on
+  // distinct banks: ^ 4 (r & 3) for rows of 16 or more chunks, ^ 2 ((r >> 1) & 1)
+  // for 128-byte rows (odd rows start half a bank cycle later).
+  constexpr int PB = BN * 2;                      // bytes per LDS row of the [k][n] B tile
+  constexpr int LPR = BN / 8, RPB = 64 / LPR;     // lanes per B row, B rows per DMA instruction
+  auto swzB = [](int r) { return LPR >= 16 ? 4 * (r & 3) : 2 * ((r >> 1) & 1); };
   constexpr int BK = kGemmBK;                     // 64: one 128-byte row segment per operand row
   constexpr int KK = BK / 16;                     // MFMA k-steps per stage
   constexpr int WTM = BM / 2, WTN = BN / 2;       // 2 x 2 waves
@@ -176,9 +183,15 @@ ns_gemm_kernel(const GemmArgs p) {
   }
 #pragma unroll
   for (int i = 0; i < IB; ++i) {
-    const int r = RPI * (wave * IB + i) + lane / CPR;
-    const int gr = min(n0 + r, p.N - 1);
-    offB[i] = gr * p.ldb + (((lane % CPR) ^ swz(r)) * 8);
+    if (NNB) {   // k-row r of the stage, 16-byte chunk (lane % LPR) ^ swzB(r) of columns n0..
+      const int r = RPB * (wave * IB + i) + lane / LPR;
+      const int c = (lane % LPR) ^ swzB(r);
+      offB[i] = r * p.ldb + min(n0 + c * 8, p.N - 8);
+    } else {
+      const int r = RPI * (wave * IB + i) + lane / CPR;
+      const int gr = min(n0 + r, p.N - 1);
+      offB[i] = gr * p.ldb + (((lane % CPR) ^ swz(r)) * 8);
+    }
   }
 
   // segment bases and boundaries, read from the kernel arguments once so the
@@ -203,7 +216,7 @@ ns_gemm_kernel(const GemmArgs p) {
     if (kg_ >= kb1) { dA_ = A2; dB_ = B2; kl_ = kg_ - kb1; }                             \
     else if (kg_ >= kb0) { dA_ = A1; dB_ = B1; kl_ = kg_ - kb0; }                        \
     dA_ += kl_ * BK;                                                                     \
-    dB_ += kl_ * BK;                                                                     \
+    dB_ += kl_ * BK * (NNB ? p.ldb : 1);                                                 \
   }
   // DMA instruction j_ (compile-time) of a stage: j_ < IA fill A rows, the
   // rest B rows; db_ is the stage's LDS slot
@@ -225,6 +238,24 @@ ns_gemm_kernel(const GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
   bf16x8_t af[2][FM], bfr[2][FN];
+  typedef short v4i16_t __attribute__((ext_vector_type(4)));
+  v4i16_t bl[2][FN], bh[2][FN];          // NNB: B fragments as two transposing 8-byte reads
+  // NNB per-lane byte offsets of fragment j inside a B stage at k-step 0. A
+  // ds_read_b64_tr_b16 gives lane t of a 16-lane group element b of the lanes
+  // 4q + t/4 (q = 0..3): with lane 4q + a of group G pointing at k-row
+  // 8 (G/2) + q, columns 16 (G%2) + 4a of the fragment, lane t receives rows
+  // 8 (G/2) .. +3 of column 16 (G%2) + t, and a second read four rows lower
+  // completes the eight k values of the MFMA B operand.
+  uint32_t fragB[FN];
+  {
+    const int G = lane >> 4, q = (lane & 15) >> 2, a2 = lane & 3;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = 8 * (G >> 1) + q;
+      const int c = (wn * WTN + 32 * j + 16 * (G & 1) + 4 * a2) >> 3;
+      fragB[j] = r * PB + ((c ^ swzB(r)) << 4) + (a2 & 1) * 8;
+    }
+  }
 
   // Fragment reads of k-step kk_ (16 k) of stage kt_ into register slot sl_.
   // They are issued as inline ds_read_b128 so the compiler does not track
@@ -246,9 +277,15 @@ ns_gemm_kernel(const GemmArgs p) {
       asm volatile("ds_read_b128 %0, %1" : "=v"(af[(sl_)][i]) : "v"(ad_));              \
     }                                                                                    \
     _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                     \
-      const int r_ = wn * WTN + j * 32 + (lane & 31);                                    \
-      const uint32_t ad_ = base_ + BM * ROWB + r_ * ROWB + ((c_ ^ swz(r_)) << 4);        \
-      asm volatile("ds_read_b128 %0, %1" : "=v"(bfr[(sl_)][j]) : "v"(ad_));             \
+      if (NNB) {                                                                         \
+        const uint32_t ad_ = base_ + BM * ROWB + (kk_) * 16 * PB + fragB[j];             \
+        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(bl[(sl_)][j]) : "v"(ad_));       \
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(bh[(sl_)][j]) : "v"(ad_), "i"(4 * PB)); \
+      } else {                                                                           \
+        const int r_ = wn * WTN + j * 32 + (lane & 31);                                  \
+        const uint32_t ad_ = base_ + BM * ROWB + r_ * ROWB + ((c_ ^ swz(r_)) << 4);      \
+        asm volatile("ds_read_b128 %0, %1" : "=v"(bfr[(sl_)][j]) : "v"(ad_));           \
+      }                                                                                  \
     }                                                                                    \
   }
   // wait until at most n_ fragment reads are outstanding
@@ -260,8 +297,8 @@ ns_gemm_kernel(const GemmArgs p) {
   // memory instructions between MFMAs keeps the in-order issue from stalling
   // the matrix core behind a burst of loads. Every flag and count is a
   // compile-time constant at each use, so no branch enters the MFMA stream.
-  constexpr int NSTEP = (FM * FN > FM + FN ? FM * FN : FM + FN) > IA + IB
-                            ? (FM * FN > FM + FN ? FM * FN : FM + FN) : IA + IB;
+  constexpr int NRD = FM + (NNB ? 2 : 1) * FN;    // fragment reads per k-step
+  constexpr int NSTEP = (FM * FN > NRD ? FM * FN : NRD) > IA + IB ? (FM * FN > NRD ? FM * FN : NRD) : IA + IB;
 #define MC_STEP(sl_, rd_, rkt_, rkk_, rsl_, dma_, dsrc_, dkt_, d0_, d1_)                 \
   {                                                                                      \
     const uint32_t rb_ = lds_base + ((rkt_) % NSTAGE) * STAGE;                           \
@@ -273,17 +310,27 @@ ns_gemm_kernel(const GemmArgs p) {
     _Pragma("unroll") for (int m = 0; m < NSTEP; ++m) {                                  \
       if (m < FM * FN)                                                                   \
         acc[m / FN][m % FN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                   \
-            af[(sl_)][m / FN], bfr[(sl_)][m % FN], acc[m / FN][m % FN], 0, 0, 0);        \
+            af[(sl_)][m / FN], NNB ? __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(  \
+            bl[(sl_)][m % FN], bh[(sl_)][m % FN], 0, 1, 2, 3, 4, 5, 6, 7)) : bfr[(sl_)][m % FN], \
+            acc[m / FN][m % FN], 0, 0, 0);                                               \
       __builtin_amdgcn_sched_barrier(0);                                                 \
       if ((rd_) && m < FM) {                                                             \
         const int r_ = wm * WTM + m * 32 + (lane & 31);                                  \
         const uint32_t ad_ = rb_ + r_ * ROWB + ((rc_ ^ swz(r_)) << 4);                   \
         asm volatile("ds_read_b128 %0, %1" : "=v"(af[(rsl_)][m < FM ? m : 0]) : "v"(ad_)); \
-      } else if ((rd_) && m < FM + FN) {                                                 \
+      } else if ((rd_) && !NNB && m < FM + FN) {                                         \
         const int j_ = m - FM;                                                           \
         const int r_ = wn * WTN + j_ * 32 + (lane & 31);                                 \
         const uint32_t ad_ = rb_ + BM * ROWB + r_ * ROWB + ((rc_ ^ swz(r_)) << 4);       \
         asm volatile("ds_read_b128 %0, %1" : "=v"(bfr[(rsl_)][j_ < FN ? j_ : 0]) : "v"(ad_)); \
+      } else if ((rd_) && NNB && m < FM + 2 * FN) {                                      \
+        const int j_ = (m - FM) >> 1;                                                    \
+        const uint32_t ad_ = rb_ + BM * ROWB + (rkk_) * 16 * PB + fragB[j_ < FN ? j_ : 0];  \
+        if (((m - FM) & 1) == 0)                                                         \
+          asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(bl[(rsl_)][j_ < FN ? j_ : 0]) : "v"(ad_)); \
+        else                                                                             \
+          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(bh[(rsl_)][j_ < FN ? j_ : 0]) \
+                       : "v"(ad_), "i"(4 * PB));                                          \
       }                                                                                  \
       if ((dma_) && dn_ > 0 && m % ds_ == 0 && (d0_) + m / ds_ < (d1_))                  \
         MC_DMA((d0_) + m / ds_, dA_, dB_, db_);                                          \
@@ -392,12 +439,11 @@ ns_gemm_kernel(const GemmArgs p) {
   }
 
   const int ld_hi = (EPI & E_HI) ? p.epi.ld_hi : 0, ld_lo = (EPI & E_LO) ? p.epi.ld_lo : 0;
-  const int ld_t = (EPI & E_T) ? p.epi.ld_t : 0, ld_cin = (EPI & E_CIN) ? p.epi.ld_cin : 0;
+  const int ld_cin = (EPI & E_CIN) ? p.epi.ld_cin : 0;
   const uint16_t* cin_hi = (EPI & E_CIN) ? p.epi.cin_hi + (int64_t)b * p.epi.bs_cin : nullptr;
   const uint16_t* cin_lo = (EPI & E_CIN) ? p.epi.cin_lo + (int64_t)b * p.epi.bs_cin : nullptr;
   uint16_t* ohi = (EPI & E_HI) ? p.epi.out_hi + (int64_t)b * p.epi.bs_hi : nullptr;
   uint16_t* olo = (EPI & E_LO) ? p.epi.out_lo + (int64_t)b * p.epi.bs_lo : nullptr;
-  uint16_t* ot = (EPI & E_T) ? p.epi.out_t + (int64_t)b * p.epi.bs_t : nullptr;
   const uint32_t t_cin = (uint32_t)((wj0 + lj) * ld_cin + wi0 + li);
 
   // private staging region of this wave: T[WTN][WTM] bf16, row pitch TP
@@ -486,8 +532,7 @@ ns_gemm_kernel(const GemmArgs p) {
 
   stage(false);
   if (EPI & E_HI) store_direct(ohi, ld_hi);
-  if (EPI & E_T) store_trans(ot, ld_t);
-  else if ((EPI & E_HI) && mirror) store_trans(ohi, ld_hi);
+  if ((EPI & E_HI) && mirror) store_trans(ohi, ld_hi);
   if (EPI & E_LO) {
     MC_WAIT_LGKM_ALL();
     stage(true);
@@ -512,12 +557,12 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs p) {
   }
 }
 
-template <int EPI>
+template <int EPI, int NNB = 0>
 static void launch_epi(GemmTile tile, const GemmArgs& a, int total, hipStream_t s) {
   switch (tile) {
-    case TILE_256: ns_gemm_kernel<256, 256, 2, EPI><<<total, 256, 0, s>>>(a); break;
-    case TILE_128: ns_gemm_kernel<128, 128, 2, EPI><<<total, 256, 0, s>>>(a); break;
-    default:       ns_gemm_kernel<64, 64, 2, EPI><<<total, 256, 0, s>>>(a); break;
+    case TILE_256: ns_gemm_kernel<256, 256, 2, EPI, NNB><<<total, 256, 0, s>>>(a); break;
+    case TILE_128: ns_gemm_kernel<128, 128, 2, EPI, NNB><<<total, 256, 0, s>>>(a); break;
+    default:       ns_gemm_kernel<64, 64, 2, EPI, NNB><<<total, 256, 0, s>>>(a); break;
   }
 }
 
@@ -537,7 +582,7 @@ hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const G
     return ptr && ((ld & 7) || (bs & 7) || ((uintptr_t)ptr & 15));
   };
   if ((a.M & 31) || (a.N & 31) || bad(e.cin_hi, e.ld_cin, e.bs_cin) || bad(e.cin_lo, e.ld_cin, e.bs_cin) ||
-      bad(e.out_hi, e.ld_hi, e.bs_hi) || bad(e.out_lo, e.ld_lo, e.bs_lo) || bad(e.out_t, e.ld_t, e.bs_t))
+      bad(e.out_hi, e.ld_hi, e.bs_hi) || bad(e.out_lo, e.ld_lo, e.bs_lo))
     return hipErrorInvalidValue;
   if (a.splits > 1) {
     launch_epi<E_PART>(tile, a, total, s);
@@ -549,7 +594,7 @@ hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const G
     if (split_pair) launch_epi<E_SYM | E_CIN | E_DIAG | E_HI | E_LO>(tile, a, total, s);
     else launch_epi<E_SYM | E_CIN | E_DIAG | E_HI>(tile, a, total, s);
   } else {
-    launch_epi<E_HI | E_T>(tile, a, total, s);
+    launch_epi<E_HI, 1>(tile, a, total, s);   // apply: B = X stored [k][n]
   }
   return hipGetLastError();
 }

@@ -1,6 +1,7 @@
 """Static check of the NS GEMM's gfx950 assembly (CPU only: hipcc emits it).
 
-The GEMM issues its LDS fragment reads as inline ds_read_b128, which the
+The GEMM issues its LDS fragment reads as inline ds_read_b128 (and, for the
+apply's [k][n] operand, ds_read_b64_tr_b16), which the
 compiler does not track with the LDS counter: it treats the destination
 registers as written when the asm issues. A compiler-inserted copy or any
 other use of such a register before the explicit `s_waitcnt lgkmcnt(0)`
@@ -66,7 +67,7 @@ def check_function(lines):
             if re.search(r"lgkmcnt\(0\)", rest):
                 pending.clear()
             continue
-        if in_asm and op == "ds_read_b128":
+        if in_asm and op in ("ds_read_b128", "ds_read_b64_tr_b16"):
             dst, _, addr = rest.partition(",")
             if regs_of(addr) & pending:
                 bad.append(f"line {n}: address of an inline read is in flight: {line}")
@@ -133,6 +134,8 @@ def test_ns_gemm_inline_reads_are_waited_before_use(gemm_asm):
     problems = {}
     for name, body in ks.items():
         assert any("ds_read_b128" in l for l in body), name
+        if "ILi1EEEv" in name:   # the apply instantiations read B with transposing reads
+            assert any("ds_read_b64_tr_b16" in l for l in body), name
         bad = check_function(body)
         if bad:
             problems[name] = bad[:5]
