@@ -27,7 +27,10 @@
  *   - `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue
  *     work on it and return; nothing is synchronised, no device->host copy is
  *     made, and no device memory is allocated: the caller owns every buffer,
- *     including the workspace. The library keeps no state between calls.
+ *     including the workspace. The only state kept between calls is, per
+ *     device, one auxiliary stream and two events (created on first use,
+ *     kept until the process ends) that muonclip_step forks from and joins
+ *     back into `stream` to run two independent chains at once.
  *   - Every argument is validated before the first launch; on an error status
  *     nothing has been enqueued and nothing is modified. mc_last_error()
  *     returns a text for the last non-OK status of the calling thread.
@@ -122,8 +125,10 @@ typedef struct {
 void mc_default_hparams(mc_hparams *hp);
 
 /* (host) Workspace bytes muonclip_step needs to run every shape group of
- * `mats` with up to 64 matrices in flight at once (larger buffers are not
- * used; smaller ones down to mc_workspace_min_size work in more waves).
+ * `mats` with up to 64 matrices in flight at once, twice over when the step
+ * has more than one shape group, so that two groups can run concurrently
+ * (larger buffers are not used; smaller ones down to mc_workspace_min_size
+ * work in more waves, on one stream).
  * Returns 0 on invalid arguments (see mc_last_error). */
 size_t mc_workspace_size(const mc_matrix *mats /* host, n */, int32_t n, const mc_hparams *hp /* host */);
 /* (host) The smallest workspace muonclip_step accepts for these matrices
@@ -140,7 +145,12 @@ size_t mc_workspace_min_size(const mc_matrix *mats /* host, n */, int32_t n, con
  * Matrices are processed in groups of equal (min, max) shape; within a group
  * the momentum kernel, five Newton-Schulz iterations (bf16 MFMA, fp32
  * accumulation) and the fused update/decay/clip kernel run per wave of
- * matrices that fit the workspace. */
+ * matrices that fit the workspace. Waves are independent chains: with at
+ * least two shape groups and a workspace that holds a wave of each twice
+ * over, the chains are split between `stream` and the library's auxiliary
+ * stream, which is forked after the work already on `stream` and joined back
+ * before the call's work counts as done on `stream`. Results are identical
+ * either way. */
 mc_status muonclip_step(const mc_matrix *mats /* host, n */, int32_t n, const mc_hparams *hp /* host */,
                         const float *s_max, int32_t slots, int32_t heads, float *gamma_out,
                         void *workspace, size_t workspace_bytes, void *stream);

@@ -450,6 +450,52 @@ int largest_wave(const Group& g, int limit, size_t ws_bytes) {
   return best;
 }
 
+// A chain is one wave of one shape group: momentum, Newton-Schulz and update
+// of nb matrices, independent of every other chain.
+struct Chain { int gi, b0, nb; double flops; };
+
+// Waves of at most cap[gi] matrices per group, sized evenly.
+std::vector<Chain> plan_chains(const std::vector<Group>& groups, const std::vector<int>& cap, int ns_steps) {
+  std::vector<Chain> out;
+  for (size_t gi = 0; gi < groups.size(); ++gi) {
+    const Group& g = groups[gi];
+    const int count = (int)g.idx.size();
+    const int waves = (count + cap[gi] - 1) / cap[gi];
+    for (int w = 0, b0 = 0; w < waves; ++w) {
+      const int nb = count / waves + (w < count % waves ? 1 : 0);
+      const double f = (double)ns_steps * 2.0 * (2.0 * g.n * g.m * g.m + (double)g.m * g.m * g.m) * nb;
+      out.push_back({(int)gi, b0, nb, f});
+      b0 += nb;
+    }
+  }
+  return out;
+}
+
+// One auxiliary stream and a fork / join event pair per device, created on
+// first use and kept for the life of the process. Two chains in flight let
+// one chain's bandwidth-bound momentum and update kernels, and its launches
+// that cannot fill the chip, overlap another chain's matrix-core work.
+struct AuxLane { hipStream_t s = nullptr; hipEvent_t fork = nullptr, join = nullptr; };
+std::mutex g_aux_mu;
+std::map<int, AuxLane> g_aux;
+
+// Under g_aux_mu. Returns nullptr when the device's lane cannot be created.
+AuxLane* aux_lane() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  auto it = g_aux.find(dev);
+  if (it != g_aux.end()) return it->second.s ? &it->second : nullptr;
+  AuxLane l;
+  if (hipStreamCreateWithFlags(&l.s, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&l.fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&l.join, hipEventDisableTiming) != hipSuccess) {
+    (void)hipGetLastError();
+    l = AuxLane{};
+  }
+  g_aux[dev] = l;
+  return l.s ? &g_aux[dev] : nullptr;
+}
+
 }  // namespace
 
 // ================================================================ C ABI
@@ -470,10 +516,15 @@ static size_t workspace_for(const mc_matrix* mats, int32_t n, const mc_hparams* 
   if (check_hparams(hp) != MC_OK) return 0;
   if (check_matrices_step(mats, n, 0, 0, false) != MC_OK) return 0;
   size_t best = 0;
-  for (const Group& g : make_groups(mats, n)) {
+  const std::vector<Group> groups = make_groups(mats, n);
+  std::vector<int> cap;
+  for (const Group& g : groups) {
     const int nb = minimal ? 1 : std::min<int>((int)g.idx.size(), kWaveCap);
+    cap.push_back(nb);
     best = std::max(best, plan_wave(g, nb).bytes);
   }
+  // room for two chains in flight when the step has more than one shape group
+  if (!minimal && groups.size() >= 2) best = 2 * align_up(best);
   return best;
 }
 
@@ -508,24 +559,68 @@ mc_status muonclip_step(const mc_matrix* mats, int32_t n, const mc_hparams* hp, 
       return fail(MC_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for one %lldx%lld matrix", workspace_bytes,
                   plan_wave(g, 1).bytes, (long long)g.m, (long long)g.n);
   }
+  // Two lanes (the caller's stream and the library's auxiliary stream, each
+  // with half the workspace) when there are at least two shape groups and
+  // every group fits a half. A single wave is never split to fill a second
+  // lane (on the MHA layer two half-waves measured slower than one wave), and
+  // waves of one group stay on one lane (on the 1155 MoE experts a second
+  // lane measured no faster: the matrix cores are the bound); shape groups of
+  // different sizes (the MLA layer's five matrices) gain 9 %.
+  const size_t half = (workspace_bytes / 2) & ~(kAlign - 1);
+  std::vector<Chain> chains = plan_chains(groups, wave_cap, hp->ns_steps);
+  bool two = groups.size() >= 2 && chains.size() >= 2;
+  std::vector<int> cap2(groups.size());
+  for (size_t gi = 0; gi < groups.size() && two; ++gi) {
+    cap2[gi] = largest_wave(groups[gi], std::min<int>((int)groups[gi].idx.size(), kWaveCap), half);
+    two = cap2[gi] > 0;
+  }
+  if (two) chains = plan_chains(groups, cap2, hp->ns_steps);
+
   hipStream_t s = (hipStream_t)stream;
   if (gamma_out) {
     Prof pr(F_GAMMA, s, 0.0, 0.0);
     hipError_t e = launch_gamma(s_max, gamma_out, slots, heads, hp->tau, hp->clip_global, s);
     if (e != hipSuccess) return fail(MC_ERR_HIP, "gamma launch: %s", hipGetErrorString(e));
   }
-  for (size_t gi = 0; gi < groups.size(); ++gi) {
-    const Group& g = groups[gi];
-    const int count = (int)g.idx.size();
-    for (int b0 = 0; b0 < count;) {
-      int nb = std::min(wave_cap[gi], count - b0);
-      while (nb > 1 && plan_wave(g, nb).bytes > workspace_bytes) --nb;
-      st = run_wave(mats, g, g.idx.data() + b0, nb, *hp, s_max, heads, (char*)workspace, s);
-      if (st) return st;
-      b0 += nb;
+  std::unique_lock<std::mutex> lk(g_aux_mu, std::defer_lock);
+  AuxLane* aux = nullptr;
+  if (two) {
+    lk.lock();
+    aux = aux_lane();
+    if (!aux) {   // no auxiliary stream: everything on `stream`
+      lk.unlock();
+      two = false;
+      chains = plan_chains(groups, wave_cap, hp->ns_steps);
     }
   }
-  return MC_OK;
+  if (!two) {
+    for (const Chain& c : chains) {
+      st = run_wave(mats, groups[c.gi], groups[c.gi].idx.data() + c.b0, c.nb, *hp, s_max, heads, (char*)workspace, s);
+      if (st) return st;
+    }
+    return MC_OK;
+  }
+  // fork: the auxiliary stream starts after everything enqueued on `stream`
+  if (hipEventRecord(aux->fork, s) != hipSuccess || hipStreamWaitEvent(aux->s, aux->fork, 0) != hipSuccess)
+    return fail(MC_ERR_HIP, "stream fork failed");
+  // largest chains first, each to the lane with less work so far
+  std::vector<int> order(chains.size());
+  for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return chains[x].flops > chains[y].flops; });
+  double load[2] = {0.0, 0.0};
+  for (int i : order) {
+    const Chain& c = chains[i];
+    const int lane = load[1] < load[0] ? 1 : 0;
+    load[lane] += c.flops;
+    st = run_wave(mats, groups[c.gi], groups[c.gi].idx.data() + c.b0, c.nb, *hp, s_max, heads,
+                  (char*)workspace + lane * half, lane ? aux->s : s);
+    if (st) break;
+  }
+  // join: `stream` continues only after the auxiliary stream's work (also
+  // after an error, so the caller's stream stays ordered)
+  if (hipEventRecord(aux->join, aux->s) != hipSuccess || hipStreamWaitEvent(s, aux->join, 0) != hipSuccess)
+    return st ? st : fail(MC_ERR_HIP, "stream join failed");
+  return st;
 }
 
 mc_status max_logits_per_head(const void* q, const void* k, const void* k_shared, int32_t dtype, int32_t B, int32_t T,

@@ -118,8 +118,14 @@ def test_workspace_sizes_are_monotone_and_grouped():
     # a tall and a wide matrix of the same shape share one group
     mixed = [fake_matrix(7168, 2048), fake_matrix(2048, 7168)]
     assert mc.workspace_size(mixed) == mc.workspace_size([fake_matrix(2048, 7168)] * 2)
-    # 64 matrices per wave at most
-    assert mc.workspace_size([fake_matrix(256, 512)] * 200) == mc.workspace_size([fake_matrix(256, 512)] * 64)
+    # 64 matrices per wave at most; more than one shape group asks for room
+    # for two waves in flight
+    w64 = mc.workspace_size([fake_matrix(256, 512)] * 64)
+    assert mc.workspace_size([fake_matrix(256, 512)] * 200) == w64
+    assert mc.workspace_size([fake_matrix(256, 512)] * 200, minimal=True) == \
+        mc.workspace_size([fake_matrix(256, 512)], minimal=True)
+    two_groups = [fake_matrix(256, 512), fake_matrix(512, 1024)]
+    assert mc.workspace_size(two_groups) == 2 * mc.workspace_size([fake_matrix(512, 1024)])
 
 
 def test_max_logits_rejects_bad_arguments():

@@ -230,6 +230,35 @@ def test_determinism_and_wave_split():
         assert torch.equal(w0, w1) and torch.equal(m0, m1) and torch.equal(o0, o1)
 
 
+def test_two_lanes_match_one_lane_bit_for_bit():
+    """A step with two chains (two shape groups) runs them on two streams
+    when the workspace holds both; the results are bit-identical to the
+    one-stream run with the smallest workspace, and match the oracle."""
+    cfg = wl.config(1)
+    q, k, ks = wl.draw_attention_inputs(cfg, weights_of(cfg))
+    qd, kd, _ = qk_to_device(q, k, ks, "f32")
+    s_gpu = mc.max_logits_per_head(qd, kd, None, causal=False)
+    gam_orc = oracle.clip_factor(smax_oracle(cfg, q, k, None), cfg.tau)
+    outs = []
+    for ws_mode in ("full", "min", "full"):
+        print("two lanes vs one:", ws_mode, flush=True)
+        states = load_config_states(cfg)               # 256x512 and two 64x64: two groups
+        descs = [s.desc() for s in states]
+        hp = hp_for(cfg, lr=0.02)
+        size = mc.workspace_size(descs, hp, minimal=(ws_mode == "min"))
+        if ws_mode == "full":
+            assert size >= 2 * mc.workspace_size([descs[0]], hp)
+        ws = torch.empty(size, dtype=torch.uint8, device="cuda")
+        mc.muonclip_step(descs, hp, s_max=s_gpu, slots=1, heads=4, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append([(s.w.cpu().clone(), s.m.cpu().clone(), s.o.cpu().clone()) for s in states])
+        for s in states:
+            check_matrix(s, hp, gam_orc)
+    for run in outs[1:]:
+        for (w0, m0, o0), (w1, m1, o1) in zip(outs[0], run):
+            assert torch.equal(w0, w1) and torch.equal(m0, m1) and torch.equal(o0, o1)
+
+
 # ----------------------------------------------------------------- QK-Clip alone
 
 def test_qk_clip_apply_essay_invariants():
