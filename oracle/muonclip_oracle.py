@@ -45,6 +45,10 @@ Readings where the pages are silent or garbled (each is listed in the design doc):
     look-ahead G_t + mu M_t.
   * Global clip ([K2-cn] 2.1, the naive variant): gamma from the largest
     S_max^h of the layer, NaN heads ignored by that max.
+  * The attention forward that S_max is observed in ([K2-report] "Taming Muon
+    with QK-Clip", [K2-cn] 2.1) is the plain softmax attention the pages
+    write down, with the same logits (and MLA shared rotary key) as S_max and
+    the causal mask j <= i; no dropout, no bias, no soft-cap.
   * AdamW for the parameters Muon does not cover ([Muon-blog] "Limitation":
     only 2-D parameters; the rest still need AdamW; [Moonlight] "Scaling up
     Muon": Muon and AdamW share the learning rate and weight decay). The pages
@@ -299,6 +303,49 @@ def muonclip_step_matrix(w, g, m, *, lr, mu, weight_decay, rms_scale=0.2,
     else:                                   # "f64": unrounded, for pins
         w_out = w_new
     return w_out, m_new.astype(np.float32), o
+
+
+# ---------------------------------------------------------------------------
+# the attention forward whose logits S_max is taken from
+# ---------------------------------------------------------------------------
+
+def attention_forward(q, k, k_shared, v, causal: bool, scale: float, rows=None):
+    """Attention output of one layer with its per-row log-sum-exp
+    ([K2-report] "Taming Muon with QK-Clip": O^h = softmax(Q^h K^h^T / sqrt(d)) V^h;
+    [K2-cn] 2.1, the same equation).
+
+    q [B,T,H,d_q], k [B,T,H,d_k], k_shared [B,T,d_s] or None, v [B,T,H,d_v].
+    The logit of (query i, key j, head h) in sample b is the one max_logits
+    uses, times scale; keys j > i are left out when causal. `rows` (optional
+    list of query indices) restricts the output to those queries, which the
+    definition computes independently of each other.
+    Returns fp64 (o [B,R,H,d_v], lse [B,H,R]) with R = T or len(rows); lse is
+    the natural log of the sum of exp(scaled logit) over the row's keys. A row
+    with no key (not reachable: the diagonal is always kept) gives o = NaN.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, T, H, _ = q.shape
+    dv = v.shape[3]
+    ridx = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = len(ridx)
+    o = np.zeros((B, R, H, dv))
+    lse = np.zeros((B, H, R))
+    for b in range(B):
+        for h in range(H):
+            kk = k[b, :, h, :]
+            if k_shared is not None:
+                kk = np.concatenate([kk, np.asarray(k_shared[b], np.float64)], axis=1)
+            logits = scale * (q[b, ridx, h, :] @ kk.T)              # [R, T]
+            if causal:
+                logits = np.where(np.arange(T)[None, :] <= ridx[:, None], logits, -np.inf)
+            m = logits.max(axis=1, keepdims=True)
+            e = np.exp(logits - m)
+            ssum = e.sum(axis=1, keepdims=True)
+            o[b, :, h, :] = (e / ssum) @ v[b, :, h, :]
+            lse[b, h, :] = (m + np.log(ssum))[:, 0]
+    return o, lse
 
 
 # ---------------------------------------------------------------------------

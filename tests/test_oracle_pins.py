@@ -435,3 +435,79 @@ def test_adamw_decay_only_and_rounding():
     import torch
     want = torch.tensor(p * (1.0 - 0.001), dtype=torch.float64).to(torch.bfloat16).double().numpy()
     assert np.array_equal(p1, want)
+
+
+# ---------------------------------------------------------------- attention forward
+
+def _tiny_qkv(rng, B, T, H, dk, ds, dv):
+    q, k, ks = _tiny_qk(rng, B, T, H, dk, ds)
+    v = rng.standard_normal((B, T, H, dv))
+    return q, k, ks, v
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("ds", [0, 3])
+def test_attention_matches_torch_sdpa(causal, ds):
+    # a library route: torch's scaled_dot_product_attention in fp64 on the
+    # CPU, fed [B,H,T,d] with the shared key appended to every head's key
+    import torch
+    rng = np.random.default_rng(40 + ds)
+    q, k, ks, v = _tiny_qkv(rng, 2, 11, 3, 4, ds, 5)
+    scale = 0.37
+    o, lse = oracle.attention_forward(q, k, ks, v, causal, scale)
+    kk = k if ks is None else np.concatenate([k, np.repeat(ks[:, :, None, :], 3, axis=2)], axis=3)
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(kk).permute(0, 2, 1, 3)
+    vt = torch.from_numpy(v).permute(0, 2, 1, 3)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=causal, scale=scale)
+    assert np.allclose(o, ref.permute(0, 2, 1, 3).numpy(), rtol=1e-12, atol=1e-12)
+    # lse through scipy's logsumexp of torch's logits
+    from scipy.special import logsumexp
+    logits = (torch.einsum("bhid,bhjd->bhij", qt, kt) * scale).numpy()
+    if causal:
+        logits = np.where(np.tril(np.ones((11, 11), bool)), logits, -np.inf)
+    assert np.allclose(lse, logsumexp(logits, axis=3), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_identical_keys_average_the_values(causal):
+    # every key equal -> every allowed key gets the same weight: o_i is the
+    # mean of v over j <= i (causal) or over all j, and lse_i = scale q_i.k + ln(count)
+    rng = np.random.default_rng(7)
+    B, T, H, d = 1, 9, 2, 4
+    q = rng.standard_normal((B, T, H, d))
+    k = np.broadcast_to(rng.standard_normal((1, 1, H, d)), (B, T, H, d)).copy()
+    v = rng.standard_normal((B, T, H, 3))
+    o, lse = oracle.attention_forward(q, k, None, v, causal, 0.5)
+    for i in range(T):
+        n = i + 1 if causal else T
+        assert np.allclose(o[0, i], v[0, :n].mean(axis=0), rtol=1e-13, atol=1e-13)
+        for h in range(H):
+            assert math.isclose(lse[0, h, i], 0.5 * float(q[0, i, h] @ k[0, 0, h]) + math.log(n), rel_tol=1e-13)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(8)
+    q, k, ks, v = _tiny_qkv(rng, 2, 6, 2, 4, 2, 3)
+    # causal row 0 sees key 0 only: o = v_0 and lse = its logit
+    o, lse = oracle.attention_forward(q, k, ks, v, True, 0.25)
+    assert np.array_equal(o[:, 0], v[:, 0])
+    for b in range(2):
+        for h in range(2):
+            s = float(q[b, 0, h, :4] @ k[b, 0, h] + q[b, 0, h, 4:] @ ks[b, 0])
+            assert math.isclose(lse[b, h, 0], 0.25 * s, rel_tol=1e-14)
+    # constant values come back unchanged (the weights sum to one)
+    vc = np.full_like(v, 2.5)
+    oc, _ = oracle.attention_forward(q, k, ks, vc, False, 0.25)
+    assert np.allclose(oc, 2.5, rtol=1e-14)
+    # one dominant logit selects its value row
+    qd = np.zeros((1, 4, 1, 2)); kd = np.zeros((1, 4, 1, 2)); vd = rng.standard_normal((1, 4, 1, 3))
+    qd[0, :, 0, 0] = 1.0
+    kd[0, 2, 0, 0] = 200.0
+    od, _ = oracle.attention_forward(qd, kd, None, vd, False, 1.0)
+    assert np.allclose(od[0, :, 0], vd[0, 2, 0], rtol=1e-12, atol=1e-12)
+    # selected rows equal the same rows of the full output
+    orow, lrow = oracle.attention_forward(q, k, ks, v, True, 0.25, rows=[5, 1])
+    assert np.array_equal(orow[:, 0], o[:, 5]) and np.array_equal(orow[:, 1], o[:, 1])
+    assert np.array_equal(lrow[:, :, 0], lse[:, :, 5])
+

@@ -20,7 +20,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-KIND_W, KIND_G, KIND_M, KIND_X, KIND_S = 0, 1, 2, 3, 4
+KIND_W, KIND_G, KIND_M, KIND_X, KIND_S, KIND_V = 0, 1, 2, 3, 4, 5
 
 # Hyper-parameters of the step, as the configurations use them.
 DEFAULT_HPARAMS = dict(lr=2e-4, mu=0.95, weight_decay=0.1, rms_scale=0.2,
@@ -86,6 +86,11 @@ class AttnSpec:
     d_q: int
     d_k: int
     d_shared: int
+
+    @property
+    def d_v(self) -> int:
+        """Value width per head: the head width for MHA, 128 for MLA."""
+        return 128 if self.kind == "mla" else self.d_q
 
 
 @dataclass
@@ -279,6 +284,38 @@ def draw_attention_inputs(cfg: Config, weights: dict):
     kv_b = weights["kv_b"].reshape(H, 256, 512)[:, :128, :].reshape(H * 128, 512)
     k_c = quantize_bf16(_matmul_f32(c_kv, kv_b.T)).reshape(a.B, a.T, H, 128)
     return q, k_c, k_r
+
+
+def draw_attention_values(cfg: Config, weights: dict) -> np.ndarray:
+    """V [B,T,H,d_v] of the same forward (float32 on the bf16 grid for bf16
+    configurations). MHA: V = x W_v^T from the same seeded x. MLA: v =
+    c_KV kv_b[v rows]^T, the v rows being 128..255 of every head's 256 rows of
+    kv_b. The tiny fp32 configuration has no W_v: V ~ N(0, 1) is drawn."""
+    a = cfg.attn
+    if a.dtype == "f32":
+        v = normal(cfg.seed, tensor_id(len(cfg.matrices), KIND_V), (a.B, a.T, a.H, a.d_v), 1.0)
+        return quantize_f32(v)
+    xid = tensor_id(len(cfg.matrices), KIND_X)
+    x = quantize_bf16(normal(cfg.seed, xid, (a.B * a.T, a.d_model), 1.0))
+    if a.kind == "mha":
+        v = quantize_bf16(_matmul_f32(x, weights["wv"].T))
+        return v.reshape(a.B, a.T, a.H, a.d_v)
+    H = a.H
+    c_kv = quantize_bf16(_matmul_f32(x, weights["kv_a"][:512].T))
+    kv_b = weights["kv_b"].reshape(H, 256, 512)[:, 128:, :].reshape(H * 128, 512)
+    return quantize_bf16(_matmul_f32(c_kv, kv_b.T)).reshape(a.B, a.T, H, 128)
+
+
+def draw_attention_case(seed: int, B: int, T: int, H: int, d_k: int, d_s: int, d_v: int,
+                        q_std: float = 1.0, k_std: float = 1.0, v_std: float = 1.0):
+    """A free-standing attention input on the bf16 grid (float32 arrays):
+    q [B,T,H,d_k+d_s], k [B,T,H,d_k], k_shared [B,T,d_s] or None, v [B,T,H,d_v],
+    each from its own stream of `seed`."""
+    q = quantize_bf16(normal(seed, 1, (B, T, H, d_k + d_s), q_std))
+    k = quantize_bf16(normal(seed, 2, (B, T, H, d_k), k_std))
+    ks = quantize_bf16(normal(seed, 3, (B, T, d_s), k_std)) if d_s else None
+    v = quantize_bf16(normal(seed, 4, (B, T, H, d_v), v_std))
+    return q, k, ks, v
 
 
 def draw_smax(cfg: Config, n_over: int = 4) -> np.ndarray:
