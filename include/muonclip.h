@@ -175,6 +175,37 @@ mc_status max_logits_per_head(const void *q, const void *k, const void *k_shared
                               const int64_t *ks_stride /* host [2], or NULL */,
                               int32_t causal, float scale, float *s_max_out, void *stream);
 
+/* Softmax attention forward of one layer with S_max observed on the way
+ * (Kimi K2 report, "Taming Muon with QK-Clip": O^h = softmax(Q^h K^h^T /
+ * sqrt(d)) V^h, and S_max^h is the largest softmax input of that same
+ * forward; K2 report 2.1 in translation, the same equations). For every
+ * sample b, head h and query i:
+ *   o[b,i,h,:] = sum_j w_j v[b,j,h,:],  w = softmax_j(scale * logit(b,i,j,h))
+ * over keys j < T (j <= i if causal), logit as in max_logits_per_head (q, k
+ * and k_shared have the same shapes and strides as there). bf16 in and out,
+ * fp32 arithmetic (probabilities rounded to bf16 for the value product).
+ *   v: [B,T,H,d_v] with v_stride {b, t, h}; o: [B,T,H,d_v] with o_stride,
+ *      written; it must not overlap any input
+ *   lse: optional fp32 [B][H][T] (contiguous), the natural log of the row's
+ *      sum of exp(scale * logit); NULL = not written
+ *   s_max_out: optional fp32 [H], overwritten with the value
+ *      max_logits_per_head gives for the same q, k, k_shared, taken from the
+ *      softmax's running row maxima (no second Q K^T pass); -inf for every
+ *      head when B or T is 0; NULL = not computed
+ * Covers (d_k, d_shared, d_v) in {(128, 0, 128), (128, 64, 128)} with d_q =
+ * d_k + d_shared (MHA d = 128; MLA [q^C | q^R] against [k^C_h | k^R]).
+ * q, k, k_shared, v, o 16-byte aligned, every stride a multiple of 8 elements
+ * and t strides of k, k_shared, v below 2^23 elements; otherwise MC_ERR_SHAPE
+ * or MC_ERR_ALIGN before anything is enqueued. scale finite and > 0. One
+ * launch (plus two tiny ones for s_max_out) on `stream`; allocates nothing. */
+mc_status attention_forward(const void *q, const void *k, const void *k_shared, const void *v, void *o,
+                            float *lse, float *s_max_out,
+                            int32_t B, int32_t T, int32_t H, int32_t d_q, int32_t d_k, int32_t d_shared,
+                            int32_t d_v, const int64_t *q_stride /* host [3] */,
+                            const int64_t *k_stride /* host [3] */, const int64_t *ks_stride /* host [2], or NULL */,
+                            const int64_t *v_stride /* host [3] */, const int64_t *o_stride /* host [3] */,
+                            int32_t causal, float scale, void *stream);
+
 /* QK-Clip alone on existing weights (the clip part of muonclip_step without
  * the Muon update): for every matrix with clip_slot >= 0, rows in its
  * segments are scaled by gamma_h ** expo, gamma from s_max[slots][heads] and

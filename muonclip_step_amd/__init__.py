@@ -22,7 +22,8 @@ MC_F32, MC_BF16 = 0, 1
 
 EXPORTS = ("mc_default_hparams", "mc_workspace_size", "mc_workspace_min_size", "muonclip_step",
            "max_logits_per_head", "qk_clip_apply", "mc_last_error", "mc_version",
-           "mc_profile_enable", "mc_profile_read", "mc_default_adamw_hparams", "adamw_step")
+           "mc_profile_enable", "mc_profile_read", "mc_default_adamw_hparams", "adamw_step",
+           "attention_forward")
 
 
 class MuonClipError(RuntimeError):
@@ -103,6 +104,8 @@ def load():
     lib.mc_default_adamw_hparams.restype = None
     lib.adamw_step.argtypes = [POINTER(Vector), c_int32, POINTER(AdamWHParams), c_void_p]
     lib.adamw_step.restype = c_int32
+    lib.attention_forward.argtypes = [c_void_p] * 7 + [c_int32] * 7 + [c_void_p] * 5 + [c_int32, c_float, c_void_p]
+    lib.attention_forward.restype = c_int32
     _lib = lib
     return lib
 
@@ -212,6 +215,34 @@ def max_logits_per_head(q, k, k_shared=None, causal: bool = True, scale: float |
             raise ValueError("last dimension must be contiguous")
     _check(load().max_logits_per_head(_ptr(q), _ptr(k), _ptr(k_shared), _dtype_code(q), B, T, H, d_q, d_k, d_s,
                                       qs, ks, kss, int(bool(causal)), scale, _ptr(out), _stream(stream)))
+    return out
+
+
+def attention_forward(q, k, k_shared, v, causal: bool = True, scale: float | None = None, out=None, lse=None,
+                      s_max=None, stream=None):
+    """Softmax attention forward (bf16) with the per-head max logit taken on
+    the way: q [B,T,H,d_q], k [B,T,H,d_k], k_shared [B,T,d_s] or None,
+    v [B,T,H,d_v]. Returns out [B,T,H,d_v] (allocated when None). lse
+    (fp32 [B,H,T], contiguous) and s_max (fp32 [H]) are filled when given."""
+    import torch
+    B, T, H, d_q = q.shape
+    d_k = k.shape[3]
+    d_s = k_shared.shape[2] if k_shared is not None else 0
+    d_v = v.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_q)
+    if out is None:
+        out = torch.empty(B, T, H, d_v, dtype=v.dtype, device=v.device)
+    for t in (q, k, v, out) + ((k_shared,) if k_shared is not None else ()):
+        if t.stride(-1) != 1:
+            raise ValueError("last dimension must be contiguous")
+    if lse is not None and not lse.is_contiguous():
+        raise ValueError("lse must be contiguous [B, H, T]")
+    st3 = lambda t: (c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+    kss = (c_int64 * 2)(k_shared.stride(0), k_shared.stride(1)) if k_shared is not None else None
+    _check(load().attention_forward(_ptr(q), _ptr(k), _ptr(k_shared), _ptr(v), _ptr(out), _ptr(lse), _ptr(s_max),
+                                    B, T, H, d_q, d_k, d_s, d_v, st3(q), st3(k), kss, st3(v), st3(out),
+                                    int(bool(causal)), scale, _stream(stream)))
     return out
 
 

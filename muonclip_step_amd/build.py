@@ -34,9 +34,17 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Per-source additions. The attention kernel keeps its logits in VGPRs for
+# the softmax, so its MFMAs write VGPRs (accumulators the register allocator
+# cannot fit there go to AGPRs as spill slots).
+EXTRA = {
+    "attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *FLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

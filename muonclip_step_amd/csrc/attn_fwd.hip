@@ -1,0 +1,380 @@
+// Softmax attention forward with the per-head max logit observed on the way.
+//
+// O^h = softmax(scale Q^h K^h^T) V^h per (sample, head) (K2 report, "Taming
+// Muon with QK-Clip"; K2 report 2.1 in translation): the max logit S_max^h
+// that QK-Clip needs is the largest softmax input of this same forward, so
+// the kernel takes it from the running row maxima the online softmax keeps
+// anyway, instead of a second Q K^T pass. Causal masking keeps j <= i. MLA
+// keys are [k^C_h | k^R] with the rotary key shared by every head; the value
+// width is 128.
+//
+// Layout of the work. A 256-thread block owns 256 query rows of one
+// (sample, head); each wave keeps 64 of them in registers as two MFMA
+// B-fragments for the whole kernel and walks the key axis in tiles of 64
+// keys, which pass through a double-buffered LDS ring (K rows XOR-swizzled
+// for 16-byte fragment reads, V rows swizzled for transposing reads). Both
+// products run transposed, with v_mfma_f32_32x32x16_bf16:
+//   S^T = K Q^T   (A = K from LDS, B = Q from registers)
+//   O^T += V^T P^T (A = V^T via ds_read_b64_tr_b16, B = P^T from registers)
+// so that every lane holds one query's logits, probabilities and output
+// column: the row max and row sum stay inside a lane pair (lanes l, l^32),
+// the rescale is a per-lane scalar, and P^T is the S^T accumulator itself
+// converted to bf16 (the MFMA's k order is permuted to match it on both
+// operands). The running max used for the exponentials moves only when a
+// tile's max exceeds it by more than 8 binary orders, so the output
+// accumulators are rescaled rarely; the exact running max is kept beside it
+// for S_max. Blocks are issued heaviest causal row first; the q-tiles of one
+// (sample, head) are HB apart in launch order, which keeps them on one XCD
+// (and its L2) whenever HB is a multiple of 8.
+#include <math.h>
+
+#include <type_traits>
+
+#include "mc_internal.h"
+
+namespace mc {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt on the vector-memory counter alone (the direct-to-LDS loads are
+// the only vector loads in flight inside the loop)
+#define FA_WAIT_DMA() __builtin_amdgcn_s_waitcnt(0x70 | 0xF00)
+
+constexpr int kBQ = 256, kBKV = 64, kDV = 128;
+
+// V rows (256 bytes): a transposing read's 16-lane group covers four
+// consecutive rows at the same columns; chunk ^ 4 (r & 3) puts them on
+// distinct banks.
+__device__ __forceinline__ int v_swz(int r) { return 4 * (r & 3); }
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+
+template <int DK, int DS, bool SMAX>
+__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attn_fwd_kernel(const AttnArgs a) {
+  static_assert(DK == 128 && (DS == 0 || DS == 64), "head widths");
+  constexpr int D = DK + DS, KS = D / 16;
+  // one LDS stage: K content rows [64][256 B], rotary rows [64][128 B], V rows [64][256 B]
+  constexpr int KC_BYTES = kBKV * 256, KR_BYTES = kBKV * DS * 2, VT_BYTES = kBKV * kDV * 2;
+  constexpr int STAGE = KC_BYTES + KR_BYTES + VT_BYTES;
+  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
+  __shared__ float red[4];
+
+  const int HB = a.H * a.B;
+  const int nqt = (a.T + kBQ - 1) / kBQ;
+  const int hb = blockIdx.x % HB;
+  const int qt = nqt - 1 - (int)(blockIdx.x / HB);   // heaviest causal rows first
+  const int h = hb % a.H, b = hb / a.H;
+  const int q0 = qt * kBQ;
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int wq0 = q0 + wave * 64;
+
+  const uint16_t* Q = (const uint16_t*)a.q + (int64_t)b * a.qs_b + (int64_t)h * a.qs_h;
+  const char* K = (const char*)((const uint16_t*)a.k + (int64_t)b * a.ks_b + (int64_t)h * a.ks_h);
+  const char* KR = DS > 0 ? (const char*)((const uint16_t*)a.ks + (int64_t)b * a.kss_b) : nullptr;
+  const char* V = (const char*)((const uint16_t*)a.v + (int64_t)b * a.vs_b + (int64_t)h * a.vs_h);
+
+  // the wave's 64 query rows as B fragments: lane l holds query l % 32 of
+  // fragment f, dimensions 16 s + 8 (l / 32) .. +7. Rows past T re-read row
+  // T - 1: they see exactly row T - 1's keys, so they change no maximum, and
+  // their outputs are not stored.
+  bf16x8_t qf[2][KS];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int row = wq0 + 32 * f + (lane & 31);
+    const int rr = row < a.T ? row : a.T - 1;
+    const uint16_t* base = Q + (int64_t)rr * a.qs_t + 8 * hl;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[f][s] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(base + 16 * s));
+  }
+
+  const int kend = a.causal ? min(a.T, q0 + kBQ) : a.T;
+  const int nkv = (kend + kBKV - 1) / kBKV;
+  const float c2 = a.scale * 1.4426950408889634f;   // scale * log2(e)
+  const float thr = 8.0f / c2;                      // lazy-rescale slack in raw logit units
+
+  f32x16_t oacc[2][4];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) oacc[f][n] = f32x16_t{};
+  float m_use[2] = {-INFINITY, -INFINITY};   // max the exponentials are taken against
+  float m_all[2] = {-INFINITY, -INFINITY};   // exact running max (S_max)
+  float lsum[2] = {0.0f, 0.0f};              // this lane's half of the row sum
+
+  // Tiles reach LDS through direct-to-LDS loads (global_load_lds_dwordx4:
+  // 64 lanes fill 1 KB of consecutive LDS, so each swizzle is applied on the
+  // source side: the lane filling physical chunk pc of row r fetches logical
+  // chunk pc ^ swz(r)). Per wave: 4 instructions of K content rows, 2 of
+  // rotary rows (MLA), 4 of V rows; lane offsets are relative to the tile's
+  // first key, whose address is the only per-tile arithmetic. Keys past T
+  // (only in the tile holding key T - 1) re-read key T - 1 and are masked.
+  constexpr int IC = 4, IR = DS > 0 ? 2 : 0, IV = 4;
+  int crow[IC], coff[IC], vrow[IV], voffs[IV];
+  int rrow[IR > 0 ? IR : 1], roff[IR > 0 ? IR : 1];
+#pragma unroll
+  for (int i = 0; i < IC; ++i) {
+    const int idx = 64 * (IC * wave + i) + lane, r = idx >> 4, c = (idx & 15) ^ (r & 15);
+    crow[i] = r;
+    coff[i] = r * (int)a.ks_t * 2 + c * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < IR; ++i) {
+    const int idx = 64 * (IR * wave + i) + lane, r = idx >> 3, c = (idx & 7) ^ ((r >> 1) & 7);
+    rrow[i] = r;
+    roff[i] = r * (int)a.kss_t * 2 + c * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < IV; ++i) {
+    const int idx = 64 * (IV * wave + i) + lane, r = idx >> 4, c = (idx & 15) ^ v_swz(r);
+    vrow[i] = r;
+    voffs[i] = r * (int)a.vs_t * 2 + c * 16;
+  }
+  auto dma = [&](const int it, const int buf) {
+    const int kv0 = it * kBKV;
+    char* st = lds + buf * STAGE;
+    const char* kb = K + (int64_t)kv0 * a.ks_t * 2;
+    const char* rb = DS > 0 ? KR + (int64_t)kv0 * a.kss_t * 2 : nullptr;
+    const char* vb = V + (int64_t)kv0 * a.vs_t * 2;
+    if (kv0 + kBKV <= a.T) {
+#pragma unroll
+      for (int i = 0; i < IC; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(kb + coff[i]), (lds_void_t*)(st + 1024 * (IC * wave + i)), 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < IR; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(rb + roff[i]),
+                                         (lds_void_t*)(st + KC_BYTES + 1024 * (IR * wave + i)), 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < IV; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(vb + voffs[i]),
+                                         (lds_void_t*)(st + KC_BYTES + KR_BYTES + 1024 * (IV * wave + i)), 16, 0, 0);
+    } else {
+      const int last = a.T - 1 - kv0;   // rows past it re-read this one
+#pragma unroll
+      for (int i = 0; i < IC; ++i) {
+        const int d = (min(crow[i], last) - crow[i]) * (int)a.ks_t * 2;
+        __builtin_amdgcn_global_load_lds((const void*)(kb + coff[i] + d), (lds_void_t*)(st + 1024 * (IC * wave + i)), 16, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < IR; ++i) {
+        const int d = (min(rrow[i], last) - rrow[i]) * (int)a.kss_t * 2;
+        __builtin_amdgcn_global_load_lds((const void*)(rb + roff[i] + d),
+                                         (lds_void_t*)(st + KC_BYTES + 1024 * (IR * wave + i)), 16, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < IV; ++i) {
+        const int d = (min(vrow[i], last) - vrow[i]) * (int)a.vs_t * 2;
+        __builtin_amdgcn_global_load_lds((const void*)(vb + voffs[i] + d),
+                                         (lds_void_t*)(st + KC_BYTES + KR_BYTES + 1024 * (IV * wave + i)), 16, 0, 0);
+      }
+    }
+  };
+
+  // per-lane byte offsets of the transposing V reads inside a V tile: lane
+  // 4 q + a of 16-lane group G points at key row 4 (G / 2) + q, columns
+  // 16 (G % 2) + 4 a of a 32-column block; the read returns to lane t of the
+  // group rows 4 (G / 2) .. +3 of column 16 (G % 2) + t, and a second read 8
+  // rows lower gives the other four keys of the MFMA's k order.
+  uint32_t voff[4];
+  {
+    const int G = lane >> 4, qq = (lane & 15) >> 2, a2 = lane & 3;
+    const int r = 4 * (G >> 1) + qq;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int c = (32 * n + 16 * (G & 1) + 4 * a2) >> 3;
+      voff[n] = r * (kDV * 2) + ((c ^ v_swz(r)) << 4) + (a2 & 1) * 8;
+    }
+  }
+
+  // One key tile of 64, in two halves of 32 keys (g): S^T = K Q^T, online
+  // softmax, O^T += V^T P^T. MASK applies the causal and ragged-end masks
+  // (only the wave's diagonal tile and the tile holding key T - 1 need it).
+  auto tile = [&](const int kv0, const char* kt, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const char* vt = kt + KC_BYTES + KR_BYTES;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      // sacc[f] register e of lane l: key kv0 + 32 g + 8 (e / 4) + 4 (l / 32)
+      // + e % 4, query wq0 + 32 f + l % 32
+      f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
+      const int r = 32 * g + (lane & 31);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        // content dimensions: 256-byte rows, chunk ^ (r & 15); rotary: 128-byte
+        // rows, chunk ^ ((r >> 1) & 7) (two rows per bank cycle)
+        const int c = 2 * (s < 8 ? s : s - 8) + hl;
+        const char* ka = s < 8 ? kt + r * 256 + ((c ^ (r & 15)) << 4)
+                               : kt + KC_BYTES + r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)ka);
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+          sacc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[f][s], sacc[f], 0, 0, 0);
+      }
+      if (MASK) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const int i = wq0 + 32 * f + (lane & 31);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int j = kv0 + 32 * g + 8 * (e >> 2) + 4 * hl + (e & 3);
+            if (j >= a.T || (a.causal && j > i)) sacc[f][e] = -INFINITY;
+          }
+        }
+      }
+      // row max over the 32 keys (the lane pair l, l ^ 32 holds one query)
+      float bm[2];
+      bool grow = false;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        float x = sacc[f][0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) x = fmaxf(x, sacc[f][e]);
+        x = fmaxf(x, __shfl_xor(x, 32));
+        bm[f] = x;
+        if (SMAX) m_all[f] = fmaxf(m_all[f], x);
+        grow = grow || (x > m_use[f] + thr);
+      }
+      if (__any(grow)) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const float mn = fmaxf(m_use[f], bm[f]);
+          const float alpha = __builtin_amdgcn_exp2f((m_use[f] - mn) * c2);
+          m_use[f] = mn;
+          lsum[f] *= alpha;
+#pragma unroll
+          for (int n = 0; n < 4; ++n) oacc[f][n] *= alpha;
+        }
+      }
+      // P^T = exp2(c2 (S^T - m)) in bf16; k-step p takes registers 8 p .. 8 p + 7
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        bf16x8_t pb[2];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const float nm = -m_use[f] * c2;
+          float ls = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[f][8 * p + e], c2, nm));
+            ls += pv;
+            pb[f][e] = (__bf16)pv;
+          }
+          lsum[f] += ls;
+        }
+        const char* vs = vt + (32 * g + 16 * p) * (kDV * 2);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vs + voff[n]));
+          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vs + voff[n] + 8 * (kDV * 2)));
+          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+            oacc[f][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[f], oacc[f][n], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // Tiles this wave computes: all of them without a causal mask; with one,
+  // those starting at or before its last query. The leading ones that need
+  // no mask (wholly below the diagonal and inside T) run without it. Every
+  // wave takes part in every tile's loads and barrier.
+  const int n_w = wq0 >= a.T ? 0 : (a.causal ? min(nkv, (wq0 >> 6) + 1) : nkv);
+  const int n_full = min(n_w, a.causal ? min(a.T >> 6, wq0 >> 6) : (a.T >> 6));
+  if (nkv > 0) {
+    dma(0, 0);
+    FA_WAIT_DMA();
+    __syncthreads();
+  }
+  int it = 0;
+  for (; it < n_full; ++it) {
+    if (it + 1 < nkv) dma(it + 1, (it + 1) & 1);
+    tile(it * kBKV, lds + (it & 1) * STAGE, std::false_type{});
+    FA_WAIT_DMA();   // this wave's loads of the next tile have landed
+    __syncthreads();
+  }
+  for (; it < n_w; ++it) {
+    if (it + 1 < nkv) dma(it + 1, (it + 1) & 1);
+    tile(it * kBKV, lds + (it & 1) * STAGE, std::true_type{});
+    FA_WAIT_DMA();
+    __syncthreads();
+  }
+  for (; it < nkv; ++it) {
+    if (it + 1 < nkv) dma(it + 1, (it + 1) & 1);
+    FA_WAIT_DMA();
+    __syncthreads();
+  }
+
+  // normalise and store: oacc[f][n] register e of lane l is column
+  // 32 n + 8 (e / 4) + 4 (l / 32) + e % 4 of query wq0 + 32 f + l % 32
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const float lt = lsum[f] + __shfl_xor(lsum[f], 32);
+    const int i = wq0 + 32 * f + (lane & 31);
+    if (i < a.T) {
+      const float inv = 1.0f / lt;
+      uint16_t* orow = (uint16_t*)a.o + (int64_t)b * a.os_b + (int64_t)i * a.os_t + (int64_t)h * a.os_h;
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          uint2 w;
+          w.x = f32x2_to_bf16x2(oacc[f][n][4 * t] * inv, oacc[f][n][4 * t + 1] * inv);
+          w.y = f32x2_to_bf16x2(oacc[f][n][4 * t + 2] * inv, oacc[f][n][4 * t + 3] * inv);
+          *(uint2*)(orow + 32 * n + 8 * t + 4 * hl) = w;
+        }
+      if (a.lse && hl == 0) a.lse[((int64_t)b * a.H + h) * a.T + i] = a.scale * m_use[f] + logf(lt);
+    }
+  }
+  if (SMAX) {
+    float mx = wave_max(fmaxf(m_all[0], m_all[1]));
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    if (tid == 0) {
+      mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      atomicMax(a.smax_enc + h, order_enc(mx));
+    }
+  }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+bool attention_supported(const AttnArgs& a) {
+  const bool shape = a.d_k == 128 && (a.d_s == 0 || a.d_s == 64) && a.d_v == kDV;
+  if (!shape) return false;
+  if (!aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v) || !aligned16(a.o) || (a.d_s && !aligned16(a.ks)))
+    return false;
+  if ((a.qs_b | a.qs_t | a.qs_h | a.ks_b | a.ks_t | a.ks_h | a.vs_b | a.vs_t | a.vs_h | a.os_b | a.os_t | a.os_h) & 7)
+    return false;
+  if (a.d_s && ((a.kss_b | a.kss_t) & 7)) return false;
+  return true;
+}
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  if (a.B <= 0 || a.T <= 0 || a.H <= 0) return hipSuccess;
+  const int grid = (a.T + kBQ - 1) / kBQ * a.H * a.B;
+  const bool sm = a.smax_enc != nullptr;
+  if (a.d_s == 64) {
+    if (sm) attn_fwd_kernel<128, 64, true><<<grid, 256, 0, s>>>(a);
+    else attn_fwd_kernel<128, 64, false><<<grid, 256, 0, s>>>(a);
+  } else {
+    if (sm) attn_fwd_kernel<128, 0, true><<<grid, 256, 0, s>>>(a);
+    else attn_fwd_kernel<128, 0, false><<<grid, 256, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mc

@@ -57,11 +57,11 @@ constexpr int kSplitThreshold = 1024;   // m below this: hi/lo operand pairs
 
 enum Family {
   F_MOMENTUM = 0, F_NORM, F_GEMM, F_SPLITK, F_UPDATE, F_GAMMA, F_CLIP,
-  F_ML_INIT, F_ML, F_ML_FIN, F_ADAMW, F_COUNT
+  F_ML_INIT, F_ML, F_ML_FIN, F_ADAMW, F_ATTN, F_COUNT
 };
 const char* kFamilyNames[F_COUNT] = {"momentum_norm", "norm_finalize", "ns_gemm", "splitk_reduce",
                                      "update_clip", "gamma", "clip_apply", "max_logits_init",
-                                     "max_logits", "max_logits_finalize", "adamw"};
+                                     "max_logits", "max_logits_finalize", "adamw", "attention"};
 
 struct ProfRec { int fam; hipEvent_t a, b; double flops, bytes; };
 std::mutex g_prof_mu;
@@ -672,6 +672,65 @@ mc_status max_logits_per_head(const void* q, const void* k, const void* k_shared
     Prof pr(F_ML_FIN, s, 0.0, 0.0);
     hipError_t e = launch_max_logits_finalize(a.out_enc, scale, H, s);
     if (e != hipSuccess) return fail(MC_ERR_HIP, "max_logits finalize: %s", hipGetErrorString(e));
+  }
+  return MC_OK;
+}
+
+mc_status attention_forward(const void* q, const void* k, const void* k_shared, const void* v, void* o, float* lse,
+                            float* s_max_out, int32_t B, int32_t T, int32_t H, int32_t d_q, int32_t d_k,
+                            int32_t d_shared, int32_t d_v, const int64_t* q_stride, const int64_t* k_stride,
+                            const int64_t* ks_stride, const int64_t* v_stride, const int64_t* o_stride,
+                            int32_t causal, float scale, void* stream) {
+  if (B < 0 || T < 0 || H <= 0) return fail(MC_ERR_SHAPE, "B, T must be >= 0 and H >= 1");
+  if (d_q != d_k + d_shared || d_k != 128 || !(d_shared == 0 || d_shared == 64) || d_v != 128)
+    return fail(MC_ERR_SHAPE, "attention_forward covers (d_k, d_shared, d_v) = (128, 0 or 64, 128) with "
+                "d_q = d_k + d_shared (got %d, %d, %d, %d)", d_q, d_k, d_shared, d_v);
+  if (!isfinite(scale) || scale <= 0.0f) return fail(MC_ERR_HPARAM, "scale must be finite and > 0");
+  if ((lse && !aligned(lse, 4)) || (s_max_out && !aligned(s_max_out, 4)))
+    return fail(MC_ERR_ALIGN, "lse / s_max_out misaligned");
+  const bool empty = B == 0 || T == 0;
+  AttnArgs a{};
+  if (!empty) {
+    if (!q || !k || !v || !o) return fail(MC_ERR_NULL, "q, k, v or o is NULL");
+    if (!q_stride || !k_stride || !v_stride || !o_stride) return fail(MC_ERR_NULL, "a stride array is NULL");
+    if (d_shared > 0 && (!k_shared || !ks_stride)) return fail(MC_ERR_NULL, "k_shared / ks_stride is NULL");
+    for (int i = 0; i < 3; ++i)
+      if (q_stride[i] < 0 || k_stride[i] < 0 || v_stride[i] < 0 || o_stride[i] < 0)
+        return fail(MC_ERR_SHAPE, "negative stride");
+    if (d_shared > 0 && (ks_stride[0] < 0 || ks_stride[1] < 0)) return fail(MC_ERR_SHAPE, "negative stride");
+    // the tile loads keep 64 rows of offsets in 32 bits
+    const int64_t kLimit = (int64_t)1 << 23;
+    if (k_stride[1] >= kLimit || v_stride[1] >= kLimit || (d_shared > 0 && ks_stride[1] >= kLimit))
+      return fail(MC_ERR_SHAPE, "t stride of k, k_shared or v must be < 2^23 elements");
+    a.q = q; a.k = k; a.ks = d_shared > 0 ? k_shared : nullptr; a.v = v; a.o = o;
+    a.qs_b = q_stride[0]; a.qs_t = q_stride[1]; a.qs_h = q_stride[2];
+    a.ks_b = k_stride[0]; a.ks_t = k_stride[1]; a.ks_h = k_stride[2];
+    a.kss_b = d_shared > 0 ? ks_stride[0] : 0; a.kss_t = d_shared > 0 ? ks_stride[1] : 0;
+    a.vs_b = v_stride[0]; a.vs_t = v_stride[1]; a.vs_h = v_stride[2];
+    a.os_b = o_stride[0]; a.os_t = o_stride[1]; a.os_h = o_stride[2];
+  }
+  a.B = B; a.T = T; a.H = H; a.d_k = d_k; a.d_s = d_shared; a.d_v = d_v;
+  a.causal = causal ? 1 : 0; a.scale = scale;
+  a.lse = lse; a.smax_enc = (uint32_t*)s_max_out;
+  if (!empty && !attention_supported(a))
+    return fail(MC_ERR_ALIGN, "attention_forward needs 16-byte aligned q, k, k_shared, v, o and strides that "
+                "are multiples of 8 elements");
+  hipStream_t s = (hipStream_t)stream;
+  if (s_max_out) {
+    Prof pr(F_ML_INIT, s, 0.0, 0.0);
+    hipError_t e = launch_max_logits_init(a.smax_enc, H, s);
+    if (e != hipSuccess) return fail(MC_ERR_HIP, "s_max init: %s", hipGetErrorString(e));
+  }
+  if (!empty) {
+    const double pairs = causal ? (double)T * (T + 1) / 2.0 : (double)T * T;
+    Prof pr(F_ATTN, s, 2.0 * (d_q + d_v) * pairs * B * H, 0.0);
+    hipError_t e = launch_attention(a, s);
+    if (e != hipSuccess) return fail(MC_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
+  }
+  if (s_max_out) {
+    Prof pr(F_ML_FIN, s, 0.0, 0.0);
+    hipError_t e = launch_max_logits_finalize(a.smax_enc, scale, H, s);
+    if (e != hipSuccess) return fail(MC_ERR_HIP, "s_max finalize: %s", hipGetErrorString(e));
   }
   return MC_OK;
 }

@@ -179,4 +179,38 @@ hipError_t launch_max_logits_init(uint32_t* enc, int32_t H, hipStream_t s);
 hipError_t launch_max_logits(const MaxLogitArgs& a, hipStream_t s, bool* used_mfma);
 hipError_t launch_max_logits_finalize(uint32_t* enc, float scale, int32_t H, hipStream_t s);
 
+// Order-preserving map of fp32 onto uint32 (a < b  <=>  enc(a) < enc(b) for
+// non-NaN values), so that integer atomicMax reduces floats.
+__device__ inline uint32_t order_enc(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline float order_dec(uint32_t k) {
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __builtin_bit_cast(float, u);
+}
+
+// ---------------------------------------------------------------- attention forward
+
+// Softmax attention of one layer (bf16 in and out), with the per-head max
+// logit taken from the same pass when smax_enc is set. Element strides; the
+// last dimension of every tensor is contiguous.
+struct AttnArgs {
+  const void* q; const void* k; const void* ks; const void* v;
+  void* o;
+  float* lse;            // [B][H][T] natural-log sum of exp(scaled logits), or NULL
+  uint32_t* smax_enc;    // [H] ordered-integer running max of the raw logits, or NULL
+  int64_t qs_b, qs_t, qs_h;
+  int64_t ks_b, ks_t, ks_h;
+  int64_t kss_b, kss_t;
+  int64_t vs_b, vs_t, vs_h;
+  int64_t os_b, os_t, os_h;
+  int32_t B, T, H, d_k, d_s, d_v;
+  int32_t causal;
+  float scale;           // softmax scale (1/sqrt(d) normally)
+};
+// true when the kernel covers (d_k, d_s, d_v) and the alignments
+bool attention_supported(const AttnArgs& a);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
 }  // namespace mc

@@ -15,10 +15,10 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mu
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text))
-    keywords = {"if", "sizeof", "defined", "return"}
-    return sorted(n for n in names if n not in keywords and (n.startswith("mc_") or n in (
-        "muonclip_step", "max_logits_per_head", "qk_clip_apply", "adamw_step")))
+    # every function declaration: a return type at the start of a line, then the name
+    names = re.findall(r"^(?:const\s+)?(?:mc_status|void|size_t|int32_t|char)\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
 
 
 def test_library_exports_every_declared_function():
