@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--adamw", action="store_true",
                     help="time the AdamW entry point (the parameters Muon does not cover) on a "
                          "synthetic set: one 512M-element vector plus 64 norm-sized vectors of 7168")
+    ap.add_argument("--attention", action="store_true",
+                    help="time attention_forward (softmax attention with S_max taken from its own row "
+                         "maxima) on the attention shape of --config (2: MHA layer, 3: MLA layer), against "
+                         "the same forward without S_max and the separate max_logits_per_head pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain streaming copy of MIB MiB (read + write) five times, "
                          "to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -235,6 +239,75 @@ def adamw_bench(args):
                                    "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}), flush=True)
 
 
+def attention_bench(args):
+    """attention_forward on one attention layer's seeded Q, K, V (resident on
+    the device): with S_max and lse (the fused path), without them (the plain
+    forward), and max_logits_per_head alone (the pass the fused path makes
+    unnecessary). Prints its own JSON line; value = the fused forward in ms."""
+    import numpy as np
+    import torch
+
+    import muonclip_step_amd as mc
+    import workloads as wl
+    mc.load()
+    if args.config not in (2, 3):
+        raise SystemExit("--attention covers --config 2 (MHA layer) and 3 (MLA layer)")
+    cfg = wl.config(args.config)
+    a = cfg.attn
+    print(f"[bench] drawing Q, K, V of {cfg.name}", file=sys.stderr, flush=True)
+    wts = {s.name: wl.draw_weight(cfg, i) for i, s in enumerate(cfg.matrices) if not s.device_drawn}
+    q, k, ks = wl.draw_attention_inputs(cfg, wts)
+    v = wl.draw_attention_values(cfg, wts)
+    dev = torch.device("cuda:0")
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).to(dev)
+    qd, kd, vd = up(q), up(k), up(v)
+    ksd = up(ks) if ks is not None else None
+    del q, k, ks, v, wts
+    o = torch.empty(a.B, a.T, a.H, a.d_v, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(a.B, a.H, a.T, dtype=torch.float32, device=dev)
+    smax = torch.empty(a.H, dtype=torch.float32, device=dev)
+    fused = lambda: mc.attention_forward(qd, kd, ksd, vd, causal=True, out=o, lse=lse, s_max=smax)
+    plain = lambda: mc.attention_forward(qd, kd, ksd, vd, causal=True, out=o)
+    separate = lambda: mc.max_logits_per_head(qd, kd, ksd, causal=True, out=smax)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_fused, ms_plain, ms_sep = timed(fused), timed(plain), timed(separate)
+    mc.profile_enable(True)
+    for _ in range(args.steps):
+        fused()
+    torch.cuda.synchronize()
+    prof = mc.profile_read()
+    mc.profile_enable(False)
+    at = prof["attention"]
+    tflops = at["flops"] / (at["ms"] * 1e-3) / 1e12
+    pairs = a.B * a.H * a.T * (a.T + 1) / 2
+    print(json.dumps({
+        "metric": "attention forward with S_max ms (fused S_max source)", "value": round(ms_fused, 4), "unit": "ms",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_fused, 4),
+        "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name + "_attention", "attention": f"B{a.B} T{a.T} H{a.H} d{a.d_q}/{a.d_v} causal"},
+        "forward_without_smax_ms": round(ms_plain, 4),
+        "smax_overhead_ms": round(ms_fused - ms_plain, 4),
+        "separate_max_logits_pass_ms": round(ms_sep, 4),
+        "logits": int(pairs),
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_launch_us": round(at["ms"] / max(1, at["launches"]) * 1e3, 2)},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -248,6 +321,9 @@ def main():
         return
     if args.adamw:
         adamw_bench(args)
+        return
+    if args.attention:
+        attention_bench(args)
         return
 
     import muonclip_step_amd as mc

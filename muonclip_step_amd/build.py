@@ -34,12 +34,8 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-# Per-source additions. The attention kernel keeps its logits in VGPRs for
-# the softmax, so its MFMAs write VGPRs (accumulators the register allocator
-# cannot fit there go to AGPRs as spill slots).
-EXTRA = {
-    "attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-}
+# Per-source additions to FLAGS (none at present).
+EXTRA: dict = {}
 
 
 def _compile(src: str) -> str:

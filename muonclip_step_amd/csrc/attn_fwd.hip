@@ -29,6 +29,7 @@
 #include <math.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "mc_internal.h"
 
@@ -53,6 +54,77 @@ constexpr int kBQ = 256, kBKV = 64, kDV = 128;
 // consecutive rows at the same columns; chunk ^ 4 (r & 3) puts them on
 // distinct banks.
 __device__ __forceinline__ int v_swz(int r) { return 4 * (r & 3); }
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// inline LDS reads with an immediate offset, and waits that name the
+// registers they complete (see the kernel)
+template <int OFF>
+__device__ __forceinline__ void lds_read_b128(u32x4_t& dst, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void lds_read_tr(v4i16_t& dst, uint32_t addr) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "i"(OFF));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4_t& r) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(v4i16_t (&l)[4], v4i16_t (&h)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(l[0]), "+v"(l[1]), "+v"(l[2]), "+v"(l[3]), "+v"(h[0]), "+v"(h[1]), "+v"(h[2]), "+v"(h[3])
+               : "i"(N));
+}
+
+// S^T = K Q^T k-step as inline MFMAs writing VGPRs (the softmax reads the
+// logits with VALU instructions; the output accumulators, which only MFMAs
+// touch, stay in AGPRs through the compiler's own MFMAs). Hazards the
+// compiler cannot see: a VALU write of an operand needs two wait states
+// before the MFMA reads it (the leading s_nop 1), and VALU reads of the
+// result wait for s_wait_logits below.
+__device__ __forceinline__ void mfma_s_first(f32x16_t& acc, const u32x4_t& a, const bf16x8_t& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s(f32x16_t& acc, const u32x4_t& a, const bf16x8_t& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+// 24 wait states between the last logit MFMA and the first VALU read of its
+// result (more than the 8-pass MFMA's requirement)
+__device__ __forceinline__ void s_wait_logits(f32x16_t& a0, f32x16_t& a1) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0), "+v"(a1));
+}
+
+// Rescale of one output accumulator in place in its AGPR. The compiler only
+// sees an AGPR operand, so the accumulators never leave the AGPRs (VALU
+// arithmetic on them would make it keep copies in VGPRs across the loop).
+// acc_wait_mfma separates the MFMAs that last wrote the accumulators from
+// these reads (more wait states than an 8-pass MFMA needs); acc_wait_valu
+// separates the writes from the next MFMA that accumulates into them.
+__device__ __forceinline__ void acc_scale(float& x, float s) {
+  float t;
+  asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+               : "+a"(x), "=&v"(t) : "v"(s));
+}
+__device__ __forceinline__ void acc_wait_mfma(f32x16_t (&o)[2][4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]),
+                 "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
+}
+__device__ __forceinline__ void acc_wait_valu(f32x16_t (&o)[2][4]) {
+  asm volatile("s_nop 4"
+               : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]),
+                 "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
+}
 
 __device__ __forceinline__ float wave_max(float x) {
   for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
@@ -181,46 +253,90 @@ attn_fwd_kernel(const AttnArgs a) {
     }
   };
 
-  // per-lane byte offsets of the transposing V reads inside a V tile: lane
-  // 4 q + a of 16-lane group G points at key row 4 (G / 2) + q, columns
-  // 16 (G % 2) + 4 a of a 32-column block; the read returns to lane t of the
-  // group rows 4 (G / 2) .. +3 of column 16 (G % 2) + t, and a second read 8
-  // rows lower gives the other four keys of the MFMA's k order.
-  uint32_t voff[4];
+  // LDS fragment reads are inline ds_read instructions, issued ahead of
+  // their MFMAs and waited for with explicit counts: the compiler does not
+  // see them, so it neither waits for every outstanding read before each use
+  // nor (taking them for aliases of the direct-to-LDS loads) for the next
+  // tile's loads. LDS operations complete in issue order, so a count that
+  // also covers a compiler-issued operation (the lane-pair shuffles) only
+  // waits longer. Each wait names the registers it completes, so nothing
+  // reads or moves them earlier. Immediate offsets carry the buffer, the key
+  // half and the k-step; the per-lane parts are computed once.
+  //
+  // K fragment reads (A operand of S^T): lane l reads key row 32 g + l % 32,
+  // chunk 2 s + l / 32 (content dims, 256-byte rows, chunk ^ (r & 15)) or
+  // 2 (s - 8) + l / 32 (rotary dims, 128-byte rows, chunk ^ ((r >> 1) & 7));
+  // row r and r + 32 share the swizzle, so g is an immediate.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)lds);
+  uint32_t kq[KS];
+  {
+    const int r = lane & 31;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      kq[s] = lds0 + (s < 8 ? r * 256 + (((2 * s + hl) ^ (r & 15)) << 4)
+                            : KC_BYTES + r * 128 + (((2 * (s - 8) + hl) ^ ((r >> 1) & 7)) << 4));
+  }
+  // V^T fragment reads: lane 4 q + a of 16-lane group G points at key row
+  // 4 (G / 2) + q, columns 16 (G % 2) + 4 a of 32-column block n; the
+  // transposing read returns to lane t of the group rows 4 (G / 2) .. +3 of
+  // column 16 (G % 2) + t, and a second read 8 rows lower gives the other
+  // four keys of the MFMA's k order.
+  uint32_t vq[4];
   {
     const int G = lane >> 4, qq = (lane & 15) >> 2, a2 = lane & 3;
     const int r = 4 * (G >> 1) + qq;
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       const int c = (32 * n + 16 * (G & 1) + 4 * a2) >> 3;
-      voff[n] = r * (kDV * 2) + ((c ^ v_swz(r)) << 4) + (a2 & 1) * 8;
+      vq[n] = lds0 + KC_BYTES + KR_BYTES + r * (kDV * 2) + ((c ^ v_swz(r)) << 4) + (a2 & 1) * 8;
     }
   }
 
-  // One key tile of 64, in two halves of 32 keys (g): S^T = K Q^T, online
+  // One key tile of 64 in two halves of 32 keys (g): S^T = K Q^T, online
   // softmax, O^T += V^T P^T. MASK applies the causal and ragged-end masks
-  // (only the wave's diagonal tile and the tile holding key T - 1 need it).
-  auto tile = [&](const int kv0, const char* kt, auto mask_tag) {
+  // (only the wave's diagonal tile and the tile holding key T - 1 need it);
+  // BUF is the LDS stage.
+  auto tile = [&](const int kv0, auto mask_tag, auto buf_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const char* vt = kt + KC_BYTES + KR_BYTES;
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    u32x4_t kf[KS];
+    v4i16_t vl[2][4], vh[2][4];
+    auto read_k = [&](auto g_) {
+      constexpr int g = decltype(g_)::value;
+      static_for<KS>([&](auto s_) {
+        constexpr int s = decltype(s_)::value;
+        constexpr int off = BUF * STAGE + g * (s < 8 ? 32 * 256 : 32 * 128);
+        lds_read_b128<off>(kf[s], kq[s]);
+      });
+    };
+    auto read_v = [&](auto g_, auto p_) {
+      constexpr int g = decltype(g_)::value, p = decltype(p_)::value;
+      static_for<4>([&](auto n_) {
+        constexpr int n = decltype(n_)::value;
+        constexpr int off = BUF * STAGE + (32 * g + 16 * p) * (kDV * 2);
+        lds_read_tr<off>(vl[p][n], vq[n]);
+        lds_read_tr<off + 8 * kDV * 2>(vh[p][n], vq[n]);
+      });
+    };
+    read_k(std::integral_constant<int, 0>{});
+    static_for<2>([&](auto g_) {
+      constexpr int g = decltype(g_)::value;
       // sacc[f] register e of lane l: key kv0 + 32 g + 8 (e / 4) + 4 (l / 32)
       // + e % 4, query wq0 + 32 f + l % 32
-      f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
-      const int r = 32 * g + (lane & 31);
+      f32x16_t sacc[2];
+      // outstanding before the waits: the KS K reads of this half (issued
+      // last), nothing else
+      static_for<KS>([&](auto s_) {
+        constexpr int s = decltype(s_)::value;
+        lgkm_wait<KS - 1 - s>(kf[s]);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        // content dimensions: 256-byte rows, chunk ^ (r & 15); rotary: 128-byte
-        // rows, chunk ^ ((r >> 1) & 7) (two rows per bank cycle)
-        const int c = 2 * (s < 8 ? s : s - 8) + hl;
-        const char* ka = s < 8 ? kt + r * 256 + ((c ^ (r & 15)) << 4)
-                               : kt + KC_BYTES + r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
-        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)ka);
-#pragma unroll
-        for (int f = 0; f < 2; ++f)
-          sacc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[f][s], sacc[f], 0, 0, 0);
-      }
+        for (int f = 0; f < 2; ++f) {
+          if (s == 0) mfma_s_first(sacc[f], kf[s], qf[f][s]);
+          else mfma_s(sacc[f], kf[s], qf[f][s]);
+        }
+      });
+      s_wait_logits(sacc[0], sacc[1]);
+      read_v(g_, std::integral_constant<int, 0>{});
       if (MASK) {
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
@@ -246,6 +362,7 @@ attn_fwd_kernel(const AttnArgs a) {
         grow = grow || (x > m_use[f] + thr);
       }
       if (__any(grow)) {
+        acc_wait_mfma(oacc);
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
           const float mn = fmaxf(m_use[f], bm[f]);
@@ -253,13 +370,19 @@ attn_fwd_kernel(const AttnArgs a) {
           m_use[f] = mn;
           lsum[f] *= alpha;
 #pragma unroll
-          for (int n = 0; n < 4; ++n) oacc[f][n] *= alpha;
+          for (int n = 0; n < 4; ++n)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              float x = oacc[f][n][e];
+              acc_scale(x, alpha);
+              oacc[f][n][e] = x;
+            }
         }
+        acc_wait_valu(oacc);
       }
       // P^T = exp2(c2 (S^T - m)) in bf16; k-step p takes registers 8 p .. 8 p + 7
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        bf16x8_t pb[2];
+      bf16x8_t pb[2][2];   // [p][f]
+      auto probs = [&](const int p) {
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
           const float nm = -m_use[f] * c2;
@@ -268,22 +391,31 @@ attn_fwd_kernel(const AttnArgs a) {
           for (int e = 0; e < 8; ++e) {
             const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[f][8 * p + e], c2, nm));
             ls += pv;
-            pb[f][e] = (__bf16)pv;
+            pb[p][f][e] = (__bf16)pv;
           }
           lsum[f] += ls;
         }
-        const char* vs = vt + (32 * g + 16 * p) * (kDV * 2);
+      };
+      auto pv_step = [&](const int p) {
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
-          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vs + voff[n]));
-          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(vs + voff[n] + 8 * (kDV * 2)));
-          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(vl[p][n], vh[p][n], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int f = 0; f < 2; ++f)
-            oacc[f][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[f], oacc[f][n], 0, 0, 0);
+            oacc[f][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[p][f], oacc[f][n], 0, 0, 0);
         }
-      }
-    }
+      };
+      probs(0);
+      read_v(g_, std::integral_constant<int, 1>{});
+      // outstanding: the 8 reads of p = 1 (those of p = 0 are older)
+      lgkm_wait<8>(vl[0], vh[0]);
+      pv_step(0);
+      probs(1);
+      if (g == 0) read_k(std::integral_constant<int, 1>{});
+      // outstanding: (the next half's KS K reads, issued after) the reads of p = 1
+      lgkm_wait<g == 0 ? KS : 0>(vl[1], vh[1]);
+      pv_step(1);
+    });
   };
 
   // Tiles this wave computes: all of them without a causal mask; with one,
@@ -297,16 +429,32 @@ attn_fwd_kernel(const AttnArgs a) {
     FA_WAIT_DMA();
     __syncthreads();
   }
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  // the mask-free tiles in pairs (stage 0, stage 1), so each stage's LDS
+  // offsets are immediates and the accumulators take one path
   int it = 0;
-  for (; it < n_full; ++it) {
-    if (it + 1 < nkv) dma(it + 1, (it + 1) & 1);
-    tile(it * kBKV, lds + (it & 1) * STAGE, std::false_type{});
+  for (; it + 2 <= n_full; it += 2) {
+    if (it + 1 < nkv) dma(it + 1, 1);
+    tile(it * kBKV, std::false_type{}, B0{});
     FA_WAIT_DMA();   // this wave's loads of the next tile have landed
     __syncthreads();
+    if (it + 2 < nkv) dma(it + 2, 0);
+    tile((it + 1) * kBKV, std::false_type{}, B1{});
+    FA_WAIT_DMA();
+    __syncthreads();
+  }
+  if (it < n_full) {   // it is even here
+    if (it + 1 < nkv) dma(it + 1, 1);
+    tile(it * kBKV, std::false_type{}, B0{});
+    FA_WAIT_DMA();
+    __syncthreads();
+    ++it;
   }
   for (; it < n_w; ++it) {
     if (it + 1 < nkv) dma(it + 1, (it + 1) & 1);
-    tile(it * kBKV, lds + (it & 1) * STAGE, std::true_type{});
+    if (it & 1) tile(it * kBKV, std::true_type{}, B1{});
+    else tile(it * kBKV, std::true_type{}, B0{});
     FA_WAIT_DMA();
     __syncthreads();
   }
