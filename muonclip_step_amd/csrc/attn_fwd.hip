@@ -21,7 +21,8 @@
 // the rescale is a per-lane scalar, and P^T is the S^T accumulator itself
 // converted to bf16 (the MFMA's k order is permuted to match it on both
 // operands). The running max used for the exponentials moves only when a
-// tile's max exceeds it by more than 8 binary orders, so the output
+// tile's max exceeds it by more than 96 binary orders (and then moves 32
+// orders past the tile max), so the output
 // accumulators are rescaled rarely; the exact running max is kept beside it
 // for S_max. Blocks are issued heaviest causal row first; the q-tiles of one
 // (sample, head) are HB apart in launch order, which keeps them on one XCD
@@ -174,7 +175,14 @@ attn_fwd_kernel(const AttnArgs a) {
   const int kend = a.causal ? min(a.T, q0 + kBQ) : a.T;
   const int nkv = (kend + kBKV - 1) / kBKV;
   const float c2 = a.scale * 1.4426950408889634f;   // scale * log2(e)
-  const float thr = 8.0f / c2;                      // lazy-rescale slack in raw logit units
+  // lazy-rescale slack in raw logit units: probabilities stay below 2^96,
+  // so row sums and output accumulators stay below 2^96 T max|v| (below the
+  // fp32 / bf16 limit of 2^128 for T max|v| < 2^32), with the same relative
+  // precision
+  const float thr = 96.0f / c2;
+  // a new reference sits this far above the tile max (the max element's
+  // probability is then 2^-32), so the next rescale needs 128 orders of growth
+  const float head = 32.0f / c2;
 
   f32x16_t oacc[2][4];
 #pragma unroll
@@ -365,7 +373,7 @@ attn_fwd_kernel(const AttnArgs a) {
         acc_wait_mfma(oacc);
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
-          const float mn = fmaxf(m_use[f], bm[f]);
+          const float mn = fmaxf(m_use[f], bm[f] + head);
           const float alpha = __builtin_amdgcn_exp2f((m_use[f] - mn) * c2);
           m_use[f] = mn;
           lsum[f] *= alpha;
