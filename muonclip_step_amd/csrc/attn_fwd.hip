@@ -127,6 +127,15 @@ __device__ __forceinline__ void acc_wait_valu(f32x16_t (&o)[2][4]) {
                  "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
 }
 
+// max of three numbers ignoring quiet NaNs (IEEE maxNum, as fmaxf), in one
+// v_max3_f32 and without the quieting copies the compiler puts before fmaxf
+// on MFMA results (the logits are read after s_wait_logits)
+__device__ __forceinline__ float max3_nan_ignoring(float a, float b, float c) {
+  float r;
+  asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ float wave_max(float x) {
   for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
   return x;
@@ -361,9 +370,10 @@ attn_fwd_kernel(const AttnArgs a) {
       bool grow = false;
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
-        float x = sacc[f][0];
+        float x = max3_nan_ignoring(sacc[f][0], sacc[f][1], sacc[f][2]);
 #pragma unroll
-        for (int e = 1; e < 16; ++e) x = fmaxf(x, sacc[f][e]);
+        for (int e = 3; e < 15; e += 2) x = max3_nan_ignoring(x, sacc[f][e], sacc[f][e + 1]);
+        x = max3_nan_ignoring(x, sacc[f][15], sacc[f][15]);
         x = fmaxf(x, __shfl_xor(x, 32));
         bm[f] = x;
         if (SMAX) m_all[f] = fmaxf(m_all[f], x);

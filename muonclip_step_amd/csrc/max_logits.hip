@@ -42,20 +42,63 @@ __device__ inline void block_max_commit(float mx, uint32_t* out, float* red) {
 typedef __attribute__((address_space(3))) void ml_lds_void_t;
 
 
+// XOR swizzle of the 16-byte chunks of an LDS key row of CPR chunks: a
+// ds_read_b128 pass serves 16 lanes that read one logical chunk of 16
+// consecutive rows, and the swizzle puts them on 16 distinct 4-bank groups.
+// Rows of 256 bytes: chunk ^ (r & 15). Rows of 128 or 384 bytes, whose odd
+// rows start half a bank cycle later: chunk ^ ((r >> 1) & 7). The XOR stays
+// inside the chunk's aligned group of 8 or 16, so it never leaves the row.
+template <int CPR>
+__device__ __forceinline__ int ml_swz(int r) {
+  static_assert(CPR == 8 || CPR == 16 || CPR == 24, "key row width");
+  return CPR == 16 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// Inline LDS fragment read and a counted wait that names the register it
+// completes (the compiler neither tracks the read nor, taking it for an alias
+// of the direct-to-LDS loads, waits for those before it).
+__device__ __forceinline__ void ml_lds_read(u32x4_t& dst, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1" : "=v"(dst) : "v"(addr));
+}
+template <int N>
+__device__ __forceinline__ void ml_lgkm_wait(u32x4_t& r) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
+}
+// Running max of a 32x32 logit fragment pair. v_max3_f32 returns the larger
+// of two numbers when one is a quiet NaN (IEEE maxNum), as fmaxf does; the
+// inline form skips the quieting copies the compiler otherwise puts before
+// every fmaxf on an MFMA result. The MFMA results are read only after
+// ml_wait_mfma's 24 wait states (more than an 8-pass MFMA's requirement).
+__device__ __forceinline__ void ml_wait_mfma(f32x16_t& a0, f32x16_t& a1) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0), "+v"(a1));
+}
+__device__ __forceinline__ float ml_max3(float m, float x, float y) {
+  float r;
+  asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(x), "v"(y));
+  return r;
+}
+// s_waitcnt on the vector-memory counter alone
+template <int N>
+__device__ __forceinline__ void ml_vm_wait() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
+}
+
 // Key-tile kernel for per-head keys (d = 64, 128): a 256-thread block owns
 // 256 query rows, each wave keeps 64 of them as A fragments, and 64-key tiles
-// of K pass through double-buffered, XOR-swizzled LDS via registers (the next
-// tile's loads go out before the current tile's MFMAs). Its registers allow
-// two blocks per CU, whose interleaving hides each block's start-up and the
-// per-tile barrier.
+// of K arrive in a three-stage LDS ring through direct-to-LDS loads issued
+// two tiles ahead (the XOR swizzle is applied on the source side: the lane
+// filling physical chunk pc of row r fetches chunk pc ^ swz(r)). A wave
+// reads the eight fragments of a 32-key half with inline reads and consumes
+// them under counted waits. At most 256 registers, so two blocks share a CU
+// and hide each other's start-up and per-tile barrier.
 template <int DK>
-__global__ void __launch_bounds__(256, 1) max_logits_tile_kernel(const MaxLogitArgs a) {
-  constexpr int DS = 0;
-  constexpr int D = DK + DS, DC = D / 8, KS = D / 16;
-  constexpr int BQ = 256, BKV = 64;
-  constexpr int PT = BKV * DC / 256;              // 16-byte chunks per thread per key tile
-  static_assert((BKV * DC) % 256 == 0 && (DC % 8) == 0, "tile shape");
-  __shared__ u32x4_t kt[2][BKV * DC];
+__global__ void __launch_bounds__(256, 2) max_logits_tile_kernel(const MaxLogitArgs a) {
+  constexpr int D = DK, DC = D / 8, KS = D / 16, RB = 2 * D;
+  constexpr int BQ = 256, BKV = 64, NST = 3;
+  constexpr int TILE = BKV * RB;                  // bytes per stage
+  constexpr int PW = BKV * DC / 64 / 4;           // direct-to-LDS instructions per wave per tile
+  static_assert(PW * 256 == BKV * DC && KS <= 8, "tile shape");
+  __shared__ __attribute__((aligned(16))) char kt[NST * TILE];
   __shared__ float red[4];
 
   const int HB = a.H * a.B;
@@ -64,12 +107,12 @@ __global__ void __launch_bounds__(256, 1) max_logits_tile_kernel(const MaxLogitA
   const int qt = nqt - 1 - (int)(blockIdx.x / HB);   // heaviest causal rows first
   const int h = hb % a.H, b = hb / a.H;
   const int q0 = qt * BQ;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wr0 = q0 + wave * 64;
 
   const uint16_t* Q = (const uint16_t*)a.q + (int64_t)b * a.qs_b + (int64_t)h * a.qs_h;
-  const uint16_t* K = (const uint16_t*)a.k + (int64_t)b * a.ks_b + (int64_t)h * a.ks_h;
-  const uint16_t* KS_ = DS > 0 ? (const uint16_t*)a.ks + (int64_t)b * a.kss_b : nullptr;
+  const char* K = (const char*)((const uint16_t*)a.k + (int64_t)b * a.ks_b + (int64_t)h * a.ks_h);
 
   // this wave's query rows as A-fragments: lane l holds row l%32, k-chunk l/32.
   // Rows and keys past T re-read the last valid one; every logit they touch
@@ -87,53 +130,79 @@ __global__ void __launch_bounds__(256, 1) max_logits_tile_kernel(const MaxLogitA
   const int kend = a.causal ? min(a.T, q0 + BQ) : a.T;
   const int nkv = (kend + BKV - 1) / BKV;
   float mx = -INFINITY;
-  u32x4_t st[PT];
 
-#define ML_GLOAD(it_)                                                                  \
-  {                                                                                    \
-    const int kv0_ = (it_) * BKV;                                                      \
-    _Pragma("unroll") for (int i = 0; i < PT; ++i) {                                   \
-      const int q = tid + i * 256, r = q / DC, c = q - r * DC;                         \
-      const int key = kv0_ + r, kr = key < a.T ? key : a.T - 1;                        \
-      const uint16_t* src = (DS == 0 || c < DK / 8)                                    \
-                                ? K + (int64_t)kr * a.ks_t + c * 8                     \
-                                : KS_ + (int64_t)kr * a.kss_t + (c - DK / 8) * 8;      \
-      st[i] = *(const u32x4_t*)src;                                                    \
-    }                                                                                  \
+  // direct-to-LDS loads: instruction i of wave w fills LDS chunks
+  // 64 (PW w + i) .. +63 of the stage; lane offsets relative to the tile's
+  // first key
+  int lrow[PW], loff[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int q = 64 * (PW * wave + i) + lane, r = q / DC, c = (q % DC) ^ ml_swz<DC>(r);
+    lrow[i] = r;
+    loff[i] = r * (int)a.ks_t * 2 + c * 16;
   }
-#define ML_LSTORE(buf_)                                                                \
-  {                                                                                    \
-    _Pragma("unroll") for (int i = 0; i < PT; ++i) {                                   \
-      const int q = tid + i * 256, r = q / DC, c = q - r * DC;                         \
-      kt[(buf_)][r * DC + (c ^ (r & 7))] = st[i];                                      \
-    }                                                                                  \
-  }
-
-  if (nkv > 0) {
-    ML_GLOAD(0);
-    ML_LSTORE(0);
-    __syncthreads();
-  }
-  for (int it = 0; it < nkv; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < nkv) ML_GLOAD(it + 1);
+  auto dma = [&](const int it) __attribute__((always_inline)) {
     const int kv0 = it * BKV;
+    char* st = kt + (it % NST) * TILE;
+    const char* kb = K + (int64_t)kv0 * a.ks_t * 2;
+    const int last = a.T - 1 - kv0;   // rows past it re-read this one
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const int d = lrow[i] > last ? (last - lrow[i]) * (int)a.ks_t * 2 : 0;
+      __builtin_amdgcn_global_load_lds((const void*)(kb + loff[i] + d),
+                                       (ml_lds_void_t*)(st + 1024 * (PW * wave + i)), 16, 0, 0);
+    }
+  };
+  // per-lane LDS offsets of the fragment reads: key row fk * 32 + l % 32,
+  // chunk 2 s + l / 32
+  const uint32_t kt0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)kt);
+  uint32_t fo[KS];
+  {
+    const int r = lane & 31;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) fo[s] = kt0 + r * RB + (((2 * s + (lane >> 5)) ^ ml_swz<DC>(r)) << 4);
+  }
+
+  if (nkv > 0) dma(0);
+  if (nkv > 1) dma(1);
+  if (nkv > 1) ml_vm_wait<PW>();   // tile 0 landed (tile 1 may be in flight)
+  else ml_vm_wait<0>();
+  __syncthreads();
+  for (int it = 0; it < nkv; ++it) {
+    // the stage of tile it + 2 held tile it - 1, which every wave finished
+    // before the last barrier
+    if (it + 2 < nkv) dma(it + 2);
+    const int kv0 = it * BKV;
+    const uint32_t sb = (uint32_t)((it % NST) * TILE);
     if (!(a.causal && kv0 > wr0 + 63) && wr0 < a.T) {
       const bool need_mask = (a.causal && kv0 + BKV - 1 > wr0) || (kv0 + BKV > a.T) || (wr0 + 63 >= a.T);
 #pragma unroll
       for (int fk = 0; fk < 2; ++fk) {
+        u32x4_t kf[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) ml_lds_read(kf[s], fo[s] + sb + fk * 32 * RB);
         f32x16_t acc0 = f32x16_t{}, acc1 = f32x16_t{};
-        const int r = fk * 32 + (lane & 31);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          const int c = 2 * s + (lane >> 5);
-          const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, kt[cur][r * DC + (c ^ (r & 7))]);
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], kf, acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], kf, acc1, 0, 0, 0);
+          switch (KS - 1 - s) {   // reads complete in issue order
+            case 7: ml_lgkm_wait<7>(kf[s]); break;
+            case 6: ml_lgkm_wait<6>(kf[s]); break;
+            case 5: ml_lgkm_wait<5>(kf[s]); break;
+            case 4: ml_lgkm_wait<4>(kf[s]); break;
+            case 3: ml_lgkm_wait<3>(kf[s]); break;
+            case 2: ml_lgkm_wait<2>(kf[s]); break;
+            case 1: ml_lgkm_wait<1>(kf[s]); break;
+            default: ml_lgkm_wait<0>(kf[s]); break;
+          }
+          const bf16x8_t k8 = __builtin_bit_cast(bf16x8_t, kf[s]);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[0][s], k8, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[1][s], k8, acc1, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);   // keep each wait next to its MFMAs
         }
         if (!need_mask) {
+          ml_wait_mfma(acc0, acc1);
 #pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(acc0[e], acc1[e]));
+          for (int e = 0; e < 16; ++e) mx = ml_max3(mx, acc0[e], acc1[e]);
         } else {
           // register e of lane l: query row 8*(e/4) + 4*(l/32) + e%4, key column l%32
           const int j = kv0 + fk * 32 + (lane & 31);
@@ -149,24 +218,13 @@ __global__ void __launch_bounds__(256, 1) max_logits_tile_kernel(const MaxLogitA
         }
       }
     }
-    if (it + 1 < nkv) ML_LSTORE(cur ^ 1);
+    // tile it + 1 landed for this wave (tile it + 2 may be in flight), then
+    // for every wave
+    if (it + 2 < nkv) ml_vm_wait<PW>();
+    else ml_vm_wait<0>();
     __syncthreads();
   }
-#undef ML_GLOAD
-#undef ML_LSTORE
   block_max_commit(mx, a.out_enc + h, red);
-}
-
-// XOR swizzle of the 16-byte chunks of an LDS key row of CPR chunks: a
-// ds_read_b128 pass serves 16 lanes that read one logical chunk of 16
-// consecutive rows, and the swizzle puts them on 16 distinct 4-bank groups.
-// Rows of 256 bytes: chunk ^ (r & 15). Rows of 128 or 384 bytes, whose odd
-// rows start half a bank cycle later: chunk ^ ((r >> 1) & 7). The XOR stays
-// inside the chunk's aligned group of 8 or 16, so it never leaves the row.
-template <int CPR>
-__device__ __forceinline__ int ml_swz(int r) {
-  static_assert(CPR == 8 || CPR == 16 || CPR == 24, "key row width");
-  return CPR == 16 ? (r & 15) : ((r >> 1) & 7);
 }
 
 // A 256-thread block owns 256 query rows of one (head, sample) and walks the
