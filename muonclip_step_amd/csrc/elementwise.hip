@@ -171,6 +171,8 @@ hipError_t launch_norm_finalize(const float* partial, int32_t parts, int64_t str
   return hipGetLastError();
 }
 
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+
 // ---------------------------------------------------------------- update
 
 __global__ void __launch_bounds__(256) update_kernel(const UpdArgs a) {
@@ -194,7 +196,67 @@ __global__ void __launch_bounds__(256) update_kernel(const UpdArgs a) {
     }
     __syncthreads();
   }
+  if (u.vec8 && !u.o_trans) {
+    // 8-element (16-byte) vectors: the 64x64 tile as 32 rows x 8 vectors,
+    // two rows per thread, every load before the first store (W and O never
+    // alias, but the compiler cannot know that and would serialise the rows)
+    const int c8 = tc * 64 + (tid & 7) * 8, r8 = tr * 64 + (tid >> 3);
+    if (c8 >= u.cols) return;
+    u16x8_t ov[2], wv[2];
+    bool in[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int row = r8 + 32 * k;
+      in[k] = row < u.rows;
+      if (in[k]) {
+        ov[k] = *(const u16x8_t*)(u.o + (int64_t)row * u.ld_o + c8);
+        wv[k] = *(const u16x8_t*)((const uint16_t*)u.w + (int64_t)row * u.ld + c8);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (!in[k]) break;
+      const int row = r8 + 32 * k;
+      const float sc = row_clip_scale(u.clip, row, a.s_max, a.heads, a.tau, a.clip_global);
+      if (u.o_out) *(u16x8_t*)(u.o_out + (int64_t)row * u.cols + c8) = ov[k];
+      u16x8_t r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        r[e] = f32_to_bf16(fmaf(-u.lr_rms, bf16_to_f32(ov[k][e]), bf16_to_f32(wv[k][e]) * a.decay) * sc);
+      *(u16x8_t*)((uint16_t*)u.w + (int64_t)row * u.ld + c8) = r;
+    }
+    return;
+  }
   if (col >= u.cols) return;
+  if (u.vec && !u.o_trans && u.w_bf16) {
+    // the common case, with every load of the thread's four rows issued
+    // before the first store (W and O never alias, but the compiler cannot
+    // know that and would otherwise serialise the rows)
+    u16x4_t ov[4], wv[4];
+    bool in[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int row = tr * 64 + ry + 16 * k;
+      in[k] = row < u.rows;
+      if (in[k]) {
+        ov[k] = *(const u16x4_t*)(u.o + (int64_t)row * u.ld_o + col);
+        wv[k] = *(const u16x4_t*)((const uint16_t*)u.w + (int64_t)row * u.ld + col);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (!in[k]) break;
+      const int row = tr * 64 + ry + 16 * k;
+      const float sc = row_clip_scale(u.clip, row, a.s_max, a.heads, a.tau, a.clip_global);
+      if (u.o_out) *(u16x4_t*)(u.o_out + (int64_t)row * u.cols + col) = ov[k];
+      u16x4_t r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        r[e] = f32_to_bf16(fmaf(-u.lr_rms, bf16_to_f32(ov[k][e]), bf16_to_f32(wv[k][e]) * a.decay) * sc);
+      *(u16x4_t*)((uint16_t*)u.w + (int64_t)row * u.ld + col) = r;
+    }
+    return;
+  }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int row = tr * 64 + ry + 16 * k;

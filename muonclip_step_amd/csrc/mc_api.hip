@@ -426,6 +426,8 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
               (!m.o_out || aligned(m.o_out, 8));
       u.o = x_final + (size_t)slot * mp * np;
       u.ld_o = (int32_t)np;
+      u.vec8 = u.vec && u.w_bf16 && m.cols % 8 == 0 && m.ld % 8 == 0 && aligned(m.w, 16) &&
+               (!m.o_out || aligned(m.o_out, 16)) && np % 8 == 0 && aligned(u.o, 16);
       u.o_trans = wide ? 0 : 1;
       u.o_out = (uint16_t*)m.o_out;
       u.lr_rms = (float)((double)hp.lr * (double)hp.rms_scale * sqrt((double)std::max(m.rows, m.cols)));

@@ -112,6 +112,7 @@ struct ClipRule {
 // W <- clip_row * ((1 - lr wd) W - lr * rms * O)
 struct UpdMat {
   void* w; int32_t w_bf16, vec;
+  int32_t vec8;                        // bf16 W, O and o_out rows of 16-byte aligned 8-element vectors
   int64_t ld;
   int32_t rows, cols;
   const uint16_t* o; int32_t ld_o;
