@@ -78,6 +78,27 @@ __global__ void __launch_bounds__(256) momentum_kernel(const MomArgs a) {
   const int tid = threadIdx.x, cx = tid & 15, ry = tid >> 4;
   const int col = tc * 64 + cx * 4;
   float ss = 0.0f;
+  // vector path: every load of the thread's four rows goes out before the
+  // first store (M is read and written in place and G is another buffer,
+  // but the compiler cannot know the rows do not overlap and would
+  // serialise them)
+  f32x4_t mvs[4], gvs[4];
+  if (mm.vec && col < mm.cols) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int row = tr * 64 + ry + 16 * k;
+      if (row < mm.rows) {
+        const int64_t base = (int64_t)row * mm.ld + col;
+        mvs[k] = *(const f32x4_t*)(mm.m + base);
+        if (mm.g_bf16) {
+          const u16x4_t gb = *(const u16x4_t*)((const uint16_t*)mm.g + base);
+          gvs[k] = f32x4_t{bf16_to_f32(gb[0]), bf16_to_f32(gb[1]), bf16_to_f32(gb[2]), bf16_to_f32(gb[3])};
+        } else {
+          gvs[k] = *(const f32x4_t*)((const float*)mm.g + base);
+        }
+      }
+    }
+  }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int lr = ry + 16 * k, row = tr * 64 + lr;
@@ -85,14 +106,7 @@ __global__ void __launch_bounds__(256) momentum_kernel(const MomArgs a) {
     if (row < mm.rows) {
       const int64_t base = (int64_t)row * mm.ld + col;
       if (mm.vec && col < mm.cols) {
-        f32x4_t mv = *(const f32x4_t*)(mm.m + base);
-        f32x4_t gv;
-        if (mm.g_bf16) {
-          const u16x4_t gb = *(const u16x4_t*)((const uint16_t*)mm.g + base);
-          gv = f32x4_t{bf16_to_f32(gb[0]), bf16_to_f32(gb[1]), bf16_to_f32(gb[2]), bf16_to_f32(gb[3])};
-        } else {
-          gv = *(const f32x4_t*)((const float*)mm.g + base);
-        }
+        const f32x4_t mv = mvs[k], gv = gvs[k];
         f32x4_t nv;
         nv[0] = fmaf(a.mu, mv[0], gv[0]); nv[1] = fmaf(a.mu, mv[1], gv[1]);
         nv[2] = fmaf(a.mu, mv[2], gv[2]); nv[3] = fmaf(a.mu, mv[3], gv[3]);
