@@ -191,6 +191,9 @@ typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 
 __global__ void __launch_bounds__(256) update_kernel(const UpdArgs a) {
   __shared__ uint16_t ot[64][66];
+  if (a.gamma_out && blockIdx.x == 0)   // the step's gamma output, from the same s_max
+    for (int i = threadIdx.x; i < a.gamma_slots * a.heads; i += blockDim.x)
+      a.gamma_out[i] = gamma_of(layer_s(a.s_max, i / a.heads, i % a.heads, a.heads, a.clip_global), a.tau);
   const int j = find_mat(a.mat, a.nmat, blockIdx.x);
   const UpdMat& u = a.mat[j];
   const int local = blockIdx.x - u.block_start;

@@ -301,8 +301,12 @@ ClipRule clip_rule(const mc_matrix& m, bool clip_on) {
   return c;
 }
 
+// gamma_once: when it points at a non-NULL gamma output, the first update
+// launch of this wave also writes gamma [slots][heads] and the pointer is
+// cleared, so exactly one launch of the step writes it.
 mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb, const mc_hparams& hp,
-                   const float* s_max, int32_t heads, char* ws, hipStream_t s) {
+                   const float* s_max, int32_t heads, char* ws, hipStream_t s, float** gamma_once,
+                   int32_t slots) {
   const WavePlan w = plan_wave(g, nb);
   const int64_t mp = g.mp, np = g.np;
   // X ping-pong: iteration it reads X[it % 2] and writes X[(it + 1) % 2]
@@ -413,6 +417,10 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
   for (int b0 = 0; b0 < nb; b0 += kMaxBatchMats) {
     UpdArgs a{};
     a.decay = decay; a.s_max = s_max; a.heads = heads; a.tau = hp.tau; a.clip_global = hp.clip_global;
+    if (gamma_once && *gamma_once) {
+      a.gamma_out = *gamma_once; a.gamma_slots = slots;
+      *gamma_once = nullptr;
+    }
     int blocks = 0;
     double bytes = 0;
     for (int j = 0; j < kMaxBatchMats && b0 + j < nb; ++j) {
@@ -549,7 +557,14 @@ mc_status muonclip_step(const mc_matrix* mats, int32_t n, const mc_hparams* hp, 
     return fail(MC_ERR_ALIGN, "s_max / gamma_out misaligned");
   st = check_matrices_step(mats, n, slots, heads, have_smax);
   if (st) return st;
-  if (n == 0) return MC_OK;
+  if (n == 0) {   // nothing to update; gamma is still an output
+    if (gamma_out) {
+      Prof pr(F_GAMMA, (hipStream_t)stream, 0.0, 0.0);
+      hipError_t e = launch_gamma(s_max, gamma_out, slots, heads, hp->tau, hp->clip_global, (hipStream_t)stream);
+      if (e != hipSuccess) return fail(MC_ERR_HIP, "gamma launch: %s", hipGetErrorString(e));
+    }
+    return MC_OK;
+  }
   if (!workspace) return fail(MC_ERR_WORKSPACE, "workspace is NULL");
   if (!aligned(workspace, kAlign)) return fail(MC_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   const std::vector<Group> groups = make_groups(mats, n);
@@ -579,11 +594,7 @@ mc_status muonclip_step(const mc_matrix* mats, int32_t n, const mc_hparams* hp, 
   if (two) chains = plan_chains(groups, cap2, hp->ns_steps);
 
   hipStream_t s = (hipStream_t)stream;
-  if (gamma_out) {
-    Prof pr(F_GAMMA, s, 0.0, 0.0);
-    hipError_t e = launch_gamma(s_max, gamma_out, slots, heads, hp->tau, hp->clip_global, s);
-    if (e != hipSuccess) return fail(MC_ERR_HIP, "gamma launch: %s", hipGetErrorString(e));
-  }
+  float* gamma_once = gamma_out;   // written by the first update launch
   std::unique_lock<std::mutex> lk(g_aux_mu, std::defer_lock);
   AuxLane* aux = nullptr;
   if (two) {
@@ -597,7 +608,8 @@ mc_status muonclip_step(const mc_matrix* mats, int32_t n, const mc_hparams* hp, 
   }
   if (!two) {
     for (const Chain& c : chains) {
-      st = run_wave(mats, groups[c.gi], groups[c.gi].idx.data() + c.b0, c.nb, *hp, s_max, heads, (char*)workspace, s);
+      st = run_wave(mats, groups[c.gi], groups[c.gi].idx.data() + c.b0, c.nb, *hp, s_max, heads, (char*)workspace, s,
+                    &gamma_once, slots);
       if (st) return st;
     }
     return MC_OK;
@@ -615,7 +627,7 @@ mc_status muonclip_step(const mc_matrix* mats, int32_t n, const mc_hparams* hp, 
     const int lane = load[1] < load[0] ? 1 : 0;
     load[lane] += c.flops;
     st = run_wave(mats, groups[c.gi], groups[c.gi].idx.data() + c.b0, c.nb, *hp, s_max, heads,
-                  (char*)workspace + lane * half, lane ? aux->s : s);
+                  (char*)workspace + lane * half, lane ? aux->s : s, &gamma_once, slots);
     if (st) break;
   }
   // join: `stream` continues only after the auxiliary stream's work (also

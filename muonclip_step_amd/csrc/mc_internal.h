@@ -127,6 +127,7 @@ struct UpdArgs {
   int32_t nmat; int32_t total_blocks;
   float decay;
   const float* s_max; int32_t heads; float tau; int32_t clip_global;
+  float* gamma_out; int32_t gamma_slots;   // block 0 also writes gamma [slots][heads] when set
   UpdMat mat[kMaxBatchMats];
 };
 hipError_t launch_update(const UpdArgs& a, hipStream_t s);

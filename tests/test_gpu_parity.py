@@ -347,3 +347,24 @@ def test_max_logits_empty_gives_neg_inf_and_gamma_one():
     out = mc.max_logits_per_head(q, q, None, causal=True)
     torch.cuda.synchronize()
     assert torch.all(torch.isneginf(out))
+
+
+def test_gamma_out_without_matrices_and_with_two_lanes():
+    """gamma_out is written once per step: with no matrices at all, and when
+    the step's waves run on two streams (two shape groups)."""
+    s = torch.tensor([50.0, 400.0, -3.0, float("nan"), 100.0, 1e6], dtype=torch.float32, device="cuda")
+    want = oracle.clip_factor(host64(s), 100.0)
+    hp = mc.hparams(tau=100.0)
+    g0 = torch.full((6,), -7.0, dtype=torch.float32, device="cuda")
+    mc.muonclip_step([], hp, s_max=s, slots=2, heads=3, gamma_out=g0)
+    torch.cuda.synchronize()
+    assert np.allclose(host64(g0), want, rtol=1e-6, atol=0)
+    cfg = wl.config(1)
+    states = load_config_states(cfg)                    # 256x512 and two 64x64: two groups
+    descs = [st.desc() for st in states]
+    s4 = s[:4].contiguous()                             # config 1: one layer of 4 heads
+    g1 = torch.full((4,), -7.0, dtype=torch.float32, device="cuda")
+    ws = torch.empty(mc.workspace_size(descs, hp), dtype=torch.uint8, device="cuda")
+    mc.muonclip_step(descs, hp, s_max=s4, slots=1, heads=4, gamma_out=g1, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.allclose(host64(g1), want[:4], rtol=1e-6, atol=0)
