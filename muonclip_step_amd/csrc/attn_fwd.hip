@@ -8,9 +8,10 @@
 // keys are [k^C_h | k^R] with the rotary key shared by every head; the value
 // width is 128.
 //
-// Layout of the work. A 256-thread block owns 256 query rows of one
-// (sample, head); each wave keeps 64 of them in registers as two MFMA
-// B-fragments for the whole kernel and walks the key axis in tiles of 64
+// Layout of the work. A block owns 256 query rows of one (sample, head):
+// MHA runs eight waves of 32 rows (two waves per SIMD), MLA four waves of 64
+// rows. Each wave keeps its rows in registers as MFMA B-fragments for the
+// whole kernel and walks the key axis in tiles of 64
 // keys, which pass through a double-buffered LDS ring (K rows XOR-swizzled
 // for 16-byte fragment reads, V rows swizzled for transposing reads). Both
 // products run transposed, with v_mfma_f32_32x32x16_bf16:
@@ -88,8 +89,8 @@ __device__ __forceinline__ void lgkm_wait(v4i16_t (&l)[4], v4i16_t (&h)[4]) {
 }
 
 // S^T = K Q^T k-step as inline MFMAs writing VGPRs (the softmax reads the
-// logits with VALU instructions; the output accumulators, which only MFMAs
-// touch, stay in AGPRs through the compiler's own MFMAs). Hazards the
+// logits with VALU instructions; the compiler's own MFMAs accumulate the
+// output, in AGPRs in the four-wave kernel). Hazards the
 // compiler cannot see: a VALU write of an operand needs two wait states
 // before the MFMA reads it (the leading s_nop 1), and VALU reads of the
 // result wait for s_wait_logits below.
@@ -101,13 +102,16 @@ __device__ __forceinline__ void mfma_s(f32x16_t& acc, const u32x4_t& a, const bf
 }
 // 24 wait states between the last logit MFMA and the first VALU read of its
 // result (more than the 8-pass MFMA's requirement)
-__device__ __forceinline__ void s_wait_logits(f32x16_t& a0, f32x16_t& a1) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a0), "+v"(a1));
+template <int NF>
+__device__ __forceinline__ void s_wait_logits(f32x16_t (&a)[NF]) {
+  if constexpr (NF == 2) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a[0]), "+v"(a[1]));
+  else asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a[0]));
 }
 
-// Rescale of one output accumulator in place in its AGPR. The compiler only
-// sees an AGPR operand, so the accumulators never leave the AGPRs (VALU
-// arithmetic on them would make it keep copies in VGPRs across the loop).
+// Four-wave kernel: rescale of one output accumulator in place in its AGPR.
+// The compiler only sees an AGPR operand, so the accumulators never leave
+// the AGPRs (VALU arithmetic on them would make it keep copies in VGPRs
+// across the loop).
 // acc_wait_mfma separates the MFMAs that last wrote the accumulators from
 // these reads (more wait states than an 8-pass MFMA needs); acc_wait_valu
 // separates the writes from the next MFMA that accumulates into them.
@@ -116,15 +120,17 @@ __device__ __forceinline__ void acc_scale(float& x, float s) {
   asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
                : "+a"(x), "=&v"(t) : "v"(s));
 }
-__device__ __forceinline__ void acc_wait_mfma(f32x16_t (&o)[2][4]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-               : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]),
-                 "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
+template <int NF>
+__device__ __forceinline__ void acc_wait_mfma(f32x16_t (&o)[NF][4]) {
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o[f][0]), "+a"(o[f][1]), "+a"(o[f][2]), "+a"(o[f][3]));
 }
-__device__ __forceinline__ void acc_wait_valu(f32x16_t (&o)[2][4]) {
-  asm volatile("s_nop 4"
-               : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[0][2]), "+a"(o[0][3]),
-                 "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
+template <int NF>
+__device__ __forceinline__ void acc_wait_valu(f32x16_t (&o)[NF][4]) {
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+    asm volatile("s_nop 4" : "+a"(o[f][0]), "+a"(o[f][1]), "+a"(o[f][2]), "+a"(o[f][3]));
 }
 
 // max of three numbers ignoring quiet NaNs (IEEE maxNum, as fmaxf), in one
@@ -141,16 +147,26 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
-template <int DK, int DS, bool SMAX>
-__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// NF: query fragments (of 32 rows) per wave. NF = 2: four waves of 64 rows,
+// one wave per SIMD; NF = 1: eight waves of 32 rows, two waves per SIMD,
+// which hide each other's softmax arithmetic and LDS latency behind their
+// MFMAs (the LDS delivers about 200 bytes per clock per CU to two waves
+// per SIMD, enough for the doubled fragment traffic).
+template <int DK, int DS, bool SMAX, int NF>
+__global__ void __launch_bounds__(256 * 2 / NF, 1) __attribute__((amdgpu_waves_per_eu(2 / NF, 2 / NF)))
 attn_fwd_kernel(const AttnArgs a) {
-  static_assert(DK == 128 && (DS == 0 || DS == 64), "head widths");
+  static_assert(DK == 128 && (DS == 0 || DS == 64) && (NF == 1 || NF == 2), "head widths");
+  constexpr int NW = 8 / NF, WR = 32 * NF;   // waves per block, query rows per wave
+  // With four waves the output accumulators live in AGPRs and are rescaled
+  // in place through asm; the eight-wave kernel is compiled with every MFMA
+  // writing VGPRs (its whole state fits 256 VGPRs) and rescales with VALU.
+  constexpr bool kAccInAgpr = NF == 2;
   constexpr int D = DK + DS, KS = D / 16;
   // one LDS stage: K content rows [64][256 B], rotary rows [64][128 B], V rows [64][256 B]
   constexpr int KC_BYTES = kBKV * 256, KR_BYTES = kBKV * DS * 2, VT_BYTES = kBKV * kDV * 2;
   constexpr int STAGE = KC_BYTES + KR_BYTES + VT_BYTES;
   __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
-  __shared__ float red[4];
+  __shared__ float red[NW];
 
   const int HB = a.H * a.B;
   const int nqt = (a.T + kBQ - 1) / kBQ;
@@ -160,7 +176,7 @@ attn_fwd_kernel(const AttnArgs a) {
   const int q0 = qt * kBQ;
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int wq0 = q0 + wave * 64;
+  const int wq0 = q0 + wave * WR;
 
   const uint16_t* Q = (const uint16_t*)a.q + (int64_t)b * a.qs_b + (int64_t)h * a.qs_h;
   const char* K = (const char*)((const uint16_t*)a.k + (int64_t)b * a.ks_b + (int64_t)h * a.ks_h);
@@ -171,9 +187,9 @@ attn_fwd_kernel(const AttnArgs a) {
   // fragment f, dimensions 16 s + 8 (l / 32) .. +7. Rows past T re-read row
   // T - 1: they see exactly row T - 1's keys, so they change no maximum, and
   // their outputs are not stored.
-  bf16x8_t qf[2][KS];
+  bf16x8_t qf[NF][KS];
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+  for (int f = 0; f < NF; ++f) {
     const int row = wq0 + 32 * f + (lane & 31);
     const int rr = row < a.T ? row : a.T - 1;
     const uint16_t* base = Q + (int64_t)rr * a.qs_t + 8 * hl;
@@ -193,14 +209,18 @@ attn_fwd_kernel(const AttnArgs a) {
   // probability is then 2^-32), so the next rescale needs 128 orders of growth
   const float head = 32.0f / c2;
 
-  f32x16_t oacc[2][4];
+  f32x16_t oacc[NF][4];
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+  for (int f = 0; f < NF; ++f)
 #pragma unroll
     for (int n = 0; n < 4; ++n) oacc[f][n] = f32x16_t{};
-  float m_use[2] = {-INFINITY, -INFINITY};   // max the exponentials are taken against
-  float m_all[2] = {-INFINITY, -INFINITY};   // exact running max (S_max)
-  float lsum[2] = {0.0f, 0.0f};              // this lane's half of the row sum
+  float m_use[NF], m_all[NF], lsum[NF];   // reference max, exact running max (S_max), half row sum
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    m_use[f] = -INFINITY;
+    m_all[f] = -INFINITY;
+    lsum[f] = 0.0f;
+  }
 
   // Tiles reach LDS through direct-to-LDS loads (global_load_lds_dwordx4:
   // 64 lanes fill 1 KB of consecutive LDS, so each swizzle is applied on the
@@ -209,7 +229,7 @@ attn_fwd_kernel(const AttnArgs a) {
   // rotary rows (MLA), 4 of V rows; lane offsets are relative to the tile's
   // first key, whose address is the only per-tile arithmetic. Keys past T
   // (only in the tile holding key T - 1) re-read key T - 1 and are masked.
-  constexpr int IC = 4, IR = DS > 0 ? 2 : 0, IV = 4;
+  constexpr int IC = 16 / NW, IR = DS > 0 ? 8 / NW : 0, IV = 16 / NW;
   int crow[IC], coff[IC], vrow[IV], voffs[IV];
   int rrow[IR > 0 ? IR : 1], roff[IR > 0 ? IR : 1];
 #pragma unroll
@@ -340,23 +360,23 @@ attn_fwd_kernel(const AttnArgs a) {
       constexpr int g = decltype(g_)::value;
       // sacc[f] register e of lane l: key kv0 + 32 g + 8 (e / 4) + 4 (l / 32)
       // + e % 4, query wq0 + 32 f + l % 32
-      f32x16_t sacc[2];
+      f32x16_t sacc[NF];
       // outstanding before the waits: the KS K reads of this half (issued
       // last), nothing else
       static_for<KS>([&](auto s_) {
         constexpr int s = decltype(s_)::value;
         lgkm_wait<KS - 1 - s>(kf[s]);
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
+        for (int f = 0; f < NF; ++f) {
           if (s == 0) mfma_s_first(sacc[f], kf[s], qf[f][s]);
           else mfma_s(sacc[f], kf[s], qf[f][s]);
         }
       });
-      s_wait_logits(sacc[0], sacc[1]);
+      s_wait_logits<NF>(sacc);
       read_v(g_, std::integral_constant<int, 0>{});
       if (MASK) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
+        for (int f = 0; f < NF; ++f) {
           const int i = wq0 + 32 * f + (lane & 31);
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
@@ -366,10 +386,10 @@ attn_fwd_kernel(const AttnArgs a) {
         }
       }
       // row max over the 32 keys (the lane pair l, l ^ 32 holds one query)
-      float bm[2];
+      float bm[NF];
       bool grow = false;
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
+      for (int f = 0; f < NF; ++f) {
         float x = max3_nan_ignoring(sacc[f][0], sacc[f][1], sacc[f][2]);
 #pragma unroll
         for (int e = 3; e < 15; e += 2) x = max3_nan_ignoring(x, sacc[f][e], sacc[f][e + 1]);
@@ -380,29 +400,34 @@ attn_fwd_kernel(const AttnArgs a) {
         grow = grow || (x > m_use[f] + thr);
       }
       if (__any(grow)) {
-        acc_wait_mfma(oacc);
+        if constexpr (kAccInAgpr) acc_wait_mfma<NF>(oacc);
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
+        for (int f = 0; f < NF; ++f) {
           const float mn = fmaxf(m_use[f], bm[f] + head);
           const float alpha = __builtin_amdgcn_exp2f((m_use[f] - mn) * c2);
           m_use[f] = mn;
           lsum[f] *= alpha;
 #pragma unroll
-          for (int n = 0; n < 4; ++n)
+          for (int n = 0; n < 4; ++n) {
+            if constexpr (kAccInAgpr) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              float x = oacc[f][n][e];
-              acc_scale(x, alpha);
-              oacc[f][n][e] = x;
+              for (int e = 0; e < 16; ++e) {
+                float x = oacc[f][n][e];
+                acc_scale(x, alpha);
+                oacc[f][n][e] = x;
+              }
+            } else {
+              oacc[f][n] *= alpha;
             }
+          }
         }
-        acc_wait_valu(oacc);
+        if constexpr (kAccInAgpr) acc_wait_valu<NF>(oacc);
       }
       // P^T = exp2(c2 (S^T - m)) in bf16; k-step p takes registers 8 p .. 8 p + 7
-      bf16x8_t pb[2][2];   // [p][f]
+      bf16x8_t pb[2][NF];   // [p][f]
       auto probs = [&](const int p) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
+        for (int f = 0; f < NF; ++f) {
           const float nm = -m_use[f] * c2;
           float ls = 0.0f;
 #pragma unroll
@@ -419,7 +444,7 @@ attn_fwd_kernel(const AttnArgs a) {
         for (int n = 0; n < 4; ++n) {
           const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(vl[p][n], vh[p][n], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-          for (int f = 0; f < 2; ++f)
+          for (int f = 0; f < NF; ++f)
             oacc[f][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[p][f], oacc[f][n], 0, 0, 0);
         }
       };
@@ -440,8 +465,9 @@ attn_fwd_kernel(const AttnArgs a) {
   // those starting at or before its last query. The leading ones that need
   // no mask (wholly below the diagonal and inside T) run without it. Every
   // wave takes part in every tile's loads and barrier.
-  const int n_w = wq0 >= a.T ? 0 : (a.causal ? min(nkv, (wq0 >> 6) + 1) : nkv);
-  const int n_full = min(n_w, a.causal ? min(a.T >> 6, wq0 >> 6) : (a.T >> 6));
+  // (tile t is mask-free for the wave when its last key 64 t + 63 <= wq0)
+  const int n_w = wq0 >= a.T ? 0 : (a.causal ? min(nkv, (wq0 + WR - 1) / kBKV + 1) : nkv);
+  const int n_full = min(n_w, a.causal ? min(a.T >> 6, (wq0 + 1) >> 6) : (a.T >> 6));
   if (nkv > 0) {
     dma(0, 0);
     FA_WAIT_DMA();
@@ -485,7 +511,7 @@ attn_fwd_kernel(const AttnArgs a) {
   // normalise and store: oacc[f][n] register e of lane l is column
   // 32 n + 8 (e / 4) + 4 (l / 32) + e % 4 of query wq0 + 32 f + l % 32
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+  for (int f = 0; f < NF; ++f) {
     const float lt = lsum[f] + __shfl_xor(lsum[f], 32);
     const int i = wq0 + 32 * f + (lane & 31);
     if (i < a.T) {
@@ -504,11 +530,15 @@ attn_fwd_kernel(const AttnArgs a) {
     }
   }
   if (SMAX) {
-    float mx = wave_max(fmaxf(m_all[0], m_all[1]));
+    float mx = m_all[0];
+#pragma unroll
+    for (int f = 1; f < NF; ++f) mx = fmaxf(mx, m_all[f]);
+    mx = wave_max(mx);
     if (lane == 0) red[wave] = mx;
     __syncthreads();
     if (tid == 0) {
-      mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      mx = red[0];
+      for (int w = 1; w < NW; ++w) mx = fmaxf(mx, red[w]);
       atomicMax(a.smax_enc + h, order_enc(mx));
     }
   }
@@ -533,12 +563,14 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.T <= 0 || a.H <= 0) return hipSuccess;
   const int grid = (a.T + kBQ - 1) / kBQ * a.H * a.B;
   const bool sm = a.smax_enc != nullptr;
+  // MHA: eight waves of 32 rows (two per SIMD); MLA, whose 192-wide query
+  // fragments do not fit two waves' registers: four waves of 64 rows
   if (a.d_s == 64) {
-    if (sm) attn_fwd_kernel<128, 64, true><<<grid, 256, 0, s>>>(a);
-    else attn_fwd_kernel<128, 64, false><<<grid, 256, 0, s>>>(a);
+    if (sm) attn_fwd_kernel<128, 64, true, 2><<<grid, 256, 0, s>>>(a);
+    else attn_fwd_kernel<128, 64, false, 2><<<grid, 256, 0, s>>>(a);
   } else {
-    if (sm) attn_fwd_kernel<128, 0, true><<<grid, 256, 0, s>>>(a);
-    else attn_fwd_kernel<128, 0, false><<<grid, 256, 0, s>>>(a);
+    if (sm) attn_fwd_kernel<128, 0, true, 1><<<grid, 512, 0, s>>>(a);
+    else attn_fwd_kernel<128, 0, false, 1><<<grid, 512, 0, s>>>(a);
   }
   return hipGetLastError();
 }
