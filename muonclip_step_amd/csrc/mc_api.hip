@@ -195,8 +195,8 @@ std::vector<Group> make_groups(const mc_matrix* mats, int32_t n) {
 
 struct GemmPlan { GemmTile tile; int tiles_m, tiles_n, splits, kt_per_split; size_t partial_bytes; };
 
-// Tile size and split-K for one batched product. 256x256 tiles when they give
-// at least two full waves of workgroups, else 128x128 (64x64 below 128 rows);
+// Tile size and split-K for one batched product. 256x256 tiles when they
+// cover at least half the CUs, else 128x128 (64x64 below 128 rows);
 // K is split only when the tiles alone cannot fill the chip, keeping every
 // split at least 8 k-stages long. Symmetric products count upper tiles only.
 GemmPlan plan_gemm(int64_t M, int64_t N, int ktiles, int batch, bool sym, bool reads_cin = false,
@@ -207,11 +207,11 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int ktiles, int batch, bool sym, bool r
     return (sym ? tm * (tm + 1) / 2 : tm * tn) * batch;
   };
   // 256 tiles run ~15-25% faster per tile than 128 (half the load bytes per
-  // flop) and win as soon as they cover half the CUs; an epilogue that also
-  // reads a matrix (the Poly step's b*A term) is long enough that two
-  // co-resident 128 tiles, overlapping one's epilogue with the other's loop,
-  // stay ahead until the 256 tiles fill the chip twice
-  const int need256 = reads_cin ? 2 * kCUs : kCUs / 2;
+  // flop) and win as soon as they cover half the CUs, the Poly step (whose
+  // epilogue also reads A) included since launches of at most one tile per
+  // CU run eight waves per tile (measured against 128 tiles: 4 x 2048^2
+  // chains 2.5 % faster, MLA layer step 5 % faster)
+  const int need256 = kCUs / 2;
   // (the 256 tile of the Poly step with a hi/lo output pair needs more
   // registers than a wave has, so that case stays on 128 tiles)
   if (M >= 256 && N >= 256 && count(256) >= need256 && !(reads_cin && pair_out)) p.tile = TILE_256;
