@@ -30,34 +30,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ inline float gamma_of(float s, float tau) {
-  // 1 when S is not > 0 (covers S <= 0 and NaN); tau/inf = 0 zeroes the head
-  return s > 0.0f ? fminf(1.0f, tau / s) : 1.0f;
-}
-
-// S_max that sets head h's gamma: its own, or with clip_global the largest
-// of its layer's heads (fmaxf ignores NaN heads; all NaN gives -inf -> gamma 1)
-__device__ inline float layer_s(const float* s_max, int slot, int h, int heads, int clip_global) {
-  if (!clip_global) return s_max[slot * heads + h];
-  float m = -INFINITY;
-  for (int k = 0; k < heads; ++k) m = fmaxf(m, s_max[slot * heads + k]);
-  return m;
-}
-
-__device__ inline float row_clip_scale(const ClipRule& c, int row, const float* s_max, int heads, float tau,
-                                       int clip_global) {
-  if (c.slot < 0 || !s_max || c.nseg == 0) return 1.0f;
-  const int h = row / c.period, o = row - h * c.period;
-  float expo = 0.0f;
-  if (c.nseg > 0 && o >= c.off[0] && o < c.off[0] + c.len[0]) expo = c.expo[0];
-  else if (c.nseg > 1 && o >= c.off[1] && o < c.off[1] + c.len[1]) expo = c.expo[1];
-  if (expo == 0.0f) return 1.0f;
-  const float g = gamma_of(layer_s(s_max, c.slot, h, heads, clip_global), tau);
-  if (expo == 0.5f) return sqrtf(g);
-  if (expo == 1.0f) return g;
-  return powf(g, expo);
-}
-
 template <typename M>
 __device__ inline int find_mat(const M* mats, int nmat, int blk) {
   int j = 0;

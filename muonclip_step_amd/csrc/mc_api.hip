@@ -271,13 +271,14 @@ WavePlan plan_wave(const Group& g, int nb) {
 }
 
 mc_status launch_gemm_planned(const GemmPlan& gp, GemmKind kind, bool split_pair, GemmArgs a, hipStream_t s,
-                              void* ws_base, size_t off_splitk, double flops) {
+                              void* ws_base, size_t off_splitk, double flops, const FusedUpd* upd = nullptr,
+                              double upd_bytes = 0.0) {
   a.tiles_m = gp.tiles_m; a.tiles_n = gp.tiles_n;
   a.splits = gp.splits; a.kt_per_split = gp.kt_per_split;
   a.partial = gp.splits > 1 ? (float*)((char*)ws_base + off_splitk) : nullptr;
   {
-    Prof pr(F_GEMM, s, flops, 0.0);
-    hipError_t e = launch_ns_gemm(gp.tile, kind, split_pair, a, s);
+    Prof pr(F_GEMM, s, flops, upd_bytes);
+    hipError_t e = launch_ns_gemm(gp.tile, kind, split_pair, a, s, upd);
     if (e != hipSuccess) return fail(MC_ERR_HIP, "ns_gemm launch: %s", hipGetErrorString(e));
   }
   if (gp.splits > 1) {
@@ -354,6 +355,38 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
     if (e != hipSuccess) return fail(MC_ERR_HIP, "norm_finalize launch: %s", hipGetErrorString(e));
   }
 
+  // The update rides on the last apply's epilogue (no O round trip through
+  // HBM, no separate launch) when every matrix of the wave allows it: a bf16
+  // weight with 8-element-aligned rows, no copy of O requested, an unsplit
+  // apply, and clip rules only on the first kMaxFusedClip matrices.
+  const float decay = (float)(1.0 - (double)hp.lr * (double)hp.weight_decay);
+  FusedUpd fu{};
+  double fu_bytes = 0.0;
+  {
+    bool fuse = hp.ns_steps >= 1 && w.apply.splits == 1 && nb <= kMaxFusedMats;
+    for (int slot = 0; slot < nb && fuse; ++slot) {
+      const mc_matrix& m = mats[ids[slot]];
+      const ClipRule c = clip_rule(m, s_max != nullptr);
+      fuse = m.w_dtype == MC_BF16 && !m.o_out && m.cols % 8 == 0 && m.ld % 8 == 0 && m.ld <= INT32_MAX &&
+             aligned(m.w, 16) && (slot < kMaxFusedClip || c.slot < 0 || c.nseg == 0);
+    }
+    if (fuse) {
+      fu.n = nb; fu.m = (int32_t)g.m; fu.nn = (int32_t)g.n;
+      fu.decay = decay;
+      fu.lr_rms = (float)((double)hp.lr * (double)hp.rms_scale * sqrt((double)g.n));
+      fu.s_max = s_max; fu.heads = heads; fu.tau = hp.tau; fu.clip_global = hp.clip_global;
+      fu.nclip = std::min(nb, kMaxFusedClip);
+      for (int slot = 0; slot < nb; ++slot) {
+        const mc_matrix& m = mats[ids[slot]];
+        if (slot < kMaxFusedClip) fu.clip[slot] = clip_rule(m, s_max != nullptr);
+        fu.ld[slot] = (int32_t)m.ld;
+        fu.trans[slot] = m.rows <= m.cols ? 0 : 1;
+        fu.w[slot] = m.w;
+        fu_bytes += (double)m.rows * m.cols * 4.0;   // read and write W
+      }
+    }
+  }
+
   // 2. Newton-Schulz iterations
   const double mm_ = (double)g.m, nn_ = (double)g.n;
   for (int it = 0; it < hp.ns_steps; ++it) {
@@ -405,15 +438,21 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
       a.ktiles = w.kt_apply;
       a.epi.alpha = 1.0f; a.epi.scale_pow = first ? 1 : 0; a.epi.scale = scale;
       a.epi.out_hi = x_nxt; a.epi.ld_hi = (int32_t)np; a.epi.bs_hi = mp * np;
+      const bool last = it + 1 == hp.ns_steps;
+      if (last && fu.n > 0 && gamma_once && *gamma_once) {
+        fu.gamma_out = *gamma_once; fu.gamma_slots = slots;
+        *gamma_once = nullptr;
+      }
       mc_status st = launch_gemm_planned(w.apply, GEMM_APPLY, false, a, s, ws, w.off_splitk,
-                                         2.0 * mm_ * mm_ * nn_ * nb);
+                                         2.0 * mm_ * mm_ * nn_ * nb, last && fu.n > 0 ? &fu : nullptr,
+                                         last ? fu_bytes : 0.0);
       if (st) return st;
     }
   }
+  if (fu.n > 0) return MC_OK;
 
   // 3. update + decay + QK-Clip rows
   uint16_t* x_final = X[hp.ns_steps & 1];   // O in [m][n]: W itself (wide) or W^T (tall)
-  const float decay = (float)(1.0 - (double)hp.lr * (double)hp.weight_decay);
   for (int b0 = 0; b0 < nb; b0 += kMaxBatchMats) {
     UpdArgs a{};
     a.decay = decay; a.s_max = s_max; a.heads = heads; a.tau = hp.tau; a.clip_global = hp.clip_global;

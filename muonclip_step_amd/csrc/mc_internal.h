@@ -76,7 +76,11 @@ int gemm_tile_dim(GemmTile t);
 // workgroups per matrix and split (symmetric products count upper tiles only)
 int gemm_tile_count(const GemmArgs& a, GemmKind kind);
 // split_pair: the product's result is also stored as a residual bf16 (lo) part
-hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const GemmArgs& a, hipStream_t s);
+struct FusedUpd;
+// upd (Apply only, may be NULL): the product is the step's last X' = O and
+// the epilogue applies the update to the weights instead of storing O
+hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const GemmArgs& a, hipStream_t s,
+                          const FusedUpd* upd = nullptr);
 hipError_t launch_splitk_reduce(const GemmArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- elementwise
@@ -109,6 +113,37 @@ struct ClipRule {
   float expo[2];
 };
 
+// QK-Clip factors (device): gamma_h = min(1, tau / S_max^h), 1 when S_max^h
+// is not > 0 (S <= 0 or NaN); a row's scale is gamma of its head raised to
+// the exponent of the segment holding the row (1 outside every segment).
+__device__ inline float gamma_of(float s, float tau) {
+  // 1 when S is not > 0 (covers S <= 0 and NaN); tau/inf = 0 zeroes the head
+  return s > 0.0f ? fminf(1.0f, tau / s) : 1.0f;
+}
+
+// S_max that sets head h's gamma: its own, or with clip_global the largest
+// of its layer's heads (fmaxf ignores NaN heads; all NaN gives -inf -> gamma 1)
+__device__ inline float layer_s(const float* s_max, int slot, int h, int heads, int clip_global) {
+  if (!clip_global) return s_max[slot * heads + h];
+  float m = -INFINITY;
+  for (int k = 0; k < heads; ++k) m = fmaxf(m, s_max[slot * heads + k]);
+  return m;
+}
+
+__device__ inline float row_clip_scale(const ClipRule& c, int row, const float* s_max, int heads, float tau,
+                                       int clip_global) {
+  if (c.slot < 0 || !s_max || c.nseg == 0) return 1.0f;
+  const int h = row / c.period, o = row - h * c.period;
+  float expo = 0.0f;
+  if (c.nseg > 0 && o >= c.off[0] && o < c.off[0] + c.len[0]) expo = c.expo[0];
+  else if (c.nseg > 1 && o >= c.off[1] && o < c.off[1] + c.len[1]) expo = c.expo[1];
+  if (expo == 0.0f) return 1.0f;
+  const float g = gamma_of(layer_s(s_max, c.slot, h, heads, clip_global), tau);
+  if (expo == 0.5f) return sqrtf(g);
+  if (expo == 1.0f) return g;
+  return powf(g, expo);
+}
+
 // W <- clip_row * ((1 - lr wd) W - lr * rms * O)
 struct UpdMat {
   void* w; int32_t w_bf16, vec;
@@ -122,6 +157,27 @@ struct UpdMat {
   ClipRule clip;
   int32_t tiles_c, block_start;
 };
+// The update fused into the last Newton-Schulz apply: batch entry b is the
+// weight W_b (bf16, row-major, ld[b]) whose O is that entry's product,
+// stored as W's shape (trans = 0: O is [m][n] = [rows][cols]) or transposed
+// (trans = 1: O is [m][n] = [cols][rows]). m, n are the unpadded extents; W's
+// columns are a multiple of 8 and its rows 16-byte aligned. Entries below
+// nclip carry their clip rule, the rest are never clipped. Block 0 also
+// writes gamma [gamma_slots][heads] when gamma_out is set.
+constexpr int kMaxFusedMats = 64, kMaxFusedClip = 8;
+struct FusedUpd {
+  int32_t n;                           // batch entries (0: not fused)
+  int32_t m, nn;                       // unpadded NS extents
+  float decay, lr_rms;
+  const float* s_max; int32_t heads; float tau; int32_t clip_global;
+  float* gamma_out; int32_t gamma_slots;
+  int32_t nclip;
+  ClipRule clip[kMaxFusedClip];
+  int32_t ld[kMaxFusedMats];
+  int32_t trans[kMaxFusedMats];
+  void* w[kMaxFusedMats];
+};
+
 // clip_global: gamma of a layer from the largest S_max of its heads
 struct UpdArgs {
   int32_t nmat; int32_t total_blocks;

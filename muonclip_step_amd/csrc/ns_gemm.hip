@@ -102,6 +102,7 @@ enum : int {
   E_SYM = 128,    // upper tiles only; off-diagonal tiles also stored mirrored
   E_LOMIR = 256,  // the lo part is read only transposed (by the Poly epilogue):
                   // off-diagonal tiles store it mirrored only
+  E_UPD = 512,    // last apply: the weight update with v as O, no store of v
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -113,7 +114,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <int BM, int BN, int NSTAGE, int EPI, int NNB = 0, int NW = 4>
 __global__ void __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
-ns_gemm_kernel(const GemmArgs p) {
+ns_gemm_kernel(const GemmArgs p, const FusedUpd u) {
   // NNB: the B operand is stored [k][n] (n contiguous) and staged in LDS the
   // same way, BN columns per k-row; its fragments are read with
   // ds_read_b64_tr_b16, whose 16-lane groups read four k-rows of 32 bytes.
@@ -534,7 +535,89 @@ ns_gemm_kernel(const GemmArgs p) {
     }
   };
 
+  // Fused update: W <- clip_row ((1 - lr wd) W - lr rms O), O the bf16 value
+  // staged in T, in the same arithmetic as the update kernel. W is row-major;
+  // its rows are the product's rows (trans = 0: read T as store_direct does,
+  // 8 consecutive columns of one row per lane) or its columns (trans = 1: T
+  // rows as store_trans reads them). Each group of up to 8 vectors issues all
+  // its W loads before the first store.
+  auto store_update = [&]() __attribute__((always_inline)) {
+    typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+    uint16_t* W = (uint16_t*)u.w[b];
+    const int ldw = u.ld[b];
+    const ClipRule cr = b < u.nclip ? u.clip[b] : ClipRule{-1, 1, 0, {0, 0}, {0, 0}, {0.0f, 0.0f}};
+    auto upd8 = [&](const u16x8_t& o, const u16x8_t& w, float sc) __attribute__((always_inline)) {
+      u16x8_t r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] = f32_to_bf16(fmaf(-u.lr_rms, bf16_to_f32(o[e]), bf16_to_f32(w[e]) * u.decay) * sc);
+      return r;
+    };
+    if (!u.trans[b]) {   // W is [m][nn]: row gi, columns gj .. gj + 7
+      const int t = lane & 15, gr = lane >> 4;
+      const int sq = t >> 2, sa = t & 3;
+      constexpr int NIB = WTM / 16, NV = (WTN / 32) * NIB, CHK = NV < 8 ? NV : 8;
+#pragma unroll
+      for (int c0 = 0; c0 < NV; c0 += CHK) {
+        u16x8_t wv[CHK];
+#pragma unroll
+        for (int q = 0; q < CHK; ++q) {
+          const int jb = (c0 + q) / NIB, ib = (c0 + q) % NIB;
+          const int gi = wi0 + ib * 16 + t, gj = wj0 + jb * 32 + gr * 8;
+          if (gi < u.m && gj < u.nn) wv[q] = *(const u16x8_t*)(W + (int64_t)gi * ldw + gj);
+        }
+#pragma unroll
+        for (int q = 0; q < CHK; ++q) {
+          const int jb = (c0 + q) / NIB, ib = (c0 + q) % NIB;
+          const int i0 = ib * 16, j0 = jb * 32 + gr * 8;
+          typedef short v4i16 __attribute__((ext_vector_type(4)));
+          typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+          const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)(tw + (j0 + sq) * TP + (i0 + 4 * sa) * 2));
+          const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)(tw + (j0 + 4 + sq) * TP + (i0 + 4 * sa) * 2));
+          const int gi = wi0 + i0 + t, gj = wj0 + j0;
+          if (gi < u.m && gj < u.nn) {
+            const u16x8_t o = {(uint16_t)x0[0], (uint16_t)x0[1], (uint16_t)x0[2], (uint16_t)x0[3],
+                               (uint16_t)x1[0], (uint16_t)x1[1], (uint16_t)x1[2], (uint16_t)x1[3]};
+            const float sc = row_clip_scale(cr, gi, u.s_max, u.heads, u.tau, u.clip_global);
+            *(u16x8_t*)(W + (int64_t)gi * ldw + gj) = upd8(o, wv[q], sc);
+          }
+        }
+      }
+    } else {             // W is [nn][m]: row gj, columns gi .. gi + 7
+      constexpr int CH = WTM / 8, RPS = 64 / CH, NV = WTN / RPS, CHK = NV < 8 ? NV : 8;
+      const int ch = lane % CH, rr = lane / CH;
+      const int gi = wi0 + ch * 8;
+#pragma unroll
+      for (int c0 = 0; c0 < NV; c0 += CHK) {
+        u16x8_t wv[CHK];
+#pragma unroll
+        for (int q = 0; q < CHK; ++q) {
+          const int gj = wj0 + (c0 + q) * RPS + rr;
+          if (gj < u.nn && gi < u.m) wv[q] = *(const u16x8_t*)(W + (int64_t)gj * ldw + gi);
+        }
+#pragma unroll
+        for (int q = 0; q < CHK; ++q) {
+          const int jr = (c0 + q) * RPS + rr, gj = wj0 + jr;
+          if (gj < u.nn && gi < u.m) {
+            const u16x8_t o = *(const u16x8_t*)(tw + jr * TP + ch * 16);
+            const float sc = row_clip_scale(cr, gj, u.s_max, u.heads, u.tau, u.clip_global);
+            *(u16x8_t*)(W + (int64_t)gj * ldw + gi) = upd8(o, wv[q], sc);
+          }
+        }
+      }
+    }
+  };
+
   stage(false);
+  if (EPI & E_UPD) {
+    if (u.gamma_out && blockIdx.x == 0)   // the step's gamma output, from the same s_max
+      for (int i = tid; i < u.gamma_slots * u.heads; i += 64 * NW)
+        u.gamma_out[i] = gamma_of(layer_s(u.s_max, i / u.heads, i % u.heads, u.heads, u.clip_global), u.tau);
+    MC_WAIT_LGKM_ALL();
+    store_update();
+    return;
+  }
   if (EPI & E_HI) store_direct(ohi, ld_hi);
   if ((EPI & E_HI) && mirror) store_trans(ohi, ld_hi);
   if (EPI & E_LO) {
@@ -568,14 +651,14 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs p) {
 // 2048^2 chains, 1.2 % slower on the 1155 expert matrices).
 constexpr int kEightWaveMaxTiles = 256;
 template <int EPI, int NNB = 0>
-static void launch_epi(GemmTile tile, const GemmArgs& a, int total, hipStream_t s) {
+static void launch_epi(GemmTile tile, const GemmArgs& a, int total, hipStream_t s, const FusedUpd& u) {
   switch (tile) {
     case TILE_256:
-      if (total <= kEightWaveMaxTiles) ns_gemm_kernel<256, 256, 2, EPI, NNB, 8><<<total, 512, 0, s>>>(a);
-      else ns_gemm_kernel<256, 256, 2, EPI, NNB, 4><<<total, 256, 0, s>>>(a);
+      if (total <= kEightWaveMaxTiles) ns_gemm_kernel<256, 256, 2, EPI, NNB, 8><<<total, 512, 0, s>>>(a, u);
+      else ns_gemm_kernel<256, 256, 2, EPI, NNB, 4><<<total, 256, 0, s>>>(a, u);
       break;
-    case TILE_128: ns_gemm_kernel<128, 128, 2, EPI, NNB><<<total, 256, 0, s>>>(a); break;
-    default:       ns_gemm_kernel<64, 64, 2, EPI, NNB><<<total, 256, 0, s>>>(a); break;
+    case TILE_128: ns_gemm_kernel<128, 128, 2, EPI, NNB><<<total, 256, 0, s>>>(a, u); break;
+    default:       ns_gemm_kernel<64, 64, 2, EPI, NNB><<<total, 256, 0, s>>>(a, u); break;
   }
 }
 
@@ -584,9 +667,16 @@ int gemm_tile_count(const GemmArgs& a, GemmKind kind) {
   return sym ? a.tiles_m * (a.tiles_m + 1) / 2 : a.tiles_m * a.tiles_n;
 }
 
-hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const GemmArgs& a, hipStream_t s,
+                          const FusedUpd* upd) {
   const int total = gemm_tile_count(a, kind) * a.splits * a.batch;
   if (total <= 0) return hipSuccess;
+  static const FusedUpd none{};
+  const bool fused = upd && upd->n > 0;
+  // the fused update covers the whole batch, unsplit, of an apply
+  if (fused && (kind != GEMM_APPLY || a.splits > 1 || upd->n != a.batch || a.batch > kMaxFusedMats))
+    return hipErrorInvalidValue;
+  const FusedUpd& u = fused ? *upd : none;
   // the epilogue works on 32x32 fragments and moves 16-byte vectors:
   // extents must be multiples of 32; leading dimensions and batch strides
   // multiples of 8 elements and bases 16-byte aligned
@@ -598,16 +688,18 @@ hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const G
       bad(e.out_hi, e.ld_hi, e.bs_hi) || bad(e.out_lo, e.ld_lo, e.bs_lo))
     return hipErrorInvalidValue;
   if (a.splits > 1) {
-    launch_epi<E_PART>(tile, a, total, s);
+    launch_epi<E_PART>(tile, a, total, s, u);
   } else if (kind == GEMM_GRAM) {
     // without operand pairs A_lo only feeds the Poly epilogue's transposed read
-    if (split_pair) launch_epi<E_SYM | E_HI | E_LO>(tile, a, total, s);
-    else launch_epi<E_SYM | E_HI | E_LO | E_LOMIR>(tile, a, total, s);
+    if (split_pair) launch_epi<E_SYM | E_HI | E_LO>(tile, a, total, s, u);
+    else launch_epi<E_SYM | E_HI | E_LO | E_LOMIR>(tile, a, total, s, u);
   } else if (kind == GEMM_POLY) {
-    if (split_pair) launch_epi<E_SYM | E_CIN | E_DIAG | E_HI | E_LO>(tile, a, total, s);
-    else launch_epi<E_SYM | E_CIN | E_DIAG | E_HI>(tile, a, total, s);
+    if (split_pair) launch_epi<E_SYM | E_CIN | E_DIAG | E_HI | E_LO>(tile, a, total, s, u);
+    else launch_epi<E_SYM | E_CIN | E_DIAG | E_HI>(tile, a, total, s, u);
+  } else if (fused) {
+    launch_epi<E_UPD, 1>(tile, a, total, s, u);   // last apply with the weight update
   } else {
-    launch_epi<E_HI, 1>(tile, a, total, s);   // apply: B = X stored [k][n]
+    launch_epi<E_HI, 1>(tile, a, total, s, u);   // apply: B = X stored [k][n]
   }
   return hipGetLastError();
 }

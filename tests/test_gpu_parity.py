@@ -368,3 +368,73 @@ def test_gamma_out_without_matrices_and_with_two_lanes():
     mc.muonclip_step(descs, hp, s_max=s4, slots=1, heads=4, gamma_out=g1, workspace=ws)
     torch.cuda.synchronize()
     assert np.allclose(host64(g1), want[:4], rtol=1e-6, atol=0)
+
+
+# ----------------------------------------------------------------- fused update
+
+def _step_weights(states, hp, s_max, heads, with_o, ws_mode="full"):
+    descs = [s.desc(with_o=with_o) for s in states]
+    ws = torch.empty(mc.workspace_size(descs, hp, minimal=(ws_mode == "min")), dtype=torch.uint8, device="cuda")
+    gam = torch.full((s_max.numel(),), -7.0, dtype=torch.float32, device="cuda") if s_max is not None else None
+    mc.muonclip_step(descs, hp, s_max=s_max, slots=1 if s_max is not None else 0, heads=heads,
+                     gamma_out=gam, workspace=ws)
+    torch.cuda.synchronize()
+    return [s.w.cpu().clone() for s in states], (gam.cpu() if gam is not None else None)
+
+
+def _fresh(states):
+    for s in states:
+        s.w.copy_(dev_tensor(s.w0, s.spec.w_dtype))
+        s.g.copy_(dev_tensor(s.g0, "f32"))
+        s.m.copy_(dev_tensor(s.m0, "f32"))
+
+
+@pytest.mark.parametrize("case", ["mha_layer", "ragged_tall_wide", "many_clipped", "global_clip"])
+def test_update_fused_into_last_apply_is_bit_identical(case):
+    """Without an O output the update runs in the last Newton-Schulz apply's
+    epilogue. It must give bit for bit the weights and gamma of the separate
+    update kernel (which the oracle parity tests check, since they request
+    O): the MHA layer's four 2048^2 matrices with clipped W_q, W_k; a tall
+    and a wide matrix of one ragged shape group with padded rows, clipped;
+    eleven clipped matrices (past the fused path's clip table: the update
+    kernel runs); the global-gamma variant."""
+    print("fused update case", case, flush=True)
+    rng = np.random.default_rng(sum(map(ord, case)))
+    heads = 4
+    kw = {}
+    if case == "mha_layer":
+        cfg = wl.config(2)
+        states = load_config_states(cfg)
+        heads = cfg.attn.H
+    else:
+        if case == "ragged_tall_wide":
+            shapes = [(200, 136), (136, 200)]
+        elif case == "many_clipped":
+            shapes = [(96, 64)] * 11
+        else:
+            shapes = [(128, 256), (256, 128)]
+            kw = dict(clip_global=1)
+        states = []
+        for r, c in shapes:
+            period = r // heads
+            spec = wl.MatrixSpec("m", r, c, clip_slot=0, period=period, segments=((0, period // 2, 0.5), (period // 2, 8, 1.0)))
+            w = (rng.standard_normal((r, c)) * 0.02).astype(np.float32)
+            g = (rng.standard_normal((r, c)) * 1e-3).astype(np.float32)
+            m = (rng.standard_normal((r, c)) * 1e-3).astype(np.float32)
+            states.append(State(spec, w, g, m, ld_pad=8))
+    s_max = torch.tensor(rng.uniform(20.0, 400.0, heads), dtype=torch.float32, device="cuda")
+    hp = hp_for(wl.config(2), **kw)
+    # (the smallest workspace runs one matrix per wave, with other tiles and
+    # split-K, so each workspace size is compared with itself)
+    for ws_mode in ("full", "min"):
+        _fresh(states)
+        w_sep, g_sep = _step_weights(states, hp, s_max, heads, with_o=True, ws_mode=ws_mode)
+        _fresh(states)
+        w_fus, g_fus = _step_weights(states, hp, s_max, heads, with_o=False, ws_mode=ws_mode)
+        for a, b in zip(w_sep, w_fus):
+            assert torch.equal(a, b)
+        assert torch.equal(g_sep, g_fus)
+    assert torch.all(g_sep <= 1.0) and torch.any(g_sep < 1.0)
+    # and the padding past each row stayed untouched
+    for s in states:
+        assert torch.all(s.w_full[:, s.spec.cols:].cpu() == 0)
