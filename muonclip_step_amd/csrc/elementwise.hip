@@ -15,6 +15,9 @@
 //                    "Scaling up Muon"), with the post-update QK-Clip row scale
 //                    s_row = gamma_h^expo (Kimi K2 essay, MHA equations and the
 //                    MLA table; gamma_h = min(1, tau / S_max^h)) fused in.
+//                    The step normally applies it in the last Newton-Schulz
+//                    apply's epilogue; this kernel serves the waves that
+//                    cannot fuse it (fp32 W, an O copy, unaligned rows).
 //  gamma_kernel      gamma_h for every (layer, head); with clip_global one
 //                    gamma per layer from its largest S_max (K2 report 2.1).
 //  clip_apply_kernel the QK-Clip rescale alone on an existing weight.

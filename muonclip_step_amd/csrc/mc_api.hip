@@ -8,7 +8,8 @@
 //   5 x { Gram  A = s0^2 X X^T          -> A as a bf16 pair A_hi + A_lo
 //         Poly  P = a I + b A + c A A   -> P_hi (+ P_lo if m < 1024)
 //         Apply X' = s0 P X             -> X' (ping-pong; last step: O) }
-//   update_kernel     W <- clip_row ((1 - lr wd) W - lr rms sqrt(max) O)
+//   W <- clip_row ((1 - lr wd) W - lr rms sqrt(max) O): in the last Apply's
+//   epilogue, or by update_kernel for waves that cannot fuse it
 // (s0 = s on the first step, 1 after). The apply is the quintic step of the
 // Notes on Muon blog, "Newton-Schulz", written as X' = (aI + bA + cA^2) X.
 // Operands are bf16, accumulation and every epilogue fp32; the Poly epilogue
