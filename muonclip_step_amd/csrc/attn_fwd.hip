@@ -161,7 +161,14 @@ attn_fwd_kernel(const AttnArgs a) {
   // in place through asm; the eight-wave kernel is compiled with every MFMA
   // writing VGPRs (its whole state fits 256 VGPRs) and rescales with VALU.
   constexpr bool kAccInAgpr = NF == 2;
+  // Eight-wave MLA (192-wide queries): to fit 256 registers a half's K
+  // fragments go through a ring of KSL = KS / 2 slots (the second half of the
+  // reads is issued under the first half's MFMAs) and the two value k-steps
+  // share one fragment buffer (the second is read after the first one's
+  // MFMAs issued).
+  constexpr bool kLean = DS > 0 && NF == 1;
   constexpr int D = DK + DS, KS = D / 16;
+  constexpr int KSL = kLean ? KS / 2 : KS, NVB = kLean ? 1 : 2;   // K slots, value buffers
   // one LDS stage: K content rows [64][256 B], rotary rows [64][128 B], V rows [64][256 B]
   constexpr int KC_BYTES = kBKV * 256, KR_BYTES = kBKV * DS * 2, VT_BYTES = kBKV * kDV * 2;
   constexpr int STAGE = KC_BYTES + KR_BYTES + VT_BYTES;
@@ -336,23 +343,24 @@ attn_fwd_kernel(const AttnArgs a) {
   auto tile = [&](const int kv0, auto mask_tag, auto buf_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr int BUF = decltype(buf_tag)::value;
-    u32x4_t kf[KS];
-    v4i16_t vl[2][4], vh[2][4];
-    auto read_k = [&](auto g_) {
-      constexpr int g = decltype(g_)::value;
-      static_for<KS>([&](auto s_) {
-        constexpr int s = decltype(s_)::value;
-        constexpr int off = BUF * STAGE + g * (s < 8 ? 32 * 256 : 32 * 128);
-        lds_read_b128<off>(kf[s], kq[s]);
-      });
+    u32x4_t kf[KSL];
+    v4i16_t vl[NVB][4], vh[NVB][4];
+    // K fragment s of half g into ring slot s % KSL
+    auto read_k1 = [&](auto g_, auto s_) {
+      constexpr int g = decltype(g_)::value, s = decltype(s_)::value;
+      constexpr int off = BUF * STAGE + g * (s < 8 ? 32 * 256 : 32 * 128);
+      lds_read_b128<off>(kf[s % KSL], kq[s]);
+    };
+    auto read_k = [&](auto g_) {   // the first KSL fragments of half g
+      static_for<KSL>([&](auto s_) { read_k1(g_, s_); });
     };
     auto read_v = [&](auto g_, auto p_) {
       constexpr int g = decltype(g_)::value, p = decltype(p_)::value;
       static_for<4>([&](auto n_) {
         constexpr int n = decltype(n_)::value;
         constexpr int off = BUF * STAGE + (32 * g + 16 * p) * (kDV * 2);
-        lds_read_tr<off>(vl[p][n], vq[n]);
-        lds_read_tr<off + 8 * kDV * 2>(vh[p][n], vq[n]);
+        lds_read_tr<off>(vl[p % NVB][n], vq[n]);
+        lds_read_tr<off + 8 * kDV * 2>(vh[p % NVB][n], vq[n]);
       });
     };
     read_k(std::integral_constant<int, 0>{});
@@ -361,16 +369,20 @@ attn_fwd_kernel(const AttnArgs a) {
       // sacc[f] register e of lane l: key kv0 + 32 g + 8 (e / 4) + 4 (l / 32)
       // + e % 4, query wq0 + 32 f + l % 32
       f32x16_t sacc[NF];
-      // outstanding before the waits: the KS K reads of this half (issued
-      // last), nothing else
+      // outstanding before the first wait: the KSL K reads of this half
+      // (issued last), nothing else; fragment s + KSL is read into the slot
+      // fragment s leaves, right after its MFMAs issue (they take their
+      // operands at issue). Reads issued after fragment s's when it is
+      // waited for: KSL + min(s, KS - KSL) - s - 1.
       static_for<KS>([&](auto s_) {
         constexpr int s = decltype(s_)::value;
-        lgkm_wait<KS - 1 - s>(kf[s]);
+        lgkm_wait<KSL + (s < KS - KSL ? s : KS - KSL) - s - 1>(kf[s % KSL]);
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-          if (s == 0) mfma_s_first(sacc[f], kf[s], qf[f][s]);
-          else mfma_s(sacc[f], kf[s], qf[f][s]);
+          if (s == 0) mfma_s_first(sacc[f], kf[s % KSL], qf[f][s]);
+          else mfma_s(sacc[f], kf[s % KSL], qf[f][s]);
         }
+        if constexpr (s + KSL < KS) read_k1(g_, std::integral_constant<int, s + KSL>{});
       });
       s_wait_logits<NF>(sacc);
       read_v(g_, std::integral_constant<int, 0>{});
@@ -442,21 +454,28 @@ attn_fwd_kernel(const AttnArgs a) {
       auto pv_step = [&](const int p) {
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
-          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(vl[p][n], vh[p][n], 0, 1, 2, 3, 4, 5, 6, 7));
+          const bf16x8_t vf =
+              __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(vl[p % NVB][n], vh[p % NVB][n], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int f = 0; f < NF; ++f)
             oacc[f][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[p][f], oacc[f][n], 0, 0, 0);
         }
       };
       probs(0);
-      read_v(g_, std::integral_constant<int, 1>{});
-      // outstanding: the 8 reads of p = 1 (those of p = 0 are older)
-      lgkm_wait<8>(vl[0], vh[0]);
-      pv_step(0);
+      if constexpr (NVB == 2) {
+        read_v(g_, std::integral_constant<int, 1>{});
+        // outstanding: the 8 reads of p = 1 (those of p = 0 are older)
+        lgkm_wait<8>(vl[0], vh[0]);
+        pv_step(0);
+      } else {
+        lgkm_wait<0>(vl[0], vh[0]);
+        pv_step(0);
+        read_v(g_, std::integral_constant<int, 1>{});   // into the buffer p = 0 just used
+      }
       probs(1);
       if (g == 0) read_k(std::integral_constant<int, 1>{});
-      // outstanding: (the next half's KS K reads, issued after) the reads of p = 1
-      lgkm_wait<g == 0 ? KS : 0>(vl[1], vh[1]);
+      // outstanding: (the next half's KSL K reads, issued after) the reads of p = 1
+      lgkm_wait<g == 0 ? KSL : 0>(vl[1 % NVB], vh[1 % NVB]);
       pv_step(1);
     });
   };
@@ -566,8 +585,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   // MHA: eight waves of 32 rows (two per SIMD); MLA, whose 192-wide query
   // fragments do not fit two waves' registers: four waves of 64 rows
   if (a.d_s == 64) {
-    if (sm) attn_fwd_kernel<128, 64, true, 2><<<grid, 256, 0, s>>>(a);
-    else attn_fwd_kernel<128, 64, false, 2><<<grid, 256, 0, s>>>(a);
+    if (sm) attn_fwd_kernel<128, 64, true, 1><<<grid, 512, 0, s>>>(a);
+    else attn_fwd_kernel<128, 64, false, 1><<<grid, 512, 0, s>>>(a);
   } else {
     if (sm) attn_fwd_kernel<128, 0, true, 1><<<grid, 512, 0, s>>>(a);
     else attn_fwd_kernel<128, 0, false, 1><<<grid, 512, 0, s>>>(a);
