@@ -8,11 +8,11 @@
 // keys are [k^C_h | k^R] with the rotary key shared by every head; the value
 // width is 128.
 //
-// Layout of the work. A block owns 256 query rows of one (sample, head):
-// MHA runs eight waves of 32 rows (two waves per SIMD), MLA four waves of 64
-// rows. Each wave keeps its rows in registers as MFMA B-fragments for the
-// whole kernel and walks the key axis in tiles of 64
-// keys, which pass through a double-buffered LDS ring (K rows XOR-swizzled
+// Layout of the work. A block owns 256 query rows of one (sample, head) in
+// eight waves of 32 rows (two waves per SIMD). Each wave keeps its rows in
+// registers as an MFMA B-fragment for the whole kernel and walks the key axis
+// in tiles of 64 keys, which pass through a double-buffered LDS ring (K rows
+// XOR-swizzled
 // for 16-byte fragment reads, V rows swizzled for transposing reads). Both
 // products run transposed, with v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T   (A = K from LDS, B = Q from registers)
@@ -90,8 +90,7 @@ __device__ __forceinline__ void lgkm_wait(v4i16_t (&l)[4], v4i16_t (&h)[4]) {
 
 // S^T = K Q^T k-step as inline MFMAs writing VGPRs (the softmax reads the
 // logits with VALU instructions; the compiler's own MFMAs accumulate the
-// output, in AGPRs in the four-wave kernel). Hazards the
-// compiler cannot see: a VALU write of an operand needs two wait states
+// output). Hazards the compiler cannot see: a VALU write of an operand needs two wait states
 // before the MFMA reads it (the leading s_nop 1), and VALU reads of the
 // result wait for s_wait_logits below.
 __device__ __forceinline__ void mfma_s_first(f32x16_t& acc, const u32x4_t& a, const bf16x8_t& b) {
@@ -102,35 +101,8 @@ __device__ __forceinline__ void mfma_s(f32x16_t& acc, const u32x4_t& a, const bf
 }
 // 24 wait states between the last logit MFMA and the first VALU read of its
 // result (more than the 8-pass MFMA's requirement)
-template <int NF>
-__device__ __forceinline__ void s_wait_logits(f32x16_t (&a)[NF]) {
-  if constexpr (NF == 2) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a[0]), "+v"(a[1]));
-  else asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a[0]));
-}
-
-// Four-wave kernel: rescale of one output accumulator in place in its AGPR.
-// The compiler only sees an AGPR operand, so the accumulators never leave
-// the AGPRs (VALU arithmetic on them would make it keep copies in VGPRs
-// across the loop).
-// acc_wait_mfma separates the MFMAs that last wrote the accumulators from
-// these reads (more wait states than an 8-pass MFMA needs); acc_wait_valu
-// separates the writes from the next MFMA that accumulates into them.
-__device__ __forceinline__ void acc_scale(float& x, float s) {
-  float t;
-  asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-               : "+a"(x), "=&v"(t) : "v"(s));
-}
-template <int NF>
-__device__ __forceinline__ void acc_wait_mfma(f32x16_t (&o)[NF][4]) {
-#pragma unroll
-  for (int f = 0; f < NF; ++f)
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o[f][0]), "+a"(o[f][1]), "+a"(o[f][2]), "+a"(o[f][3]));
-}
-template <int NF>
-__device__ __forceinline__ void acc_wait_valu(f32x16_t (&o)[NF][4]) {
-#pragma unroll
-  for (int f = 0; f < NF; ++f)
-    asm volatile("s_nop 4" : "+a"(o[f][0]), "+a"(o[f][1]), "+a"(o[f][2]), "+a"(o[f][3]));
+__device__ __forceinline__ void s_wait_logits(f32x16_t& a) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a));
 }
 
 // max of three numbers ignoring quiet NaNs (IEEE maxNum, as fmaxf), in one
@@ -147,26 +119,22 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
-// NF: query fragments (of 32 rows) per wave. NF = 2: four waves of 64 rows,
-// one wave per SIMD; NF = 1: eight waves of 32 rows, two waves per SIMD,
-// which hide each other's softmax arithmetic and LDS latency behind their
-// MFMAs (the LDS delivers about 200 bytes per clock per CU to two waves
-// per SIMD, enough for the doubled fragment traffic).
-template <int DK, int DS, bool SMAX, int NF>
-__global__ void __launch_bounds__(256 * 2 / NF, 1) __attribute__((amdgpu_waves_per_eu(2 / NF, 2 / NF)))
+// Eight waves of 32 query rows (one MFMA fragment, NF = 1), two waves per
+// SIMD, which hide each other's softmax arithmetic and LDS latency behind
+// their MFMAs (the LDS delivers about 200 bytes per clock per CU to two waves
+// per SIMD, enough for the fragment traffic). The whole state fits 256
+// VGPRs: every MFMA writes VGPRs and the rescale is plain VALU arithmetic.
+template <int DK, int DS, bool SMAX>
+__global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(const AttnArgs a) {
-  static_assert(DK == 128 && (DS == 0 || DS == 64) && (NF == 1 || NF == 2), "head widths");
-  constexpr int NW = 8 / NF, WR = 32 * NF;   // waves per block, query rows per wave
-  // With four waves the output accumulators live in AGPRs and are rescaled
-  // in place through asm; the eight-wave kernel is compiled with every MFMA
-  // writing VGPRs (its whole state fits 256 VGPRs) and rescales with VALU.
-  constexpr bool kAccInAgpr = NF == 2;
-  // Eight-wave MLA (192-wide queries): to fit 256 registers a half's K
-  // fragments go through a ring of KSL = KS / 2 slots (the second half of the
-  // reads is issued under the first half's MFMAs) and the two value k-steps
-  // share one fragment buffer (the second is read after the first one's
-  // MFMAs issued).
-  constexpr bool kLean = DS > 0 && NF == 1;
+  static_assert(DK == 128 && (DS == 0 || DS == 64), "head widths");
+  constexpr int NF = 1;                      // query fragments per wave
+  constexpr int NW = 8, WR = 32;             // waves per block, query rows per wave
+  // MLA (192-wide queries): to fit 256 registers a half's K fragments go
+  // through a ring of KSL = KS / 2 slots (the second half of the reads is
+  // issued under the first half's MFMAs) and the two value k-steps share one
+  // fragment buffer (the second is read after the first one's MFMAs issued).
+  constexpr bool kLean = DS > 0;
   constexpr int D = DK + DS, KS = D / 16;
   constexpr int KSL = kLean ? KS / 2 : KS, NVB = kLean ? 1 : 2;   // K slots, value buffers
   // one LDS stage: K content rows [64][256 B], rotary rows [64][128 B], V rows [64][256 B]
@@ -384,7 +352,7 @@ attn_fwd_kernel(const AttnArgs a) {
         }
         if constexpr (s + KSL < KS) read_k1(g_, std::integral_constant<int, s + KSL>{});
       });
-      s_wait_logits<NF>(sacc);
+      s_wait_logits(sacc[0]);
       read_v(g_, std::integral_constant<int, 0>{});
       if (MASK) {
 #pragma unroll
@@ -412,7 +380,6 @@ attn_fwd_kernel(const AttnArgs a) {
         grow = grow || (x > m_use[f] + thr);
       }
       if (__any(grow)) {
-        if constexpr (kAccInAgpr) acc_wait_mfma<NF>(oacc);
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
           const float mn = fmaxf(m_use[f], bm[f] + head);
@@ -420,20 +387,8 @@ attn_fwd_kernel(const AttnArgs a) {
           m_use[f] = mn;
           lsum[f] *= alpha;
 #pragma unroll
-          for (int n = 0; n < 4; ++n) {
-            if constexpr (kAccInAgpr) {
-#pragma unroll
-              for (int e = 0; e < 16; ++e) {
-                float x = oacc[f][n][e];
-                acc_scale(x, alpha);
-                oacc[f][n][e] = x;
-              }
-            } else {
-              oacc[f][n] *= alpha;
-            }
-          }
+          for (int n = 0; n < 4; ++n) oacc[f][n] *= alpha;
         }
-        if constexpr (kAccInAgpr) acc_wait_valu<NF>(oacc);
       }
       // P^T = exp2(c2 (S^T - m)) in bf16; k-step p takes registers 8 p .. 8 p + 7
       bf16x8_t pb[2][NF];   // [p][f]
@@ -582,14 +537,12 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.T <= 0 || a.H <= 0) return hipSuccess;
   const int grid = (a.T + kBQ - 1) / kBQ * a.H * a.B;
   const bool sm = a.smax_enc != nullptr;
-  // MHA: eight waves of 32 rows (two per SIMD); MLA, whose 192-wide query
-  // fragments do not fit two waves' registers: four waves of 64 rows
   if (a.d_s == 64) {
-    if (sm) attn_fwd_kernel<128, 64, true, 1><<<grid, 512, 0, s>>>(a);
-    else attn_fwd_kernel<128, 64, false, 1><<<grid, 512, 0, s>>>(a);
+    if (sm) attn_fwd_kernel<128, 64, true><<<grid, 512, 0, s>>>(a);
+    else attn_fwd_kernel<128, 64, false><<<grid, 512, 0, s>>>(a);
   } else {
-    if (sm) attn_fwd_kernel<128, 0, true, 1><<<grid, 512, 0, s>>>(a);
-    else attn_fwd_kernel<128, 0, false, 1><<<grid, 512, 0, s>>>(a);
+    if (sm) attn_fwd_kernel<128, 0, true><<<grid, 512, 0, s>>>(a);
+    else attn_fwd_kernel<128, 0, false><<<grid, 512, 0, s>>>(a);
   }
   return hipGetLastError();
 }
