@@ -242,6 +242,10 @@ struct WavePlan {
   int64_t mom_blocks;          // momentum blocks per matrix
   GemmPlan gram, poly, apply;
   int kt_gram, kt_poly, kt_apply;
+  // the Gram hands A to the Poly epilogue as fp32 in fragment order (off_alo)
+  // instead of the bf16 residual A_lo: groups without operand pairs whose two
+  // symmetric products run unsplit on the same tiles
+  bool frag;
 };
 
 WavePlan plan_wave(const Group& g, int nb) {
@@ -250,21 +254,22 @@ WavePlan plan_wave(const Group& g, int nb) {
   const size_t mp = (size_t)g.mp, np = (size_t)g.np;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
-  w.off_x0 = take(nb * mp * np * 2);
-  w.off_x1 = take(nb * mp * np * 2);
-  w.off_ahi = take(nb * mp * mp * 2);
-  w.off_alo = take(nb * mp * mp * 2);
-  w.off_phi = take(nb * mp * mp * 2);
-  w.off_plo = g.split ? take(nb * mp * mp * 2) : 0;
-  w.mom_blocks = (int64_t)(mp / 64) * (int64_t)(np / 64);
-  w.off_part = take(nb * (size_t)w.mom_blocks * 4);
-  w.off_scale = take(nb * 4);
   w.kt_gram = (int)(np / kGemmBK);
   w.kt_poly = (int)(mp / kGemmBK) * (g.split ? 3 : 1);
   w.kt_apply = (int)(mp / kGemmBK) * (g.split ? 2 : 1);
   w.gram = plan_gemm(g.mp, g.mp, w.kt_gram, nb, true);
   w.poly = plan_gemm(g.mp, g.mp, w.kt_poly, nb, true, true, g.split);
   w.apply = plan_gemm(g.mp, g.np, w.kt_apply, nb, false);
+  w.frag = !g.split && w.gram.tile == w.poly.tile && w.gram.splits == 1 && w.poly.splits == 1;
+  w.off_x0 = take(nb * mp * np * 2);
+  w.off_x1 = take(nb * mp * np * 2);
+  w.off_ahi = take(nb * mp * mp * 2);
+  w.off_alo = take(nb * mp * mp * (w.frag ? 4 : 2));
+  w.off_phi = take(nb * mp * mp * 2);
+  w.off_plo = g.split ? take(nb * mp * mp * 2) : 0;
+  w.mom_blocks = (int64_t)(mp / 64) * (int64_t)(np / 64);
+  w.off_part = take(nb * (size_t)w.mom_blocks * 4);
+  w.off_scale = take(nb * 4);
   const size_t sk = std::max(w.gram.partial_bytes, std::max(w.poly.partial_bytes, w.apply.partial_bytes));
   w.off_splitk = sk ? take(sk) : 0;
   w.bytes = off;
@@ -402,7 +407,11 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
       a.nseg = 1; a.seg[0] = {x_cur, x_cur, w.kt_gram}; a.ktiles = w.kt_gram;
       a.epi.alpha = 1.0f; a.epi.scale_pow = first ? 2 : 0; a.epi.scale = scale;
       a.epi.out_hi = Ahi; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
-      a.epi.out_lo = Alo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp;
+      if (w.frag) {
+        a.epi.frag_out = (float*)Alo; a.epi.frag_nb = (int32_t)(mp / 32); a.epi.bs_frag = mp * mp;
+      } else {
+        a.epi.out_lo = Alo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp;
+      }
       mc_status st = launch_gemm_planned(w.gram, GEMM_GRAM, g.split, a, s, ws, w.off_splitk,
                                          2.0 * mm_ * mm_ * nn_ * nb);
       if (st) return st;
@@ -421,7 +430,11 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
       }
       a.ktiles = w.kt_poly;
       a.epi.alpha = hp.ns_c; a.epi.beta = hp.ns_b; a.epi.diag = hp.ns_a;
-      a.epi.cin_hi = Ahi; a.epi.cin_lo = Alo; a.epi.ld_cin = (int32_t)mp; a.epi.bs_cin = mp * mp;
+      if (w.frag) {
+        a.epi.frag_in = (const float*)Alo; a.epi.frag_nb = (int32_t)(mp / 32); a.epi.bs_frag = mp * mp;
+      } else {
+        a.epi.cin_hi = Ahi; a.epi.cin_lo = Alo; a.epi.ld_cin = (int32_t)mp; a.epi.bs_cin = mp * mp;
+      }
       a.epi.out_hi = Phi; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
       if (Plo) { a.epi.out_lo = Plo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp; }
       mc_status st = launch_gemm_planned(w.poly, GEMM_POLY, g.split, a, s, ws, w.off_splitk,

@@ -50,6 +50,12 @@ struct GemmEpi {
   float diag;
   uint16_t* out_hi; int32_t ld_hi; int64_t bs_hi;
   uint16_t* out_lo; int32_t ld_lo; int64_t bs_lo;
+  // fp32 v in MFMA fragment order, for a later epilogue whose tiles cover the
+  // same 32x32 blocks: register 4g+q of lane l of block (bi, bj) of batch b
+  // sits at (((bi * frag_nb + bj) * 4 + g) * 64 + l) * 4 + q + b * bs_frag,
+  // so each 16-byte access of a wave covers 1 KB. frag_out: written (the
+  // Gram); frag_in: read as the beta term instead of cin (the Poly).
+  float* frag_out; const float* frag_in; int32_t frag_nb; int64_t bs_frag;
 };
 
 struct GemmArgs {

@@ -103,6 +103,8 @@ enum : int {
   E_LOMIR = 256,  // the lo part is read only transposed (by the Poly epilogue):
                   // off-diagonal tiles store it mirrored only
   E_UPD = 512,    // last apply: the weight update with v as O, no store of v
+  E_FOUT = 1024,  // also store v in fp32 fragment order (frag_out)
+  E_FIN = 2048,   // v += beta * frag_in (fp32 fragment order) instead of cin
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -450,6 +452,23 @@ ns_gemm_kernel(const GemmArgs p, const FusedUpd u) {
   uint16_t* ohi = (EPI & E_HI) ? p.epi.out_hi + (int64_t)b * p.epi.bs_hi : nullptr;
   uint16_t* olo = (EPI & E_LO) ? p.epi.out_lo + (int64_t)b * p.epi.bs_lo : nullptr;
   const uint32_t t_cin = (uint32_t)((wj0 + lj) * ld_cin + wi0 + li);
+  // this lane's registers 4g .. 4g+3 of fragment (fi, fj) in the fp32
+  // fragment-order copy (g = 0 here; the next g is 256 floats further)
+  auto frag_ptr = [&](auto* base, int fi, int fj) __attribute__((always_inline)) {
+    const int bi = (wi0 + fi * 32) >> 5, bj = (wj0 + fj * 32) >> 5;
+    return base + (int64_t)b * p.epi.bs_frag + (int64_t)(bi * p.epi.frag_nb + bj) * 1024 + lane * 4;
+  };
+  if (EPI & E_FOUT) {   // straight from the accumulators
+    auto frag_out = [&](const f32x16_t& a, int fi, int fj) __attribute__((always_inline)) {
+      if (wi0 + fi * 32 >= p.M || wj0 + fj * 32 >= p.N) return;
+      float* d = frag_ptr(p.epi.frag_out, fi, fj);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(f32x4_t*)(d + 256 * g) =
+            f32x4_t{a[4 * g] * alpha, a[4 * g + 1] * alpha, a[4 * g + 2] * alpha, a[4 * g + 3] * alpha};
+    };
+    FragVisit<0, FM * FN, FN>::run(acc, frag_out);
+  }
 
   // private staging region of this wave: T[WTN][WTM] bf16, row pitch TP
   // bytes (16 bytes of padding keep the 8-byte writes of 16 lanes on
@@ -461,6 +480,13 @@ ns_gemm_kernel(const GemmArgs p, const FusedUpd u) {
   auto stage = [&](bool lo_pass) __attribute__((always_inline)) {
     auto frag_stage = [&](const f32x16_t& a, int fi, int fj) __attribute__((always_inline)) {
       uint2 c_hi[4], c_lo[4];
+      f32x4_t c_f[4];
+      if (EPI & E_FIN) {   // (fragments past M or N are never stored and read nothing)
+        const bool in = wi0 + fi * 32 < p.M && wj0 + fj * 32 < p.N;
+        const float* src = frag_ptr(p.epi.frag_in, in ? fi : 0, in ? fj : 0);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) c_f[g] = in ? *(const f32x4_t*)(src + 256 * g) : f32x4_t{};
+      }
       if (EPI & E_CIN) {   // rows r..r+3 at column c of the symmetric A, read as row c
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -477,6 +503,7 @@ ns_gemm_kernel(const GemmArgs p, const FusedUpd u) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           v[q] = a[4 * g + q] * alpha;
+          if (EPI & E_FIN) v[q] += beta * c_f[g][q];
           if (EPI & E_CIN) {
             const uint32_t wh = q < 2 ? c_hi[g].x : c_hi[g].y, wl = q < 2 ? c_lo[g].x : c_lo[g].y;
             const float ch = bf16_to_f32((uint16_t)((q & 1) ? wh >> 16 : wh));
@@ -688,14 +715,21 @@ hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const G
   if ((a.M & 31) || (a.N & 31) || bad(e.cin_hi, e.ld_cin, e.bs_cin) || bad(e.cin_lo, e.ld_cin, e.bs_cin) ||
       bad(e.out_hi, e.ld_hi, e.bs_hi) || bad(e.out_lo, e.ld_lo, e.bs_lo))
     return hipErrorInvalidValue;
+  const bool frag = (kind == GEMM_GRAM && e.frag_out) || (kind == GEMM_POLY && e.frag_in);
+  if (frag && (a.splits > 1 || split_pair || ((uintptr_t)(kind == GEMM_GRAM ? (const void*)e.frag_out : e.frag_in) & 15) ||
+               e.frag_nb * 32 < a.M || e.frag_nb * 32 < a.N || (e.bs_frag & 3)))
+    return hipErrorInvalidValue;
   if (a.splits > 1) {
     launch_epi<E_PART>(tile, a, total, s, u);
   } else if (kind == GEMM_GRAM) {
-    // without operand pairs A_lo only feeds the Poly epilogue's transposed read
+    // without operand pairs the Poly epilogue reads A from the fp32 copy in
+    // fragment order (with them, A_lo is an operand too)
     if (split_pair) launch_epi<E_SYM | E_HI | E_LO>(tile, a, total, s, u);
+    else if (frag) launch_epi<E_SYM | E_HI | E_FOUT>(tile, a, total, s, u);
     else launch_epi<E_SYM | E_HI | E_LO | E_LOMIR>(tile, a, total, s, u);
   } else if (kind == GEMM_POLY) {
     if (split_pair) launch_epi<E_SYM | E_CIN | E_DIAG | E_HI | E_LO>(tile, a, total, s, u);
+    else if (frag) launch_epi<E_SYM | E_FIN | E_DIAG | E_HI>(tile, a, total, s, u);
     else launch_epi<E_SYM | E_CIN | E_DIAG | E_HI>(tile, a, total, s, u);
   } else if (fused) {
     launch_epi<E_UPD, 1>(tile, a, total, s, u);   // last apply with the weight update
