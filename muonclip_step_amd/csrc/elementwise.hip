@@ -143,7 +143,17 @@ __global__ void __launch_bounds__(256) norm_finalize_kernel(const float* partial
   __shared__ double red[256];
   const float* p = partial + (int64_t)blockIdx.x * stride;
   double acc = 0.0;
-  for (int i = threadIdx.x; i < parts; i += 256) acc += (double)p[i];
+  // thread t adds elements t, t + 256, ... in that order; eight loads go out
+  // before their adds so the latency is paid once per eight
+  int i = threadIdx.x;
+  for (; i + 7 * 256 < parts; i += 8 * 256) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = p[i + k * 256];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += (double)v[k];
+  }
+  for (; i < parts; i += 256) acc += (double)p[i];
   red[threadIdx.x] = acc;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
