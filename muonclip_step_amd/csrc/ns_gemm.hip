@@ -50,16 +50,33 @@ __device__ inline int xcd_remap(int L, int total) {
   return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
 }
 
-__device__ __attribute__((always_inline)) inline void epilogue_store(const GemmEpi& e, int b, int i, int j, float acc, float sc) {
-  float v = e.alpha * sc * acc;
+// The epilogue of eight consecutive columns j0 .. j0+7 of row i (the split-K
+// finish): v = alpha scale acc + beta (cin_hi + cin_lo) + diag (i == j),
+// bf16 v to out_hi and bf16 (v - hi) to out_lo, in 16-byte accesses (row
+// starts and strides are multiples of 8 elements).
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+__device__ __attribute__((always_inline)) inline void epilogue_store8(const GemmEpi& e, int b, int i, int j0,
+                                                                      const float (&acc)[8], float sc) {
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = e.alpha * sc * acc[k];
   if (e.cin_hi) {
-    const int64_t o = (int64_t)b * e.bs_cin + (int64_t)i * e.ld_cin + j;
-    v += e.beta * (bf16_to_f32(e.cin_hi[o]) + bf16_to_f32(e.cin_lo[o]));
+    const int64_t o = (int64_t)b * e.bs_cin + (int64_t)i * e.ld_cin + j0;
+    const u16x8_t h = *(const u16x8_t*)(e.cin_hi + o), l = *(const u16x8_t*)(e.cin_lo + o);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] += e.beta * (bf16_to_f32(h[k]) + bf16_to_f32(l[k]));
   }
-  if (i == j) v += e.diag;
-  const uint16_t h = f32_to_bf16(v);
-  if (e.out_hi) e.out_hi[(int64_t)b * e.bs_hi + (int64_t)i * e.ld_hi + j] = h;
-  if (e.out_lo) e.out_lo[(int64_t)b * e.bs_lo + (int64_t)i * e.ld_lo + j] = f32_to_bf16(v - bf16_to_f32(h));
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if (i == j0 + k) v[k] += e.diag;
+  u16x8_t hi, lo;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    hi[k] = f32_to_bf16(v[k]);
+    lo[k] = f32_to_bf16(v[k] - bf16_to_f32(hi[k]));
+  }
+  if (e.out_hi) *(u16x8_t*)(e.out_hi + (int64_t)b * e.bs_hi + (int64_t)i * e.ld_hi + j0) = hi;
+  if (e.out_lo) *(u16x8_t*)(e.out_lo + (int64_t)b * e.bs_lo + (int64_t)i * e.ld_lo + j0) = lo;
 }
 
 __device__ __attribute__((always_inline)) inline float batch_scale(const GemmEpi& e, int b) {
@@ -658,17 +675,29 @@ ns_gemm_kernel(const GemmArgs p, const FusedUpd u) {
 
 // Deterministic split-K finish: fixed-order sum of the partial tiles, then the
 // same epilogue as the unsplit kernel.
+// Each thread finishes eight consecutive elements of a row; the partials are
+// added in split order, as the tiles would have accumulated them.
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs p) {
   const int64_t mn = (int64_t)p.M * p.N;
-  const int64_t total = mn * p.batch;
+  const int n8 = p.N >> 3;
+  const int64_t per_b = (int64_t)p.M * n8, total = per_b * p.batch;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
-    const int b = (int)(idx / mn);
-    const int64_t e = idx - (int64_t)b * mn;
-    const int i = (int)(e / p.N), j = (int)(e - (int64_t)i * p.N);
-    float acc = 0.0f;
-    for (int s = 0; s < p.splits; ++s) acc += p.partial[((int64_t)s * p.batch + b) * mn + e];
-    epilogue_store(p.epi, b, i, j, acc, batch_scale(p.epi, b));
+    const int b = (int)(idx / per_b);
+    const int64_t r = idx - (int64_t)b * per_b;
+    const int i = (int)(r / n8), j0 = (int)(r - (int64_t)i * n8) * 8;
+    const int64_t e = (int64_t)i * p.N + j0;
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < p.splits; ++s) {
+      const f32x4_t* src = (const f32x4_t*)(p.partial + ((int64_t)s * p.batch + b) * mn + e);
+      const f32x4_t x0 = src[0], x1 = src[1];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[k] += x0[k];
+        acc[4 + k] += x1[k];
+      }
+    }
+    epilogue_store8(p.epi, b, i, j0, acc, batch_scale(p.epi, b));
   }
 }
 
@@ -740,7 +769,10 @@ hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const G
 }
 
 hipError_t launch_splitk_reduce(const GemmArgs& a, hipStream_t s) {
-  const int64_t total = (int64_t)a.M * a.N * a.batch;
+  if ((a.N & 7) || (a.epi.out_hi && (a.epi.ld_hi & 7)) || (a.epi.out_lo && (a.epi.ld_lo & 7)) ||
+      (a.epi.cin_hi && (a.epi.ld_cin & 7)))
+    return hipErrorInvalidValue;
+  const int64_t total = (int64_t)a.M * (a.N / 8) * a.batch;
   int blocks = (int)((total + 255) / 256);
   if (blocks > 65536) blocks = 65536;
   if (blocks <= 0) return hipSuccess;
