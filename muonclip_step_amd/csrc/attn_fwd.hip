@@ -483,24 +483,36 @@ attn_fwd_kernel(const AttnArgs a) {
   }
 
   // normalise and store: oacc[f][n] register e of lane l is column
-  // 32 n + 8 (e / 4) + 4 (l / 32) + e % 4 of query wq0 + 32 f + l % 32
+  // 32 n + 8 (e / 4) + 4 (l / 32) + e % 4 of query wq0 + 32 f + l % 32. The
+  // wave's 32 output rows go through its 8 KB of the (now idle) LDS ring,
+  // rows of 256 bytes with the 16-byte chunks XOR-swizzled by row, so that
+  // each global store instruction writes four whole rows.
+  static_assert(NF == 1 && NW * 32 * kDV * 2 <= 2 * STAGE, "output staging");
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const float lt = lsum[f] + __shfl_xor(lsum[f], 32);
-    const int i = wq0 + 32 * f + (lane & 31);
-    if (i < a.T) {
-      const float inv = 1.0f / lt;
-      uint16_t* orow = (uint16_t*)a.o + (int64_t)b * a.os_b + (int64_t)i * a.os_t + (int64_t)h * a.os_h;
+    const int r = lane & 31, i = wq0 + 32 * f + r;
+    const float inv = 1.0f / lt;
+    char* ow = lds + wave * (32 * kDV * 2);
 #pragma unroll
-      for (int n = 0; n < 4; ++n)
+    for (int n = 0; n < 4; ++n)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          uint2 w;
-          w.x = f32x2_to_bf16x2(oacc[f][n][4 * t] * inv, oacc[f][n][4 * t + 1] * inv);
-          w.y = f32x2_to_bf16x2(oacc[f][n][4 * t + 2] * inv, oacc[f][n][4 * t + 3] * inv);
-          *(uint2*)(orow + 32 * n + 8 * t + 4 * hl) = w;
-        }
-      if (a.lse && hl == 0) a.lse[((int64_t)b * a.H + h) * a.T + i] = a.scale * m_use[f] + logf(lt);
+      for (int t = 0; t < 4; ++t) {
+        uint2 w;
+        w.x = f32x2_to_bf16x2(oacc[f][n][4 * t] * inv, oacc[f][n][4 * t + 1] * inv);
+        w.y = f32x2_to_bf16x2(oacc[f][n][4 * t + 2] * inv, oacc[f][n][4 * t + 3] * inv);
+        *(uint2*)(ow + r * 256 + (((4 * n + t) ^ (r & 15)) << 4) + 8 * hl) = w;
+      }
+    if (a.lse && hl == 0 && i < a.T) a.lse[((int64_t)b * a.H + h) * a.T + i] = a.scale * m_use[f] + logf(lt);
+    // (each wave reads back only what it wrote: no barrier, LDS operations
+    // of one wave complete in order)
+    const int c = lane & 15;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int rr = 4 * k + (lane >> 4), ii = wq0 + 32 * f + rr;
+      const u32x4_t v = *(const u32x4_t*)(ow + rr * 256 + ((c ^ (rr & 15)) << 4));
+      if (ii < a.T)
+        *(u32x4_t*)((uint16_t*)a.o + (int64_t)b * a.os_b + (int64_t)ii * a.os_t + (int64_t)h * a.os_h + 8 * c) = v;
     }
   }
   if (SMAX) {

@@ -226,7 +226,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int ktiles, int batch, bool sym, bool r
   if (tiles < kCUs / 2 && ktiles >= 16) {
     // split-K runs the full (non-symmetric) tile set
     const int full = p.tiles_m * p.tiles_n * batch;
-    splits = std::min((2 * kCUs + full - 1) / full, ktiles / 8);
+    // one wave of work items: a second wave of smaller splits measured
+    // slower, its extra fp32 partials costing the finish more than the
+    // better balance gained (MLA layer 9.29 -> 9.23 ms)
+    splits = std::min((kCUs + full - 1) / full, ktiles / 8);
     splits = std::max(splits, 1);
   }
   p.kt_per_split = (ktiles + splits - 1) / splits;
