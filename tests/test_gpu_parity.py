@@ -389,15 +389,17 @@ def _fresh(states):
         s.m.copy_(dev_tensor(s.m0, "f32"))
 
 
-@pytest.mark.parametrize("case", ["mha_layer", "ragged_tall_wide", "many_clipped", "global_clip"])
+@pytest.mark.parametrize("case", ["mha_layer", "ragged_tall_wide", "many_clipped", "global_clip", "many_tiles"])
 def test_update_fused_into_last_apply_is_bit_identical(case):
     """Without an O output the update runs in the last Newton-Schulz apply's
     epilogue. It must give bit for bit the weights and gamma of the separate
     update kernel (which the oracle parity tests check, since they request
-    O): the MHA layer's four 2048^2 matrices with clipped W_q, W_k; a tall
-    and a wide matrix of one ragged shape group with padded rows, clipped;
-    eleven clipped matrices (past the fused path's clip table: the update
-    kernel runs); the global-gamma variant."""
+    O): the MHA layer's four 2048^2 matrices with clipped W_q, W_k (apply
+    tiles of eight waves); a tall and a wide matrix of one ragged shape group
+    with padded rows, clipped; eleven clipped matrices (past the fused path's
+    clip table: the update kernel runs); the global-gamma variant; seventeen
+    2048x1024 / 1024x2048 matrices, a tall and a wide one clipped, whose 544
+    apply tiles run the four-wave kernel."""
     print("fused update case", case, flush=True)
     rng = np.random.default_rng(sum(map(ord, case)))
     heads = 4
@@ -411,13 +413,17 @@ def test_update_fused_into_last_apply_is_bit_identical(case):
             shapes = [(200, 136), (136, 200)]
         elif case == "many_clipped":
             shapes = [(96, 64)] * 11
+        elif case == "many_tiles":
+            shapes = [(2048, 1024)] * 4 + [(1024, 2048)] * 9 + [(2048, 1024)] * 4
         else:
             shapes = [(128, 256), (256, 128)]
             kw = dict(clip_global=1)
         states = []
-        for r, c in shapes:
+        for idx, (r, c) in enumerate(shapes):
             period = r // heads
-            spec = wl.MatrixSpec("m", r, c, clip_slot=0, period=period, segments=((0, period // 2, 0.5), (period // 2, 8, 1.0)))
+            clipped = case != "many_tiles" or idx in (0, 4)   # a tall and a wide one
+            spec = wl.MatrixSpec("m", r, c, clip_slot=0 if clipped else -1, period=period,
+                                 segments=((0, period // 2, 0.5), (period // 2, 8, 1.0)))
             w = (rng.standard_normal((r, c)) * 0.02).astype(np.float32)
             g = (rng.standard_normal((r, c)) * 1e-3).astype(np.float32)
             m = (rng.standard_normal((r, c)) * 1e-3).astype(np.float32)
