@@ -151,6 +151,26 @@ def test_ragged_shapes(shape, w_dtype, g_dtype, ld_pad):
         assert torch.all(st.w_full[:, cols:] == 0) and torch.all(st.m_full[:, cols:] == 0)
 
 
+def test_group_on_128_tiles_against_oracle():
+    """Four matrices of one shape group (m = 1024, n = 1100: two wide, two
+    tall, padded rows) whose symmetric products run unsplit on 128x128 tiles
+    (144 of them), the path where the Gram hands A to the Poly epilogue in
+    fp32 fragment order; every matrix against the oracle."""
+    states = []
+    for k, shape in enumerate([(1024, 1100), (1100, 1024), (1024, 1100), (1100, 1024)]):
+        spec = wl.MatrixSpec("g", *shape, "bf16", init_std=0.5, grad_std=1.0, mom_std=1.0)
+        seed = 3000 + k
+        w = wl.quantize_bf16(wl.normal(seed, 0, shape, 0.5))
+        g = wl.quantize_f32(wl.normal(seed, 1, shape, 1.0))
+        m = wl.quantize_f32(wl.normal(seed, 2, shape, 1.0))
+        states.append(State(spec, w, g, m, ld_pad=8 * k))
+    hp = mc.hparams(lr=0.01)
+    mc.muonclip_step([st.desc() for st in states], hp)
+    torch.cuda.synchronize()
+    for st in states:
+        check_matrix(st, hp)
+
+
 def test_zero_gradient_and_momentum_decay_only():
     spec = wl.MatrixSpec("z", 96, 160, "f32")
     w = wl.quantize_f32(wl.normal(77, 0, (96, 160), 1.0))
