@@ -494,16 +494,19 @@ ns_gemm_kernel(const GemmArgs p, const FusedUpd u) {
   __builtin_amdgcn_s_barrier();          // every wave is done with the ring
 
   // write pass: v (or its bf16 residual when lo_pass) into T
-  auto stage = [&](bool lo_pass) __attribute__((always_inline)) {
-    auto frag_stage = [&](const f32x16_t& a, int fi, int fj) __attribute__((always_inline)) {
-      uint2 c_hi[4], c_lo[4];
-      f32x4_t c_f[4];
-      if (EPI & E_FIN) {   // (fragments past M or N are never stored and read nothing)
-        const bool in = wi0 + fi * 32 < p.M && wj0 + fj * 32 < p.N;
-        const float* src = frag_ptr(p.epi.frag_in, in ? fi : 0, in ? fj : 0);
+  // The fp32 A of the Poly's b A term (E_FIN) is read for four fragments at
+  // a time before they are staged, so its latency is paid once per four.
+  constexpr int NFR = FM * FN, FGRP = (EPI & E_FIN) ? (NFR < 4 ? NFR : 4) : 1;
+  auto load_fin = [&](int fi, int fj, f32x4_t (&c_f)[4]) __attribute__((always_inline)) {
+    // (fragments past M or N are never stored and read nothing)
+    const bool in = wi0 + fi * 32 < p.M && wj0 + fj * 32 < p.N;
+    const float* src = frag_ptr(p.epi.frag_in, in ? fi : 0, in ? fj : 0);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) c_f[g] = in ? *(const f32x4_t*)(src + 256 * g) : f32x4_t{};
-      }
+    for (int g = 0; g < 4; ++g) c_f[g] = in ? *(const f32x4_t*)(src + 256 * g) : f32x4_t{};
+  };
+  auto stage = [&](bool lo_pass) __attribute__((always_inline)) {
+    auto frag_stage = [&](const f32x16_t& a, int fi, int fj, const f32x4_t (&c_f)[4]) __attribute__((always_inline)) {
+      uint2 c_hi[4], c_lo[4];
       if (EPI & E_CIN) {   // rows r..r+3 at column c of the symmetric A, read as row c
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -537,7 +540,16 @@ ns_gemm_kernel(const GemmArgs p, const FusedUpd u) {
         *(uint2*)(tw + uc * TP + ur * 2) = make_uint2(w01, w23);
       }
     };
-    FragVisit<0, FM * FN, FN>::run(acc, frag_stage);
+#pragma unroll
+    for (int I0 = 0; I0 < NFR; I0 += FGRP) {
+      f32x4_t cf[FGRP][4];
+      if (EPI & E_FIN) {
+#pragma unroll
+        for (int k = 0; k < FGRP; ++k) load_fin((I0 + k) / FN, (I0 + k) % FN, cf[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < FGRP; ++k) frag_stage(acc[(I0 + k) / FN][(I0 + k) % FN], (I0 + k) / FN, (I0 + k) % FN, cf[k]);
+    }
   };
   // row-major store of T^T: lane t of group gr reads rows i0+t, columns
   // j0..j0+7 (two transposing reads) and stores them as one 16-byte vector
