@@ -494,9 +494,10 @@ ns_gemm_kernel(const GemmArgs p, const FusedUpd u) {
   __builtin_amdgcn_s_barrier();          // every wave is done with the ring
 
   // write pass: v (or its bf16 residual when lo_pass) into T
-  // The fp32 A of the Poly's b A term (E_FIN) is read for four fragments at
-  // a time before they are staged, so its latency is paid once per four.
-  constexpr int NFR = FM * FN, FGRP = (EPI & E_FIN) ? (NFR < 4 ? NFR : 4) : 1;
+  // The fp32 A of the Poly's b A term (E_FIN) is read for a group of
+  // fragments before they are staged, so its latency is paid once per group.
+  constexpr int kFinGrp = NW == 4 ? 8 : 4;   // registers free in the epilogue (4 and 16 measured slower)
+  constexpr int NFR = FM * FN, FGRP = (EPI & E_FIN) ? (NFR < kFinGrp ? NFR : kFinGrp) : 1;
   auto load_fin = [&](int fi, int fj, f32x4_t (&c_f)[4]) __attribute__((always_inline)) {
     // (fragments past M or N are never stored and read nothing)
     const bool in = wi0 + fi * 32 < p.M && wj0 + fj * 32 < p.N;
