@@ -124,9 +124,12 @@ __device__ __forceinline__ float wave_max(float x) {
 // their MFMAs (the LDS delivers about 200 bytes per clock per CU to two waves
 // per SIMD, enough for the fragment traffic). The whole state fits 256
 // VGPRs: every MFMA writes VGPRs and the rescale is plain VALU arithmetic.
-template <int DK, int DS, bool SMAX>
+// OUT = false: the logits and S_max only (no values, softmax or output),
+// which serves max_logits_per_head for the MLA head shape.
+template <int DK, int DS, bool SMAX, bool OUT = true>
 __global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(const AttnArgs a) {
+  static_assert(OUT || SMAX, "a pass with neither output nor S_max");
   static_assert(DK == 128 && (DS == 0 || DS == 64), "head widths");
   constexpr int NF = 1;                      // query fragments per wave
   constexpr int NW = 8, WR = 32;             // waves per block, query rows per wave
@@ -243,7 +246,7 @@ attn_fwd_kernel(const AttnArgs a) {
         __builtin_amdgcn_global_load_lds((const void*)(rb + roff[i]),
                                          (lds_void_t*)(st + KC_BYTES + 1024 * (IR * wave + i)), 16, 0, 0);
 #pragma unroll
-      for (int i = 0; i < IV; ++i)
+      for (int i = 0; i < (OUT ? IV : 0); ++i)
         __builtin_amdgcn_global_load_lds((const void*)(vb + voffs[i]),
                                          (lds_void_t*)(st + KC_BYTES + KR_BYTES + 1024 * (IV * wave + i)), 16, 0, 0);
     } else {
@@ -260,7 +263,7 @@ attn_fwd_kernel(const AttnArgs a) {
                                          (lds_void_t*)(st + KC_BYTES + 1024 * (IR * wave + i)), 16, 0, 0);
       }
 #pragma unroll
-      for (int i = 0; i < IV; ++i) {
+      for (int i = 0; i < (OUT ? IV : 0); ++i) {
         const int d = (min(vrow[i], last) - vrow[i]) * (int)a.vs_t * 2;
         __builtin_amdgcn_global_load_lds((const void*)(vb + voffs[i] + d),
                                          (lds_void_t*)(st + KC_BYTES + KR_BYTES + 1024 * (IV * wave + i)), 16, 0, 0);
@@ -355,7 +358,7 @@ attn_fwd_kernel(const AttnArgs a) {
         if constexpr (s + KSL < KS) read_k1(g_, std::integral_constant<int, s + KSL>{});
       });
       s_wait_logits(sacc[0]);
-      read_v(g_, std::integral_constant<int, 0>{});
+      if constexpr (OUT) read_v(g_, std::integral_constant<int, 0>{});
       if (MASK) {
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
@@ -380,6 +383,11 @@ attn_fwd_kernel(const AttnArgs a) {
         bm[f] = x;
         if (SMAX) m_all[f] = fmaxf(m_all[f], x);
         grow = grow || (x > m_use[f] + thr);
+      }
+      if constexpr (!OUT) {
+        // outstanding after this: the next half's first KSL K reads only
+        if (g == 0) read_k(std::integral_constant<int, 1>{});
+        return;
       }
       if (__any(grow)) {
 #pragma unroll
@@ -483,6 +491,7 @@ attn_fwd_kernel(const AttnArgs a) {
     wait_next();
   }
 
+  if constexpr (OUT) {
   // normalise and store: oacc[f][n] register e of lane l is column
   // 32 n + 8 (e / 4) + 4 (l / 32) + e % 4 of query wq0 + 32 f + l % 32. The
   // wave's 32 output rows go through its 8 KB of the (now idle) LDS ring,
@@ -516,6 +525,7 @@ attn_fwd_kernel(const AttnArgs a) {
         *(u32x4_t*)((uint16_t*)a.o + (int64_t)b * a.os_b + (int64_t)ii * a.os_t + (int64_t)h * a.os_h + 8 * c) = v;
     }
   }
+  }   // OUT
   if (SMAX) {
     float mx = m_all[0];
 #pragma unroll
@@ -534,6 +544,14 @@ attn_fwd_kernel(const AttnArgs a) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
+
+hipError_t launch_attention_smax_only(const AttnArgs& a, hipStream_t s) {
+  if (a.B <= 0 || a.T <= 0 || a.H <= 0) return hipSuccess;
+  if (a.d_k != 128 || a.d_s != 64 || !a.smax_enc) return hipErrorInvalidValue;
+  const int grid = (a.T + kBQ - 1) / kBQ * a.H * a.B;
+  attn_fwd_kernel<128, 64, true, false><<<grid, 512, 0, s>>>(a);
+  return hipGetLastError();
+}
 
 bool attention_supported(const AttnArgs& a) {
   const bool shape = a.d_k == 128 && (a.d_s == 0 || a.d_s == 64) && a.d_v == kDV;

@@ -3,17 +3,18 @@
 // attention logits, S_max equation; K2 report 2.1). The logits are never
 // written to memory.
 //
-// MFMA kernels (bf16): a 256-thread block owns 256 query rows of one (head,
-// sample); waves keep their query rows as MFMA A-fragments in registers for
-// the whole kernel and stream tiles of K through XOR-swizzled LDS; each
-// 32x32 logit fragment is folded straight into per-lane running maxima; only
-// tiles on the causal diagonal or the ragged end apply a mask, and a wave
-// skips key tiles lying wholly above its causal diagonal. Blocks are issued
-// heaviest
-// causal row first. The block max goes through an order-preserving integer
-// encoding into one atomicMax per block, so the result does not depend on
-// scheduling. MLA keys are [k^C_h | k^R]: the shared rotary key supplies the
-// last d_s dimensions of every head's key (K2 report, per-head MLA clipping).
+// MFMA kernel for per-head keys (bf16, d = 64, 128): a 256-thread block owns
+// 256 query rows of one (head, sample); waves keep their query rows as MFMA
+// A-fragments in registers for the whole kernel and stream tiles of K
+// through XOR-swizzled LDS; each 32x32 logit fragment is folded straight into
+// per-lane running maxima; only tiles on the causal diagonal or the ragged
+// end apply a mask, and a wave skips key tiles lying wholly above its causal
+// diagonal. Blocks are issued heaviest causal row first. The block max goes
+// through an order-preserving integer encoding into one atomicMax per block,
+// so the result does not depend on scheduling. MLA keys are [k^C_h | k^R]:
+// the shared rotary key supplies the last d_s dimensions of every head's key
+// (K2 report, per-head MLA clipping); that shape runs the logit pass of the
+// attention kernel (attn_fwd.hip) with the same masking and encoding.
 //
 // The generic kernel (fp32 inputs, or shapes the MFMA kernel does not cover)
 // computes the same definition with one fp32 dot product per pair.
@@ -228,181 +229,6 @@ __global__ void __launch_bounds__(256, 3) max_logits_tile_kernel(const MaxLogitA
   block_max_commit(mx, a.out_enc + h, red);
 }
 
-// A 256-thread block owns 256 query rows of one (head, sample) and walks the
-// key axis in tiles of 128 keys x all D dimensions. Each wave computes
-// 32 QFR query rows x 32 FN keys of a tile as QFR x FN fragments of
-// v_mfma_f32_32x32x16_bf16 (eight independent accumulators: 4 x 2 for
-// d = 64, 128; 2 x 4 for the MLA's d = 192, whose query fragments need more
-// registers). The wave's query rows stay in registers as A fragments for the
-// whole kernel; key tiles stream through an NST-slot LDS ring that
-// direct-to-LDS loads fill NST-1 tiles ahead. The loop mirrors the NS GEMM:
-// the wait and barrier for tile t+1 sit before the last 16-wide step of tile
-// t, whose MFMAs hide the reads of tile t+1's first fragments; each step
-// reads the next step's fragments under its own MFMAs. A finished tile is
-// folded into 16 independent per-lane running maxima (masked only on the
-// causal diagonal and the ragged end); the first step of the next tile starts
-// from zero accumulators.
-template <int DK, int DS, int QFR, int NST>
-__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
-max_logits_mfma_kernel(const MaxLogitArgs a) {
-  constexpr int D = DK + DS, KS = D / 16, CPR = D / 8, RB = 2 * D;   // steps, chunks and bytes per key row
-  constexpr int BQ = 256, BKV = 128;
-  constexpr int WM = BQ / (32 * QFR), WN = 4 / WM, FN = BKV / (32 * WN);
-  constexpr int SLOT = BKV * RB;                  // bytes per key tile
-  constexpr int PW = SLOT / 1024 / 4;             // direct-to-LDS loads per wave per tile
-  static_assert(WM * WN == 4 && FN * 32 * WN == BKV && QFR % 2 == 0 && (KS % 2) == 0, "wave grid");
-  static_assert(SLOT % 4096 == 0 && NST >= 3 && NST <= 4 && NST * SLOT <= 160 * 1024, "ring");
-  __shared__ __attribute__((aligned(1024))) char lds[NST * SLOT];
-  __shared__ float red[4];
-
-  const int HB = a.H * a.B;
-  const int nqt = (a.T + BQ - 1) / BQ;
-  const int hb = blockIdx.x % HB;
-  const int qt = nqt - 1 - (int)(blockIdx.x / HB);   // heaviest causal rows first
-  const int h = hb % a.H, b = hb / a.H;
-  const int q0 = qt * BQ;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave % WN;
-  const int wr0 = q0 + 32 * QFR * wm;             // first query row of this wave
-
-  const uint16_t* Q = (const uint16_t*)a.q + (int64_t)b * a.qs_b + (int64_t)h * a.qs_h;
-  const uint16_t* K = (const uint16_t*)a.k + (int64_t)b * a.ks_b + (int64_t)h * a.ks_h;
-  const uint16_t* KS_ = DS > 0 ? (const uint16_t*)a.ks + (int64_t)b * a.kss_b : nullptr;
-
-  // query rows as A fragments: lane l holds row l%32, 8 dims at 8 (l/32) of
-  // each 16-wide step. Rows past T re-read the last valid one (masked later).
-  bf16x8_t qf[QFR][KS];
-#pragma unroll
-  for (int f = 0; f < QFR; ++f) {
-    const int row = wr0 + 32 * f + (lane & 31);
-    const int rr = row < a.T ? row : a.T - 1;
-    const uint16_t* base = Q + (int64_t)rr * a.qs_t + 8 * (lane >> 5);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[f][s] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(base + 16 * s));
-  }
-
-  const int kend = a.causal ? min(a.T, q0 + BQ) : a.T;
-  const int nkt = (kend + BKV - 1) / BKV;
-
-  // Tile t fills slot t % NST; load i of this wave fills 1 KB of it, lane l
-  // landing at chunk q = (wave PW + i) 64 + l, i.e. key row q / CPR, physical
-  // chunk q % CPR, which holds the tile's logical chunk (q % CPR) ^ swz(row).
-  // Keys past T re-read the last valid key (masked later).
-  auto issue = [&](int t) __attribute__((always_inline)) {
-    const int kv0 = t * BKV;
-    char* slot = lds + (t % NST) * SLOT;
-#pragma unroll
-    for (int i = 0; i < PW; ++i) {
-      const int q = (wave * PW + i) * 64 + lane, r = q / CPR, c = (q % CPR) ^ ml_swz<CPR>(r);
-      const int key = kv0 + r, kr = key < a.T ? key : a.T - 1;
-      const uint16_t* src = (DS == 0 || c < DK / 8) ? K + (int64_t)kr * a.ks_t + c * 8
-                                                    : KS_ + (int64_t)kr * a.kss_t + (c - DK / 8) * 8;
-      __builtin_amdgcn_global_load_lds((const void*)src, (ml_lds_void_t*)(slot + (wave * PW + i) * 1024), 16, 0, 0);
-    }
-  };
-  // this wave has keys of tile t at or below its last query row
-  auto active = [&](int t) __attribute__((always_inline)) {
-    const int wk0 = t * BKV + 32 * FN * wn;
-    return !(a.causal && wk0 > wr0 + 32 * QFR - 1) && wr0 < a.T && wk0 < a.T;
-  };
-
-  f32x16_t acc[QFR][FN];
-  bf16x8_t kf[2][FN];
-  float mxv[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) mxv[e] = -INFINITY;
-  const f32x16_t zero = f32x16_t{};
-  auto read_k = [&](int t, int s, int sl) __attribute__((always_inline)) {
-    const char* cur = lds + (t % NST) * SLOT;
-    const int c = 2 * s + (lane >> 5);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int r = 32 * FN * wn + 32 * j + (lane & 31);
-      kf[sl][j] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(cur + r * RB + ((c ^ ml_swz<CPR>(r)) << 4)));
-    }
-  };
-  auto mfma_step = [&](int s) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < QFR; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[i][s], kf[s & 1][j], s == 0 ? zero : acc[i][j], 0, 0, 0);
-  };
-  // wait until at most `ahead` tiles' loads of this wave are in flight, i.e.
-  // every older tile has landed (the query rows were loaded before any tile)
-  static_assert(2 * PW <= 63, "vmcnt field");
-#define ML_VMCNT(n_) (0xF70 | ((n_) & 15) | (((n_) >> 4) << 14))
-  auto wait_tile = [&](int ahead) __attribute__((always_inline)) {
-    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(ML_VMCNT(2 * PW));
-    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(ML_VMCNT(PW));
-    else __builtin_amdgcn_s_waitcnt(ML_VMCNT(0));
-  };
-#undef ML_VMCNT
-
-  if (nkt > 0) {
-#pragma unroll
-    for (int i = 0; i < NST - 1; ++i)
-      if (i < nkt) issue(i);
-    wait_tile(min(NST - 2, nkt - 1));          // tile 0 landed; tiles 1 .. NST-2 may be in flight
-    __syncthreads();
-    if (active(0)) read_k(0, 0, 0);
-  }
-  for (int t = 0; t < nkt; ++t) {
-    const bool act = active(t);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      if (s + 1 < KS) {
-        if (act) {
-          read_k(t, s + 1, (s + 1) & 1);
-          mfma_step(s);
-        }
-      } else {
-        // tile t+1 landed everywhere; slot (t-1) % NST is free for tile
-        // t+NST-1. Issued so far: tiles up to t+NST-2, so the tiles that may
-        // still be in flight after t+1 are t+2 .. min(t+NST-2, nkt-1).
-        if (t + 1 < nkt) {
-          wait_tile(min(NST - 3, nkt - 2 - t));
-          __syncthreads();
-          if (t + NST - 1 < nkt) issue(t + NST - 1);
-        }
-        if (act) {
-          if (t + 1 < nkt && active(t + 1)) read_k(t + 1, 0, 0);
-          mfma_step(s);
-        }
-      }
-    }
-    if (act) {   // fold tile t into the running maxima
-      const int wk0 = t * BKV + 32 * FN * wn;
-      const bool need_mask = (a.causal && wk0 + 32 * FN - 1 > wr0) || (wk0 + 32 * FN > a.T) || (wr0 + 32 * QFR > a.T);
-      if (!need_mask) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int i = 0; i < QFR; i += 2)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mxv[e] = fmaxf(mxv[e], fmaxf(acc[i][j][e], acc[i + 1][j][e]));
-      } else {
-        // register e of lane l: query row 8 (e/4) + 4 (l/32) + e%4, key column l%32
-#pragma unroll
-        for (int i = 0; i < QFR; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int kj = wk0 + 32 * j + (lane & 31);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int qi = wr0 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-              if (qi < a.T && kj < a.T && (!a.causal || kj <= qi)) mxv[e] = fmaxf(mxv[e], acc[i][j][e]);
-            }
-          }
-      }
-    }
-  }
-#pragma unroll
-  for (int e = 1; e < 16; ++e) mxv[0] = fmaxf(mxv[0], mxv[e]);
-  block_max_commit(mxv[0], a.out_enc + h, red);
-}
-
 template <bool BF16>
 __global__ void __launch_bounds__(256) max_logits_generic_kernel(const MaxLogitArgs a) {
   __shared__ float red[4];
@@ -472,7 +298,21 @@ hipError_t launch_max_logits(const MaxLogitArgs& a, hipStream_t s, bool* used_mf
     *used_mfma = true;
     const int nqt = (a.T + 255) / 256;             // 256 query rows per block
     const int grid = nqt * a.H * a.B;
-    if (a.d_k == 128 && a.d_s == 64) max_logits_mfma_kernel<128, 64, 2, 3><<<grid, 256, 0, s>>>(a);
+    if (a.d_k == 128 && a.d_s == 64) {
+      // MLA keys [k^C_h | k^R]: the attention kernel's logit pass (eight
+      // waves of 32 rows, K fragments through a six-slot ring; 472 us against
+      // 562 us for a four-wave kernel of 64 rows per wave and 128-key tiles)
+      AttnArgs t{};
+      t.q = a.q; t.k = a.k; t.ks = a.ks; t.v = a.k;
+      t.smax_enc = a.out_enc;
+      t.qs_b = a.qs_b; t.qs_t = a.qs_t; t.qs_h = a.qs_h;
+      t.ks_b = a.ks_b; t.ks_t = a.ks_t; t.ks_h = a.ks_h;
+      t.kss_b = a.kss_b; t.kss_t = a.kss_t;
+      t.vs_b = a.ks_b; t.vs_t = a.ks_t; t.vs_h = a.ks_h;
+      t.B = a.B; t.T = a.T; t.H = a.H; t.d_k = a.d_k; t.d_s = a.d_s; t.d_v = 128;
+      t.causal = a.causal; t.scale = 1.0f;
+      return launch_attention_smax_only(t, s);
+    }
     else if (a.d_k == 128) max_logits_tile_kernel<128><<<grid, 256, 0, s>>>(a);
     else max_logits_tile_kernel<64><<<grid, 256, 0, s>>>(a);
   } else if (a.bf16) {

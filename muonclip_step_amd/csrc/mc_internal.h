@@ -276,5 +276,8 @@ struct AttnArgs {
 // true when the kernel covers (d_k, d_s, d_v) and the alignments
 bool attention_supported(const AttnArgs& a);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+// S_max alone through the attention kernel's logit pass (d_k 128, d_s 64;
+// v, o and lse unused; q, k, ks 16-byte aligned rows)
+hipError_t launch_attention_smax_only(const AttnArgs& a, hipStream_t s);
 
 }  // namespace mc
