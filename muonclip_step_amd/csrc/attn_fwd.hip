@@ -547,9 +547,10 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 hipError_t launch_attention_smax_only(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.T <= 0 || a.H <= 0) return hipSuccess;
-  if (a.d_k != 128 || a.d_s != 64 || !a.smax_enc) return hipErrorInvalidValue;
+  if (a.d_k != 128 || (a.d_s != 64 && a.d_s != 0) || !a.smax_enc) return hipErrorInvalidValue;
   const int grid = (a.T + kBQ - 1) / kBQ * a.H * a.B;
-  attn_fwd_kernel<128, 64, true, false><<<grid, 512, 0, s>>>(a);
+  if (a.d_s == 64) attn_fwd_kernel<128, 64, true, false><<<grid, 512, 0, s>>>(a);
+  else attn_fwd_kernel<128, 0, true, false><<<grid, 512, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -3,7 +3,9 @@
 // attention logits, S_max equation; K2 report 2.1). The logits are never
 // written to memory.
 //
-// MFMA kernel for per-head keys (bf16, d = 64, 128): a 256-thread block owns
+// MFMA kernels (bf16). For d_k = 128 (MHA, and MLA with the 64-wide shared
+// rotary key) the logit pass of the attention kernel (attn_fwd.hip) runs; the
+// tile kernel below serves d = 64. Tile kernel: a 256-thread block owns
 // 256 query rows of one (head, sample); waves keep their query rows as MFMA
 // A-fragments in registers for the whole kernel and stream tiles of K
 // through XOR-swizzled LDS; each 32x32 logit fragment is folded straight into
@@ -13,8 +15,8 @@
 // through an order-preserving integer encoding into one atomicMax per block,
 // so the result does not depend on scheduling. MLA keys are [k^C_h | k^R]:
 // the shared rotary key supplies the last d_s dimensions of every head's key
-// (K2 report, per-head MLA clipping); that shape runs the logit pass of the
-// attention kernel (attn_fwd.hip) with the same masking and encoding.
+// (K2 report, per-head MLA clipping). The attention kernel's logit pass
+// applies the same masking and encoding.
 //
 // The generic kernel (fp32 inputs, or shapes the MFMA kernel does not cover)
 // computes the same definition with one fp32 dot product per pair.
@@ -84,7 +86,8 @@ __device__ __forceinline__ void ml_vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
 }
 
-// Key-tile kernel for per-head keys (d = 64, 128): a 256-thread block owns
+// Key-tile kernel for per-head keys (written for d = 64 and 128; d = 128 now
+// takes the attention kernel's logit pass): a 256-thread block owns
 // 256 query rows, each wave keeps 64 of them as A fragments, and 64-key tiles
 // of K arrive in a three-stage LDS ring through direct-to-LDS loads issued
 // two tiles ahead (the XOR swizzle is applied on the source side: the lane
@@ -298,10 +301,11 @@ hipError_t launch_max_logits(const MaxLogitArgs& a, hipStream_t s, bool* used_mf
     *used_mfma = true;
     const int nqt = (a.T + 255) / 256;             // 256 query rows per block
     const int grid = nqt * a.H * a.B;
-    if (a.d_k == 128 && a.d_s == 64) {
-      // MLA keys [k^C_h | k^R]: the attention kernel's logit pass (eight
-      // waves of 32 rows, K fragments through a six-slot ring; 472 us against
-      // 562 us for a four-wave kernel of 64 rows per wave and 128-key tiles)
+    if (a.d_k == 128) {
+      // d_k = 128 with or without the MLA rotary part: the attention kernel's
+      // logit pass (eight waves of 32 rows, two per SIMD). MLA layer: 472 us
+      // against 562 us for a four-wave kernel of 64 rows per wave and 128-key
+      // tiles; MHA layer: 140 us against 142 us for the tile kernel below.
       AttnArgs t{};
       t.q = a.q; t.k = a.k; t.ks = a.ks; t.v = a.k;
       t.smax_enc = a.out_enc;
@@ -313,7 +317,6 @@ hipError_t launch_max_logits(const MaxLogitArgs& a, hipStream_t s, bool* used_mf
       t.causal = a.causal; t.scale = 1.0f;
       return launch_attention_smax_only(t, s);
     }
-    else if (a.d_k == 128) max_logits_tile_kernel<128><<<grid, 256, 0, s>>>(a);
     else max_logits_tile_kernel<64><<<grid, 256, 0, s>>>(a);
   } else if (a.bf16) {
     max_logits_generic_kernel<true><<<a.H * a.B, 256, 0, s>>>(a);
