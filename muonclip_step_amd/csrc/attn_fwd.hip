@@ -127,7 +127,7 @@ __device__ __forceinline__ float wave_max(float x) {
 // OUT = false: the logits and S_max only (no values, softmax or output),
 // which serves max_logits_per_head for the MLA head shape.
 template <int DK, int DS, bool SMAX, bool OUT = true>
-__global__ void __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(512, OUT ? 1 : 2) __attribute__((amdgpu_waves_per_eu(OUT ? 2 : 4, OUT ? 2 : 4)))
 attn_fwd_kernel(const AttnArgs a) {
   static_assert(OUT || SMAX, "a pass with neither output nor S_max");
   static_assert(DK == 128 && (DS == 0 || DS == 64), "head widths");
@@ -141,7 +141,8 @@ attn_fwd_kernel(const AttnArgs a) {
   constexpr int D = DK + DS, KS = D / 16;
   constexpr int KSL = kLean ? KS / 2 : KS, NVB = kLean ? 1 : 2;   // K slots, value buffers
   // one LDS stage: K content rows [64][256 B], rotary rows [64][128 B], V rows [64][256 B]
-  constexpr int KC_BYTES = kBKV * 256, KR_BYTES = kBKV * DS * 2, VT_BYTES = kBKV * kDV * 2;
+  // (the logit pass keeps no values: two blocks share a CU, four waves per SIMD)
+  constexpr int KC_BYTES = kBKV * 256, KR_BYTES = kBKV * DS * 2, VT_BYTES = OUT ? kBKV * kDV * 2 : 0;
   constexpr int STAGE = KC_BYTES + KR_BYTES + VT_BYTES;
   // LDS ring stages: each tile's loads go out while the previous tile is
   // computed (a third stage, loading two tiles ahead, measured 3 % slower)
@@ -497,7 +498,7 @@ attn_fwd_kernel(const AttnArgs a) {
   // wave's 32 output rows go through its 8 KB of the (now idle) LDS ring,
   // rows of 256 bytes with the 16-byte chunks XOR-swizzled by row, so that
   // each global store instruction writes four whole rows.
-  static_assert(NF == 1 && NW * 32 * kDV * 2 <= NSTG * STAGE, "output staging");
+  static_assert(NF == 1 && (!OUT || NW * 32 * kDV * 2 <= NSTG * STAGE), "output staging");
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const float lt = lsum[f] + __shfl_xor(lsum[f], 32);
