@@ -537,7 +537,7 @@ attn_fwd_kernel(const AttnArgs a) {
     if (tid == 0) {
       mx = red[0];
       for (int w = 1; w < NW; ++w) mx = fmaxf(mx, red[w]);
-      atomicMax(a.smax_enc + h, order_enc(mx));
+      atomic_max_f32(a.smax + h, mx * a.scale);
     }
   }
 }
@@ -548,7 +548,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 hipError_t launch_attention_smax_only(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.T <= 0 || a.H <= 0) return hipSuccess;
-  if (a.d_k != 128 || (a.d_s != 64 && a.d_s != 0) || !a.smax_enc) return hipErrorInvalidValue;
+  if (a.d_k != 128 || (a.d_s != 64 && a.d_s != 0) || !a.smax) return hipErrorInvalidValue;
   const int grid = (a.T + kBQ - 1) / kBQ * a.H * a.B;
   if (a.d_s == 64) attn_fwd_kernel<128, 64, true, false><<<grid, 512, 0, s>>>(a);
   else attn_fwd_kernel<128, 0, true, false><<<grid, 512, 0, s>>>(a);
@@ -569,7 +569,7 @@ bool attention_supported(const AttnArgs& a) {
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.T <= 0 || a.H <= 0) return hipSuccess;
   const int grid = (a.T + kBQ - 1) / kBQ * a.H * a.B;
-  const bool sm = a.smax_enc != nullptr;
+  const bool sm = a.smax != nullptr;
   if (a.d_s == 64) {
     if (sm) attn_fwd_kernel<128, 64, true><<<grid, 512, 0, s>>>(a);
     else attn_fwd_kernel<128, 64, false><<<grid, 512, 0, s>>>(a);

@@ -11,12 +11,12 @@
 // through XOR-swizzled LDS; each 32x32 logit fragment is folded straight into
 // per-lane running maxima; only tiles on the causal diagonal or the ragged
 // end apply a mask, and a wave skips key tiles lying wholly above its causal
-// diagonal. Blocks are issued heaviest causal row first. The block max goes
-// through an order-preserving integer encoding into one atomicMax per block,
-// so the result does not depend on scheduling. MLA keys are [k^C_h | k^R]:
+// diagonal. Blocks are issued heaviest causal row first. The block max, times
+// the scale, is merged by one integer atomic (atomic_max_f32), so the result
+// does not depend on scheduling and needs no finishing pass. MLA keys are [k^C_h | k^R]:
 // the shared rotary key supplies the last d_s dimensions of every head's key
 // (K2 report, per-head MLA clipping). The attention kernel's logit pass
-// applies the same masking and encoding.
+// applies the same masking and merge.
 //
 // The generic kernel (fp32 inputs, or shapes the MFMA kernel does not cover)
 // computes the same definition with one fp32 dot product per pair.
@@ -30,7 +30,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ inline void block_max_commit(float mx, uint32_t* out, float* red) {
+__device__ inline void block_max_commit(float mx, float* out, float scale, float* red) {
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[wave] = mx;
@@ -38,7 +38,7 @@ __device__ inline void block_max_commit(float mx, uint32_t* out, float* red) {
   if (threadIdx.x == 0) {
     float m = red[0];
     for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, red[w]);
-    atomicMax(out, order_enc(m));
+    atomic_max_f32(out, m * scale);
   }
 }
 
@@ -229,7 +229,7 @@ __global__ void __launch_bounds__(256, 3) max_logits_tile_kernel(const MaxLogitA
     else ml_vm_wait<0>();
     __syncthreads();
   }
-  block_max_commit(mx, a.out_enc + h, red);
+  block_max_commit(mx, a.out + h, a.scale, red);
 }
 
 template <bool BF16>
@@ -260,20 +260,12 @@ __global__ void __launch_bounds__(256) max_logits_generic_kernel(const MaxLogitA
     }
     mx = fmaxf(mx, dot);
   }
-  block_max_commit(mx, a.out_enc + h, red);
+  block_max_commit(mx, a.out + h, a.scale, red);
 }
 
-__global__ void max_logits_init_kernel(uint32_t* enc, int H) {
+__global__ void max_logits_init_kernel(float* out, int H) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < H) enc[i] = order_enc(-INFINITY);
-}
-
-__global__ void max_logits_finalize_kernel(uint32_t* enc, float scale, int H) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < H) {
-    const float m = order_dec(enc[i]);
-    reinterpret_cast<float*>(enc)[i] = m * scale;
-  }
+  if (i < H) out[i] = -INFINITY;
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -288,9 +280,9 @@ bool max_logits_mfma_supported(const MaxLogitArgs& a) {
   return true;
 }
 
-hipError_t launch_max_logits_init(uint32_t* enc, int32_t H, hipStream_t s) {
+hipError_t launch_max_logits_init(float* out, int32_t H, hipStream_t s) {
   if (H <= 0) return hipSuccess;
-  max_logits_init_kernel<<<(H + 255) / 256, 256, 0, s>>>(enc, H);
+  max_logits_init_kernel<<<(H + 255) / 256, 256, 0, s>>>(out, H);
   return hipGetLastError();
 }
 
@@ -308,13 +300,13 @@ hipError_t launch_max_logits(const MaxLogitArgs& a, hipStream_t s, bool* used_mf
       // tiles; MHA layer: 140 us against 142 us for the tile kernel below.
       AttnArgs t{};
       t.q = a.q; t.k = a.k; t.ks = a.ks; t.v = a.k;
-      t.smax_enc = a.out_enc;
+      t.smax = a.out;
       t.qs_b = a.qs_b; t.qs_t = a.qs_t; t.qs_h = a.qs_h;
       t.ks_b = a.ks_b; t.ks_t = a.ks_t; t.ks_h = a.ks_h;
       t.kss_b = a.kss_b; t.kss_t = a.kss_t;
       t.vs_b = a.ks_b; t.vs_t = a.ks_t; t.vs_h = a.ks_h;
       t.B = a.B; t.T = a.T; t.H = a.H; t.d_k = a.d_k; t.d_s = a.d_s; t.d_v = 128;
-      t.causal = a.causal; t.scale = 1.0f;
+      t.causal = a.causal; t.scale = a.scale;
       return launch_attention_smax_only(t, s);
     }
     else max_logits_tile_kernel<64><<<grid, 256, 0, s>>>(a);
@@ -326,10 +318,5 @@ hipError_t launch_max_logits(const MaxLogitArgs& a, hipStream_t s, bool* used_mf
   return hipGetLastError();
 }
 
-hipError_t launch_max_logits_finalize(uint32_t* enc, float scale, int32_t H, hipStream_t s) {
-  if (H <= 0) return hipSuccess;
-  max_logits_finalize_kernel<<<(H + 255) / 256, 256, 0, s>>>(enc, scale, H);
-  return hipGetLastError();
-}
 
 }  // namespace mc

@@ -724,11 +724,11 @@ mc_status max_logits_per_head(const void* q, const void* k, const void* k_shared
   a.kss_b = d_shared > 0 ? ks_stride[0] : 0; a.kss_t = d_shared > 0 ? ks_stride[1] : 0;
   a.B = B; a.T = T; a.H = H; a.d_q = d_q; a.d_k = d_k; a.d_s = d_shared;
   a.causal = causal ? 1 : 0; a.bf16 = dtype == MC_BF16;
-  a.out_enc = (uint32_t*)s_max_out;
+  a.out = s_max_out; a.scale = scale;
   hipStream_t s = (hipStream_t)stream;
   {
     Prof pr(F_ML_INIT, s, 0.0, 0.0);
-    hipError_t e = launch_max_logits_init(a.out_enc, H, s);
+    hipError_t e = launch_max_logits_init(a.out, H, s);
     if (e != hipSuccess) return fail(MC_ERR_HIP, "max_logits init: %s", hipGetErrorString(e));
   }
   {
@@ -737,11 +737,6 @@ mc_status max_logits_per_head(const void* q, const void* k, const void* k_shared
     bool mfma = false;
     hipError_t e = launch_max_logits(a, s, &mfma);
     if (e != hipSuccess) return fail(MC_ERR_HIP, "max_logits launch: %s", hipGetErrorString(e));
-  }
-  {
-    Prof pr(F_ML_FIN, s, 0.0, 0.0);
-    hipError_t e = launch_max_logits_finalize(a.out_enc, scale, H, s);
-    if (e != hipSuccess) return fail(MC_ERR_HIP, "max_logits finalize: %s", hipGetErrorString(e));
   }
   return MC_OK;
 }
@@ -781,14 +776,14 @@ mc_status attention_forward(const void* q, const void* k, const void* k_shared, 
   }
   a.B = B; a.T = T; a.H = H; a.d_k = d_k; a.d_s = d_shared; a.d_v = d_v;
   a.causal = causal ? 1 : 0; a.scale = scale;
-  a.lse = lse; a.smax_enc = (uint32_t*)s_max_out;
+  a.lse = lse; a.smax = s_max_out;
   if (!empty && !attention_supported(a))
     return fail(MC_ERR_ALIGN, "attention_forward needs 16-byte aligned q, k, k_shared, v, o and strides that "
                 "are multiples of 8 elements");
   hipStream_t s = (hipStream_t)stream;
   if (s_max_out) {
     Prof pr(F_ML_INIT, s, 0.0, 0.0);
-    hipError_t e = launch_max_logits_init(a.smax_enc, H, s);
+    hipError_t e = launch_max_logits_init(a.smax, H, s);
     if (e != hipSuccess) return fail(MC_ERR_HIP, "s_max init: %s", hipGetErrorString(e));
   }
   if (!empty) {
@@ -796,11 +791,6 @@ mc_status attention_forward(const void* q, const void* k, const void* k_shared, 
     Prof pr(F_ATTN, s, 2.0 * (d_q + d_v) * pairs * B * H, 0.0);
     hipError_t e = launch_attention(a, s);
     if (e != hipSuccess) return fail(MC_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
-  }
-  if (s_max_out) {
-    Prof pr(F_ML_FIN, s, 0.0, 0.0);
-    hipError_t e = launch_max_logits_finalize(a.smax_enc, scale, H, s);
-    if (e != hipSuccess) return fail(MC_ERR_HIP, "s_max finalize: %s", hipGetErrorString(e));
   }
   return MC_OK;
 }

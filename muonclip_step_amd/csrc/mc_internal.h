@@ -234,36 +234,37 @@ struct MaxLogitArgs {
   int64_t kss_b, kss_t;
   int32_t B, T, H, d_q, d_k, d_s;
   int32_t causal, bf16;
-  uint32_t* out_enc;     // [H] ordered-integer encoding of the running max
+  float* out;            // [H] running max of the scaled logits (set to -inf first)
+  float scale;           // applied to each block's max before it is merged
 };
 // true when the MFMA kernel covers this shape (bf16, d_k and d_s supported,
 // 16-byte aligned rows); otherwise the generic kernel runs.
 bool max_logits_mfma_supported(const MaxLogitArgs& a);
-hipError_t launch_max_logits_init(uint32_t* enc, int32_t H, hipStream_t s);
+hipError_t launch_max_logits_init(float* out, int32_t H, hipStream_t s);   // out[h] = -inf
 hipError_t launch_max_logits(const MaxLogitArgs& a, hipStream_t s, bool* used_mfma);
-hipError_t launch_max_logits_finalize(uint32_t* enc, float scale, int32_t H, hipStream_t s);
 
-// Order-preserving map of fp32 onto uint32 (a < b  <=>  enc(a) < enc(b) for
-// non-NaN values), so that integer atomicMax reduces floats.
-__device__ inline uint32_t order_enc(float f) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ inline float order_dec(uint32_t k) {
-  const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
-  return __builtin_bit_cast(float, u);
+// Running maximum of floats in global memory by one integer atomic: a
+// non-negative float orders like its bits as a signed integer, a negative
+// one inversely to its bits as an unsigned integer, so atomicMax on the
+// first and atomicMin on the second keep the larger float whatever the
+// current value (initially -inf). NaN is ignored; -0 counts as +0.
+__device__ inline void atomic_max_f32(float* p, float v) {
+  if (v != v) return;
+  if (v == 0.0f) v = 0.0f;
+  if (v > 0.0f || __float_as_uint(v) == 0u) atomicMax((int*)p, __float_as_int(v));
+  else atomicMin((unsigned int*)p, __float_as_uint(v));
 }
 
 // ---------------------------------------------------------------- attention forward
 
 // Softmax attention of one layer (bf16 in and out), with the per-head max
-// logit taken from the same pass when smax_enc is set. Element strides; the
+// logit taken from the same pass when smax is set. Element strides; the
 // last dimension of every tensor is contiguous.
 struct AttnArgs {
   const void* q; const void* k; const void* ks; const void* v;
   void* o;
   float* lse;            // [B][H][T] natural-log sum of exp(scaled logits), or NULL
-  uint32_t* smax_enc;    // [H] ordered-integer running max of the raw logits, or NULL
+  float* smax;           // [H] running max of the scaled logits (-inf first), or NULL
   int64_t qs_b, qs_t, qs_h;
   int64_t ks_b, ks_t, ks_h;
   int64_t kss_b, kss_t;

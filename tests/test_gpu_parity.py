@@ -369,6 +369,44 @@ def test_max_logits_empty_gives_neg_inf_and_gamma_one():
     assert torch.all(torch.isneginf(out))
 
 
+@pytest.mark.parametrize("dk,ds,dtype", [(128, 0, "bf16"), (128, 64, "bf16"), (64, 0, "bf16"), (16, 0, "f32")])
+def test_max_logits_negative_and_zero(dk, ds, dtype):
+    """Per-head maxima that are negative (every query u, every key -u: all
+    logits -|u|^2 scale) or zero (zero queries: all logits 0, the result +0,
+    not -0 or -inf), next to a head with a positive maximum, through every
+    kernel family; checked against the oracle."""
+    B, T, H = 2, 150, 3
+    print("negative/zero S_max", dk, ds, dtype, flush=True)
+    rng = np.random.default_rng(dk + ds)
+    d = dk + ds
+    q = rng.standard_normal((B, T, H, d))
+    k = rng.standard_normal((B, T, H, dk))
+    ks = rng.standard_normal((B, T, ds)) if ds else None
+    u = rng.standard_normal(d)
+    q[:, :, 0] = u                       # head 0: all logits -|u|^2
+    k[:, :, 0] = -u[:dk]
+    if ds:
+        ks[:] = 0.0                      # (the shared rotary key adds nothing)
+        q[:, :, 0, dk:] = 0.0
+    q[:, :, 1] = 0.0                     # head 1: all logits 0
+    q = wl.quantize_bf16(q) if dtype == "bf16" else wl.quantize_f32(q)
+    k = wl.quantize_bf16(k) if dtype == "bf16" else wl.quantize_f32(k)
+    ks = (wl.quantize_bf16(ks) if dtype == "bf16" else wl.quantize_f32(ks)) if ds else None
+    qd, kd, ksd = qk_to_device(q, k, ks, dtype)
+    scale = 1.0 / math.sqrt(d)
+    got = host64(mc.max_logits_per_head(qd, kd, ksd, causal=True, scale=scale))
+    ref = oracle.max_logits(q, k, ks, True, scale)
+    assert got[0] < 0 and np.isclose(got[0], ref[0], rtol=1e-5, atol=0)
+    assert got[1] == 0.0 and not np.signbit(got[1])
+    assert got[2] > 0 and np.isclose(got[2], ref[2], rtol=1e-3, atol=0)
+    if dk == 128 and dtype == "bf16":   # the same merge inside attention_forward
+        smax = torch.empty(H, dtype=torch.float32, device="cuda")
+        v = torch.zeros(B, T, H, 128, dtype=torch.bfloat16, device="cuda")
+        mc.attention_forward(qd, kd, ksd, v, causal=True, s_max=smax)
+        torch.cuda.synchronize()
+        assert np.array_equal(host64(smax), got)
+
+
 def test_gamma_out_without_matrices_and_with_two_lanes():
     """gamma_out is written once per step: with no matrices at all, and when
     the step's waves run on two streams (two shape groups)."""
