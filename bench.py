@@ -178,7 +178,14 @@ def cpu_baseline(cfg, budget_s):
                 break
         per = (time.perf_counter() - t0) / sl
         ms_smax = per * a.B * a.H * 1e3
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu_model)
+    except OSError:
+        pass
     return {"value": ms_muon + ms_smax, "unit": "ms per step (extrapolated)", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model,
             "sample": f"{done_mats} of {len(cfg.matrices)} matrices through the full fp64 step, scaled by NS "
                       f"FLOPs to all matrices; S_max on {sl} single (sample, head) slices of T={a.T if a else 0},"
                       f" scaled by B*H" if a else f"{done_mats} matrices, scaled by NS FLOPs"}
