@@ -58,11 +58,11 @@ constexpr int kSplitThreshold = 1024;   // m below this: hi/lo operand pairs
 
 enum Family {
   F_MOMENTUM = 0, F_NORM, F_GEMM, F_SPLITK, F_UPDATE, F_GAMMA, F_CLIP,
-  F_ML_INIT, F_ML, F_ML_FIN, F_ADAMW, F_ATTN, F_COUNT
+  F_ML_INIT, F_ML, F_ADAMW, F_ATTN, F_COUNT
 };
 const char* kFamilyNames[F_COUNT] = {"momentum_norm", "norm_finalize", "ns_gemm", "splitk_reduce",
                                      "update_clip", "gamma", "clip_apply", "max_logits_init",
-                                     "max_logits", "max_logits_finalize", "adamw", "attention"};
+                                     "max_logits", "adamw", "attention"};
 
 struct ProfRec { int fam; hipEvent_t a, b; double flops, bytes; };
 std::mutex g_prof_mu;
