@@ -277,6 +277,9 @@ bool max_logits_mfma_supported(const MaxLogitArgs& a) {
   if (!aligned16(a.q) || !aligned16(a.k) || (a.d_s && !aligned16(a.ks))) return false;
   if ((a.qs_b | a.qs_t | a.qs_h | a.ks_b | a.ks_t | a.ks_h) & 7) return false;
   if (a.d_s && ((a.kss_b | a.kss_t) & 7)) return false;
+  // the key tiles' lane offsets (64 rows of the t stride) are 32-bit
+  const int64_t kLimit = (int64_t)1 << 23;
+  if (a.ks_t >= kLimit || (a.d_s && a.kss_t >= kLimit)) return false;
   return true;
 }
 

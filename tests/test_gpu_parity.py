@@ -362,6 +362,22 @@ def test_max_logits_strided_views_and_nan():
     assert np.allclose(got2, want2, rtol=1e-3)
 
 
+def test_max_logits_huge_key_stride():
+    """A key view whose t stride (2^23 elements) exceeds the MFMA kernels'
+    32-bit tile offsets runs the generic kernel and still matches the
+    oracle."""
+    B, T, H, d = 1, 3, 2, 128
+    rng = np.random.default_rng(77)
+    q = wl.quantize_bf16(rng.standard_normal((B, T, H, d)))
+    k = wl.quantize_bf16(rng.standard_normal((B, T, H, d)))
+    big = torch.zeros(T, 1 << 23, dtype=torch.bfloat16, device="cuda")
+    kv = big[:, : H * d].view(T, H, d).unsqueeze(0)          # [1, T, H, d], t stride 2^23
+    kv.copy_(dev_tensor(k, "bf16"))
+    got = host64(mc.max_logits_per_head(dev_tensor(q, "bf16"), kv, None, causal=True))
+    ref = oracle.max_logits(q, k, None, True, 1.0 / math.sqrt(d))
+    assert np.allclose(got, ref, rtol=1e-3, atol=0)
+
+
 def test_max_logits_empty_gives_neg_inf_and_gamma_one():
     q = torch.zeros(0, 4, 2, 128, dtype=torch.bfloat16, device="cuda")
     out = mc.max_logits_per_head(q, q, None, causal=True)
