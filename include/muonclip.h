@@ -72,7 +72,9 @@ typedef struct {
   float expo;
 } mc_segment;
 
-/* One 2-D Muon parameter. W, G and M share rows, cols and ld.
+/* One 2-D Muon parameter. W, G and M share rows, cols and ld. rows and cols
+ * are at most 2^20 and, each rounded up to 64, multiply to less than 2^31
+ * elements (else MC_ERR_SHAPE).
  *   w        param, w_dtype (MC_F32 or MC_BF16), updated in place
  *   g        gradient, g_dtype (MC_F32 or MC_BF16), read only
  *   m        fp32 momentum, updated in place (M_0 = 0 is a zero buffer)

@@ -143,6 +143,10 @@ mc_status check_matrix_common(const mc_matrix& m, int i) {
   if (!m.w) return fail(MC_ERR_NULL, "matrix %d: w is NULL", i);
   if (m.rows <= 0 || m.cols <= 0) return fail(MC_ERR_SHAPE, "matrix %d: rows and cols must be >= 1", i);
   if (m.rows > (1 << 20) || m.cols > (1 << 20)) return fail(MC_ERR_SHAPE, "matrix %d: dimension above 2^20", i);
+  // the Newton-Schulz buffers (rows and cols padded to 64) are addressed
+  // with 32-bit element offsets inside one matrix
+  if (((m.rows + 63) / 64 * 64) * ((m.cols + 63) / 64 * 64) >= ((int64_t)1 << 31))
+    return fail(MC_ERR_SHAPE, "matrix %d: %lld x %lld exceeds 2^31 elements", i, (long long)m.rows, (long long)m.cols);
   if (m.ld < m.cols) return fail(MC_ERR_SHAPE, "matrix %d: ld %lld < cols %lld", i, (long long)m.ld, (long long)m.cols);
   if (!dtype_ok(m.w_dtype)) return fail(MC_ERR_DTYPE, "matrix %d: w_dtype %d", i, m.w_dtype);
   if (!aligned(m.w, dtype_size(m.w_dtype))) return fail(MC_ERR_ALIGN, "matrix %d: w misaligned", i);

@@ -196,3 +196,20 @@ def test_adamw_defaults_and_rejections():
     assert status([vec()], beta2=-0.1) == mc.MC_ERR_HPARAM
     assert status([vec()], eps=-1e-8) == mc.MC_ERR_HPARAM
     assert status([vec()], lr=float("inf")) == mc.MC_ERR_HPARAM
+
+
+def test_matrix_beyond_32bit_offsets_is_rejected():
+    """rows x cols (padded to 64) of 2^31 elements or more is refused before
+    any launch (host-side validation; no device memory is touched)."""
+    import ctypes
+    import muonclip_step_amd as mc
+    lib = mc.load()
+    m = mc.Matrix()
+    m.w = m.g = m.m = 256   # never dereferenced: validation fails first
+    m.rows, m.cols, m.ld = 65536, 32768, 32768
+    m.w_dtype = m.g_dtype = 1
+    m.clip_slot = -1
+    hp = mc.hparams()
+    arr = (mc.Matrix * 1)(m)
+    assert lib.mc_workspace_size(arr, 1, ctypes.byref(hp)) == 0
+    assert b"2^31" in lib.mc_last_error()
