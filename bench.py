@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default: 2, the MHA layer)")
     ap.add_argument("--experts", type=int, default=385, help="expert count for workloads 4/5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--overlap-smax", action="store_true",
+                    help="run the S_max pass on a second stream beside momentum and Newton-Schulz "
+                         "(muonclip_step_overlapped) instead of before the step")
     ap.add_argument("--cpu-sample-s", type=float, default=15.0)
     ap.add_argument("--adamw", action="store_true",
                     help="time the AdamW entry point (the parameters Muon does not cover) on a "
@@ -350,11 +353,25 @@ def main():
     ws = torch.empty(mc.workspace_size(mats, hp), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    def step():
+    side = torch.cuda.Stream()
+    ready = torch.cuda.Event()
+
+    def step(overlap=args.overlap_smax):
         if attn is not None:
             q, k, ks = attn
-            mc.max_logits_per_head(q, k, ks, causal=cfg.attn.causal, out=s_max)
-            mc.muonclip_step(mats, hp, s_max=s_max, slots=1, heads=H, gamma_out=gamma, workspace=ws)
+            if overlap:
+                # S_max on a second stream beside momentum and Newton-Schulz;
+                # only the launches that read it wait for it
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    mc.max_logits_per_head(q, k, ks, causal=cfg.attn.causal, out=s_max)
+                    ready.record(side)
+                mc.muonclip_step(mats, hp, s_max=s_max, slots=1, heads=H, gamma_out=gamma, workspace=ws,
+                                 s_max_ready=ready)
+                torch.cuda.current_stream().wait_stream(side)
+            else:
+                mc.max_logits_per_head(q, k, ks, causal=cfg.attn.causal, out=s_max)
+                mc.muonclip_step(mats, hp, s_max=s_max, slots=1, heads=H, gamma_out=gamma, workspace=ws)
         else:
             mc.muonclip_step(mats, hp, workspace=ws)
 
@@ -374,10 +391,11 @@ def main():
     wall = time.perf_counter() - t_wall
     ms = e0.elapsed_time(e1) / args.steps
 
-    # per-kernel HIP events around every launch of the library (same stream)
+    # per-kernel HIP events around every launch of the library, with the S_max
+    # pass serialised so that no kernel's time includes another's
     mc.profile_enable(True)
     for _ in range(args.steps):
-        step()
+        step(overlap=False)
     torch.cuda.synchronize()
     prof = mc.profile_read()
     mc.profile_enable(False)
@@ -417,6 +435,7 @@ def main():
                    "attention": None if cfg.attn is None else
                    f"B{cfg.attn.B} T{cfg.attn.T} H{cfg.attn.H} d{cfg.attn.d_q} "
                    f"{'causal' if cfg.attn.causal else 'full'} {cfg.attn.kind}",
+                   "smax_pass": "second stream" if args.overlap_smax and cfg.attn else "serial",
                    "parallelism": "single GPU"},
         "ns_tflops_algorithmic": round(ns_total / (ns_ms * 1e-3) / 1e12, 2) if ns_ms else None,
         "ns_gemm_tflops": round(gemm_tflops, 2),

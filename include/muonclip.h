@@ -157,6 +157,21 @@ mc_status muonclip_step(const mc_matrix *mats /* host, n */, int32_t n, const mc
                         const float *s_max, int32_t slots, int32_t heads, float *gamma_out,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* muonclip_step with S_max still being computed on another stream (the step
+ * of Kimi K2 report 2.1 needs S_max only for the QK-Clip that follows the
+ * update, so the S_max pass can run beside momentum and Newton-Schulz).
+ *   s_max_ready  a hipEvent_t the caller recorded, before this call, after the
+ *                launch that writes s_max (e.g. max_logits_per_head on a
+ *                second stream); NULL = exactly muonclip_step
+ * Every launch of the step that reads s_max (the update, or the last
+ * Newton-Schulz product when the update rides on it, and the gamma launch
+ * when n == 0) first makes its stream wait on the event; the launches before
+ * it do not. Arguments, errors and results are those of muonclip_step, bit
+ * for bit. The event is not recorded, reset or destroyed here. */
+mc_status muonclip_step_overlapped(const mc_matrix *mats /* host, n */, int32_t n, const mc_hparams *hp /* host */,
+                                   const float *s_max, int32_t slots, int32_t heads, float *gamma_out,
+                                   void *workspace, size_t workspace_bytes, void *stream, void *s_max_ready);
+
 /* Per-head max attention logit of one attention layer's forward:
  *   s_max_out[h] = scale * max over b < B, i < T, j < T (j <= i if causal) of
  *     q[b,i,h,0:d_k] . k[b,j,h,:] + q[b,i,h,d_k:d_q] . k_shared[b,j,:]

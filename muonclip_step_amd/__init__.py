@@ -21,6 +21,7 @@ MC_OK, MC_ERR_NULL, MC_ERR_SHAPE, MC_ERR_DTYPE, MC_ERR_WORKSPACE, MC_ERR_HPARAM,
 MC_F32, MC_BF16 = 0, 1
 
 EXPORTS = ("mc_default_hparams", "mc_workspace_size", "mc_workspace_min_size", "muonclip_step",
+           "muonclip_step_overlapped",
            "max_logits_per_head", "qk_clip_apply", "mc_last_error", "mc_version",
            "mc_profile_enable", "mc_profile_read", "mc_default_adamw_hparams", "adamw_step",
            "attention_forward")
@@ -86,6 +87,8 @@ def load():
     lib.mc_workspace_min_size.restype = c_size_t
     lib.muonclip_step.argtypes = [MP, c_int32, HP, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.muonclip_step.restype = c_int32
+    lib.muonclip_step_overlapped.argtypes = lib.muonclip_step.argtypes + [c_void_p]
+    lib.muonclip_step_overlapped.restype = c_int32
     lib.max_logits_per_head.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                         c_int32, c_int32, c_int32, POINTER(c_int64), POINTER(c_int64),
                                         POINTER(c_int64), c_int32, c_float, c_void_p, c_void_p]
@@ -182,17 +185,27 @@ def workspace_size(mats, hp: HParams | None = None, minimal: bool = False) -> in
 
 
 def muonclip_step(mats, hp: HParams | None = None, s_max=None, slots: int = 0, heads: int = 0,
-                  gamma_out=None, workspace=None, stream=None):
+                  gamma_out=None, workspace=None, stream=None, s_max_ready=None):
     """One MuonClip step over `mats` (list of Matrix) on the current stream.
-    workspace: a uint8 device tensor (allocated here when None)."""
+    workspace: a uint8 device tensor (allocated here when None).
+    s_max_ready: a torch.cuda.Event recorded after the launch that writes
+    s_max on another stream; only the launches that read s_max wait on it
+    (muonclip_step_overlapped)."""
     lib = load()
     hp = hp or hparams()
     arr, n = _array(mats)
     if workspace is None:
         import torch
         workspace = torch.empty(max(workspace_size(mats, hp), 256), dtype=torch.uint8, device="cuda")
-    _check(lib.muonclip_step(arr, n, ctypes.byref(hp), _ptr(s_max), slots, heads, _ptr(gamma_out),
-                             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    args = (arr, n, ctypes.byref(hp), _ptr(s_max), slots, heads, _ptr(gamma_out),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if s_max_ready is None:
+        _check(lib.muonclip_step(*args))
+    else:
+        ev = s_max_ready if isinstance(s_max_ready, int) else s_max_ready.cuda_event
+        if not ev:
+            raise ValueError("s_max_ready has not been recorded")
+        _check(lib.muonclip_step_overlapped(*args, ctypes.c_void_p(ev)))
     return workspace
 
 

@@ -315,12 +315,21 @@ ClipRule clip_rule(const mc_matrix& m, bool clip_on) {
   return c;
 }
 
+// Launches that read s_max first make their stream wait for the caller's
+// event (recorded after the launch that writes s_max); momentum and the
+// Newton-Schulz products before them do not wait.
+mc_status wait_smax(hipEvent_t ev, const float* s_max, hipStream_t s) {
+  if (!ev || !s_max) return MC_OK;
+  hipError_t e = hipStreamWaitEvent(s, ev, 0);
+  return e == hipSuccess ? MC_OK : fail(MC_ERR_HIP, "wait on s_max_ready: %s", hipGetErrorString(e));
+}
+
 // gamma_once: when it points at a non-NULL gamma output, the first update
 // launch of this wave also writes gamma [slots][heads] and the pointer is
 // cleared, so exactly one launch of the step writes it.
 mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb, const mc_hparams& hp,
                    const float* s_max, int32_t heads, char* ws, hipStream_t s, float** gamma_once,
-                   int32_t slots) {
+                   int32_t slots, hipEvent_t smax_ready) {
   const WavePlan w = plan_wave(g, nb);
   const int64_t mp = g.mp, np = g.np;
   // X ping-pong: iteration it reads X[it % 2] and writes X[(it + 1) % 2]
@@ -460,6 +469,10 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
       a.epi.alpha = 1.0f; a.epi.scale_pow = first ? 1 : 0; a.epi.scale = scale;
       a.epi.out_hi = x_nxt; a.epi.ld_hi = (int32_t)np; a.epi.bs_hi = mp * np;
       const bool last = it + 1 == hp.ns_steps;
+      if (last && fu.n > 0) {
+        mc_status ws_ = wait_smax(smax_ready, s_max, s);
+        if (ws_) return ws_;
+      }
       if (last && fu.n > 0 && gamma_once && *gamma_once) {
         fu.gamma_out = *gamma_once; fu.gamma_slots = slots;
         *gamma_once = nullptr;
@@ -473,6 +486,7 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
   if (fu.n > 0) return MC_OK;
 
   // 3. update + decay + QK-Clip rows
+  if (mc_status ws_ = wait_smax(smax_ready, s_max, s)) return ws_;
   uint16_t* x_final = X[hp.ns_steps & 1];   // O in [m][n]: W itself (wide) or W^T (tall)
   for (int b0 = 0; b0 < nb; b0 += kMaxBatchMats) {
     UpdArgs a{};
@@ -605,9 +619,10 @@ size_t mc_workspace_min_size(const mc_matrix* mats, int32_t n, const mc_hparams*
   return workspace_for(mats, n, hp, true);
 }
 
-mc_status muonclip_step(const mc_matrix* mats, int32_t n, const mc_hparams* hp, const float* s_max,
-                        int32_t slots, int32_t heads, float* gamma_out, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+// muonclip_step with an optional event that the launches reading s_max wait on.
+static mc_status step_impl(const mc_matrix* mats, int32_t n, const mc_hparams* hp, const float* s_max,
+                           int32_t slots, int32_t heads, float* gamma_out, void* workspace, size_t workspace_bytes,
+                           void* stream, hipEvent_t smax_ready) {
   mc_status st = check_hparams(hp);
   if (st) return st;
   const bool have_smax = s_max != nullptr;
@@ -619,6 +634,7 @@ mc_status muonclip_step(const mc_matrix* mats, int32_t n, const mc_hparams* hp, 
   if (st) return st;
   if (n == 0) {   // nothing to update; gamma is still an output
     if (gamma_out) {
+      if ((st = wait_smax(smax_ready, s_max, (hipStream_t)stream))) return st;
       Prof pr(F_GAMMA, (hipStream_t)stream, 0.0, 0.0);
       hipError_t e = launch_gamma(s_max, gamma_out, slots, heads, hp->tau, hp->clip_global, (hipStream_t)stream);
       if (e != hipSuccess) return fail(MC_ERR_HIP, "gamma launch: %s", hipGetErrorString(e));
@@ -669,7 +685,7 @@ mc_status muonclip_step(const mc_matrix* mats, int32_t n, const mc_hparams* hp, 
   if (!two) {
     for (const Chain& c : chains) {
       st = run_wave(mats, groups[c.gi], groups[c.gi].idx.data() + c.b0, c.nb, *hp, s_max, heads, (char*)workspace, s,
-                    &gamma_once, slots);
+                    &gamma_once, slots, smax_ready);
       if (st) return st;
     }
     return MC_OK;
@@ -687,7 +703,7 @@ mc_status muonclip_step(const mc_matrix* mats, int32_t n, const mc_hparams* hp, 
     const int lane = load[1] < load[0] ? 1 : 0;
     load[lane] += c.flops;
     st = run_wave(mats, groups[c.gi], groups[c.gi].idx.data() + c.b0, c.nb, *hp, s_max, heads,
-                  (char*)workspace + lane * half, lane ? aux->s : s, &gamma_once, slots);
+                  (char*)workspace + lane * half, lane ? aux->s : s, &gamma_once, slots, smax_ready);
     if (st) break;
   }
   // join: `stream` continues only after the auxiliary stream's work (also
@@ -695,6 +711,19 @@ mc_status muonclip_step(const mc_matrix* mats, int32_t n, const mc_hparams* hp, 
   if (hipEventRecord(aux->join, aux->s) != hipSuccess || hipStreamWaitEvent(s, aux->join, 0) != hipSuccess)
     return st ? st : fail(MC_ERR_HIP, "stream join failed");
   return st;
+}
+
+mc_status muonclip_step(const mc_matrix* mats, int32_t n, const mc_hparams* hp, const float* s_max,
+                        int32_t slots, int32_t heads, float* gamma_out, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return step_impl(mats, n, hp, s_max, slots, heads, gamma_out, workspace, workspace_bytes, stream, nullptr);
+}
+
+mc_status muonclip_step_overlapped(const mc_matrix* mats, int32_t n, const mc_hparams* hp, const float* s_max,
+                                   int32_t slots, int32_t heads, float* gamma_out, void* workspace,
+                                   size_t workspace_bytes, void* stream, void* s_max_ready) {
+  return step_impl(mats, n, hp, s_max, slots, heads, gamma_out, workspace, workspace_bytes, stream,
+                   (hipEvent_t)s_max_ready);
 }
 
 mc_status max_logits_per_head(const void* q, const void* k, const void* k_shared, int32_t dtype, int32_t B, int32_t T,

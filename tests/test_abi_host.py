@@ -69,6 +69,26 @@ def step_status(mats, hp=None, s_max=None, slots=0, heads=0, gamma=None, ws=0x40
     return lib.muonclip_step(arr, len(mats), ctypes.byref(hp), s_max, slots, heads, gamma, ws, ws_bytes, None)
 
 
+def test_overlapped_step_validates_like_the_step():
+    """muonclip_step_overlapped runs the step's argument checks before any
+    launch or event wait: the same status for the same bad arguments."""
+    lib = mc.load()
+
+    def both(mats, hp=None, ws=0x400000, ws_bytes=1 << 40):
+        hp = hp or mc.hparams()
+        arr = (mc.Matrix * max(1, len(mats)))(*mats)
+        a = lib.muonclip_step(arr, len(mats), ctypes.byref(hp), None, 0, 0, None, ws, ws_bytes, None)
+        b = lib.muonclip_step_overlapped(arr, len(mats), ctypes.byref(hp), None, 0, 0, None, ws, ws_bytes, None,
+                                         0x600000)
+        return a, b
+
+    for args, want in [(([fake_matrix(64, 0)],), mc.MC_ERR_SHAPE),
+                       (([fake_matrix(64, 64)], mc.hparams(ns_steps=0)), mc.MC_ERR_HPARAM),
+                       (([fake_matrix(64, 64)], None, None), mc.MC_ERR_WORKSPACE),
+                       (([fake_matrix(64, 64)], None, 0x400000, 1024), mc.MC_ERR_WORKSPACE)]:
+        assert both(*args) == (want, want)
+
+
 def test_step_rejects_bad_arguments():
     assert step_status([fake_matrix(64, 0)]) == mc.MC_ERR_SHAPE
     assert step_status([fake_matrix(64, 64, ld=32)]) == mc.MC_ERR_SHAPE

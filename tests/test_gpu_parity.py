@@ -518,3 +518,78 @@ def test_update_fused_into_last_apply_is_bit_identical(case):
     # and the padding past each row stayed untouched
     for s in states:
         assert torch.all(s.w_full[:, s.spec.cols:].cpu() == 0)
+
+
+# ----------------------------------------------------------------- S_max on another stream
+
+def _smax_then_step(states, hp, attn, heads, slots, overlapped, with_o):
+    """S_max of `attn` then one step; with `overlapped` the S_max pass runs on
+    a second stream and only the launches that read it wait (the event)."""
+    q, k, ks, causal = attn
+    _fresh(states)
+    descs = [s.desc(with_o=with_o) for s in states]
+    ws = torch.empty(max(mc.workspace_size(descs, hp), 256), dtype=torch.uint8, device="cuda")
+    s_max = torch.full((slots * heads,), -5.0, dtype=torch.float32, device="cuda")
+    gam = torch.full((slots * heads,), -7.0, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    if overlapped:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for sl in range(slots):
+                mc.max_logits_per_head(q, k, ks, causal=causal, out=s_max[sl * heads:(sl + 1) * heads])
+            ready = torch.cuda.Event()
+            ready.record(side)
+        mc.muonclip_step(descs, hp, s_max=s_max, slots=slots, heads=heads, gamma_out=gam, workspace=ws,
+                         s_max_ready=ready)
+        torch.cuda.current_stream().wait_stream(side)
+    else:
+        for sl in range(slots):
+            mc.max_logits_per_head(q, k, ks, causal=causal, out=s_max[sl * heads:(sl + 1) * heads])
+        mc.muonclip_step(descs, hp, s_max=s_max, slots=slots, heads=heads, gamma_out=gam, workspace=ws)
+    torch.cuda.synchronize()
+    return ([(s.w.cpu().clone(), s.m.cpu().clone()) for s in states], gam.cpu(), s_max.cpu())
+
+
+@pytest.mark.parametrize("case", ["mha_layer", "two_lanes_with_o"])
+def test_step_overlapped_with_smax_pass_is_bit_identical(case):
+    """muonclip_step_overlapped with S_max computed on a second stream gives
+    bit for bit the weights, momenta, gamma and S_max of S_max followed by
+    muonclip_step on one stream: the MHA layer (update inside the last apply,
+    one lane) and the tiny layer's two shape groups on two lanes with O
+    requested (separate update kernel)."""
+    print("overlapped step case", case, flush=True)
+    cfg = wl.config(2 if case == "mha_layer" else 1)
+    states = load_config_states(cfg)
+    q, k, ks = wl.draw_attention_inputs(cfg, weights_of(cfg))
+    if case == "mha_layer":
+        qd, kd, ksd = qk_to_device(q, k, ks, "bf16")
+    else:
+        qd, kd, ksd = qk_to_device(q, k, ks, "f32")
+    attn = (qd, kd, ksd, cfg.attn.causal)
+    hp = hp_for(cfg, lr=0.02)
+    with_o = case != "mha_layer"
+    base = _smax_then_step(states, hp, attn, cfg.attn.H, 1, False, with_o)
+    over = _smax_then_step(states, hp, attn, cfg.attn.H, 1, True, with_o)
+    for (w0, m0), (w1, m1) in zip(base[0], over[0]):
+        assert torch.equal(w0, w1) and torch.equal(m0, m1)
+    assert torch.equal(base[1], over[1]) and torch.equal(base[2], over[2])
+    assert torch.all(base[1] <= 1.0) and torch.all(base[1] > 0.0)
+
+
+def test_step_overlapped_without_matrices_writes_gamma():
+    """With no matrices the overlapped step still writes gamma from the
+    S_max the event guards."""
+    s = torch.tensor([50.0, 400.0, -3.0, 100.0], dtype=torch.float32, device="cuda")
+    want = oracle.clip_factor(host64(s), 100.0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    s2 = torch.empty_like(s)
+    with torch.cuda.stream(side):
+        s2.copy_(s)
+        ready = torch.cuda.Event()
+        ready.record(side)
+    g = torch.full((4,), -7.0, dtype=torch.float32, device="cuda")
+    mc.muonclip_step([], mc.hparams(tau=100.0), s_max=s2, slots=1, heads=4, gamma_out=g, s_max_ready=ready)
+    torch.cuda.synchronize()
+    assert np.allclose(host64(g), want, rtol=1e-6, atol=0)
