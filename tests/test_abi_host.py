@@ -233,3 +233,16 @@ def test_matrix_beyond_32bit_offsets_is_rejected():
     arr = (mc.Matrix * 1)(m)
     assert lib.mc_workspace_size(arr, 1, ctypes.byref(hp)) == 0
     assert b"2^31" in lib.mc_last_error()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus N > 1 exits with status 2 and a
+    message before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
