@@ -104,18 +104,6 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return out
 
 
-def bf16_bits(x_bf16_valued: np.ndarray) -> np.ndarray:
-    """uint16 bit patterns of values that are already on the bf16 grid."""
-    v = np.asarray(x_bf16_valued, dtype=np.float64).astype(np.float32)
-    return (v.view(np.uint32) >> 16).astype(np.uint16)
-
-
-def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
-    """fp64 values of uint16 bfloat16 bit patterns (exact)."""
-    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
-    return b.view(np.float32).astype(np.float64)
-
-
 # ---------------------------------------------------------------------------
 # the Muon part of the step
 # ---------------------------------------------------------------------------

@@ -141,6 +141,54 @@ def test_update_step_order_against_hand_expansion():
     assert np.allclose(w_new, want, rtol=0, atol=1e-12)
 
 
+def _clip_by_hand(w, gamma, period, segments):
+    """Row-block rescale written out row by row: row r of head h = r // period
+    at offset r % period inside a segment (off, len, expo) is multiplied by
+    gamma_h ** expo (essay, MHA sqrt(gamma) equations and the MLA table)."""
+    out = np.array(w, np.float64, copy=True)
+    for r in range(out.shape[0]):
+        h, o = divmod(r, period)
+        for off, ln, ex in segments:
+            if off <= o < off + ln:
+                out[r, :] = out[r, :] * gamma[h] ** ex
+    return out
+
+
+@pytest.mark.parametrize("segments,period", [(((0, 4, 0.5),), 4), (((0, 3, 0.5), (3, 2, 1.0)), 6)])
+def test_clip_runs_after_the_update(segments, period):
+    # The clip rescales the weights once the optimizer update is done (essay,
+    # section on why neither a logit soft-cap nor QK-Norm is used; K2 report,
+    # "Taming Muon with QK-Clip": the rescale is post-update). Expected value:
+    # the Moonlight update with the closed-form NS, then the row rescale by
+    # hand. A plausible mistake, clipping W before the update (so that the
+    # update term escapes the clip), must not pass the same check.
+    rng = np.random.default_rng(31)
+    heads = 3
+    rows, cols = heads * period, 11
+    w = rng.standard_normal((rows, cols))
+    g = rng.standard_normal((rows, cols))
+    m = rng.standard_normal((rows, cols))
+    lr, mu, wd = 0.05, 0.9, 0.1
+    gamma = np.array([0.3, 1.0, 0.05])
+    kw = dict(lr=lr, mu=mu, weight_decay=wd, w_dtype="f64", period=period, segments=segments)
+    w_clip, m_clip, o_clip = oracle.muonclip_step_matrix(w, g, m, gamma=gamma, **kw)
+    w_free, m_free, o_free = oracle.muonclip_step_matrix(w, g, m, gamma=None, **kw)
+    # the clip touches neither the momentum nor the orthogonalised update
+    assert np.array_equal(m_clip, m_free) and np.array_equal(o_clip, o_free)
+    upd = 0.2 * math.sqrt(max(rows, cols)) * closed_form_ns(mu * m + g)
+    want = _clip_by_hand(w - lr * upd - lr * wd * w, gamma, period, segments)
+    assert np.allclose(w_clip, want, rtol=0, atol=1e-12)
+    # composition: the clipped step is the clip of the unclipped step
+    assert np.array_equal(w_clip, oracle.qk_clip_rows(w_free, gamma, period, segments))
+    # planted wrong order: clip first, then the update
+    w_pre = _clip_by_hand(w, gamma, period, segments)
+    wrong = w_pre - lr * upd - lr * wd * w_pre
+    assert not np.allclose(wrong, want, rtol=0, atol=1e-6)
+    assert np.abs(wrong - w_clip).max() > 1e-3
+    # heads with gamma = 1 and rows outside every segment are the same either way
+    assert np.array_equal(w_clip[period:2 * period], w_free[period:2 * period])
+
+
 # ---------------------------------------------------------------- S_max
 
 def _tiny_qk(rng, B, T, H, dk, ds):
