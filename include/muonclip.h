@@ -137,7 +137,14 @@ size_t mc_workspace_size(const mc_matrix *mats /* host, n */, int32_t n, const m
  * (one matrix of the largest shape group in flight). */
 size_t mc_workspace_min_size(const mc_matrix *mats /* host, n */, int32_t n, const mc_hparams *hp /* host */);
 
-/* One MuonClip step over n matrices (host array `mats`).
+/* One MuonClip step over n matrices (host array `mats`): Algorithm 1 of the
+ * K2 report (only its caption survives in the report translation, section 2.1
+ * "MuonClip: stable training by weight clipping"), assembled from the Muon
+ * update paragraph of the K2 report (the 0.2 sqrt(max(rows, cols)) RMS
+ * factor), Notes on Moonlight "Background" (M <- mu M + G) and "Scaling up
+ * Muon" (decoupled decay W <- W - lr (U + weight_decay W)), Notes on Muon blog
+ * "Algorithm" (five quintic Newton-Schulz steps) and the essay's per-head
+ * clip applied to the updated weights.
  *   s_max      fp32 [slots][heads] per-head max logits of this step's forward
  *              (max_logits_per_head); NULL = no QK-Clip this step
  *   gamma_out  optional fp32 [slots][heads] receiving gamma = min(1, tau/S)
@@ -172,7 +179,10 @@ mc_status muonclip_step_overlapped(const mc_matrix *mats /* host, n */, int32_t 
                                    const float *s_max, int32_t slots, int32_t heads, float *gamma_out,
                                    void *workspace, size_t workspace_bytes, void *stream, void *s_max_ready);
 
-/* Per-head max attention logit of one attention layer's forward:
+/* Per-head max attention logit of one attention layer's forward (the essay's
+ * S_max^h equation, section on Muon and attention logits: the largest
+ * Q_i^h . K_j^h / sqrt(d) over the batch and over token pairs; the report
+ * translation, section 2.1, defines the same quantity per head):
  *   s_max_out[h] = scale * max over b < B, i < T, j < T (j <= i if causal) of
  *     q[b,i,h,0:d_k] . k[b,j,h,:] + q[b,i,h,d_k:d_q] . k_shared[b,j,:]
  * q: [B,T,H,d_q] with element strides q_stride = {b, t, h} (last dim
@@ -224,7 +234,12 @@ mc_status attention_forward(const void *q, const void *k, const void *k_shared, 
                             int32_t causal, float scale, void *stream);
 
 /* QK-Clip alone on existing weights (the clip part of muonclip_step without
- * the Muon update): for every matrix with clip_slot >= 0, rows in its
+ * the Muon update). gamma_h = min(1, tau / S_max^h) as in the essay's gamma
+ * equation, with the guard of its MHA code sample (1 when S_max^h is not
+ * positive); MHA rows of W_q and W_k scale by sqrt(gamma_h) (the essay's MHA
+ * equations), MLA q^C and k^C rows by sqrt(gamma_h), q^R rows by gamma_h and
+ * the shared k^R not at all (the essay's MLA table; report translation 2.1).
+ * For every matrix with clip_slot >= 0, rows in its
  * segments are scaled by gamma_h ** expo, gamma from s_max[slots][heads] and
  * tau (per head; the all-head variant is muonclip_step's clip_global); rows
  * whose factor is exactly 1 are not touched (bit-identical). Uses w, w_dtype,

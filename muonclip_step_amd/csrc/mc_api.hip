@@ -33,6 +33,29 @@
 
 using namespace mc;
 
+namespace mc {
+
+// Compute units of the current device, read once per device; 256 (MI355X)
+// when the runtime cannot tell (no device: host-only workspace queries).
+int device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) { (void)hipGetLastError(); return 256; }
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  cache[dev] = cus;
+  return cus;
+}
+
+}  // namespace mc
+
 namespace {
 
 thread_local std::string g_err;
@@ -51,7 +74,6 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 inline int64_t round64(int64_t x) { return (x + 63) / 64 * 64; }
 constexpr int kWaveCap = 64;
-constexpr int kCUs = 256;
 constexpr int kSplitThreshold = 1024;   // m below this: hi/lo operand pairs
 
 // ---------------------------------------------------------------- profiling
@@ -204,7 +226,7 @@ struct GemmPlan { GemmTile tile; int tiles_m, tiles_n, splits, kt_per_split; siz
 // cover at least half the CUs, else 128x128 (64x64 below 128 rows);
 // K is split only when the tiles alone cannot fill the chip, keeping every
 // split at least 8 k-stages long. Symmetric products count upper tiles only.
-GemmPlan plan_gemm(int64_t M, int64_t N, int ktiles, int batch, bool sym, bool reads_cin = false,
+GemmPlan plan_gemm(int cus, int64_t M, int64_t N, int ktiles, int batch, bool sym, bool reads_cin = false,
                    bool pair_out = false) {
   GemmPlan p{};
   auto count = [&](int d) {
@@ -216,7 +238,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int ktiles, int batch, bool sym, bool r
   // epilogue also reads A) included since launches of at most one tile per
   // CU run eight waves per tile (measured against 128 tiles: 4 x 2048^2
   // chains 2.5 % faster, MLA layer step 5 % faster)
-  const int need256 = kCUs / 2;
+  const int need256 = cus / 2;
   // (the 256 tile of the Poly step with a hi/lo output pair needs more
   // registers than a wave has, so that case stays on 128 tiles)
   if (M >= 256 && N >= 256 && count(256) >= need256 && !(reads_cin && pair_out)) p.tile = TILE_256;
@@ -227,13 +249,13 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int ktiles, int batch, bool sym, bool r
   p.tiles_n = (int)((N + d - 1) / d);
   const int tiles = count(d);
   int splits = 1;
-  if (tiles < kCUs / 2 && ktiles >= 16) {
+  if (tiles < cus / 2 && ktiles >= 16) {
     // split-K runs the full (non-symmetric) tile set
     const int full = p.tiles_m * p.tiles_n * batch;
     // one wave of work items: a second wave of smaller splits measured
     // slower, its extra fp32 partials costing the finish more than the
     // better balance gained (MLA layer 9.29 -> 9.23 ms)
-    splits = std::min((kCUs + full - 1) / full, ktiles / 8);
+    splits = std::min((cus + full - 1) / full, ktiles / 8);
     splits = std::max(splits, 1);
   }
   p.kt_per_split = (ktiles + splits - 1) / splits;
@@ -255,7 +277,7 @@ struct WavePlan {
   bool frag;
 };
 
-WavePlan plan_wave(const Group& g, int nb) {
+WavePlan plan_wave(const Group& g, int nb, int cus) {
   WavePlan w{};
   w.nb = nb;
   const size_t mp = (size_t)g.mp, np = (size_t)g.np;
@@ -264,9 +286,9 @@ WavePlan plan_wave(const Group& g, int nb) {
   w.kt_gram = (int)(np / kGemmBK);
   w.kt_poly = (int)(mp / kGemmBK) * (g.split ? 3 : 1);
   w.kt_apply = (int)(mp / kGemmBK) * (g.split ? 2 : 1);
-  w.gram = plan_gemm(g.mp, g.mp, w.kt_gram, nb, true);
-  w.poly = plan_gemm(g.mp, g.mp, w.kt_poly, nb, true, true, g.split);
-  w.apply = plan_gemm(g.mp, g.np, w.kt_apply, nb, false);
+  w.gram = plan_gemm(cus, g.mp, g.mp, w.kt_gram, nb, true);
+  w.poly = plan_gemm(cus, g.mp, g.mp, w.kt_poly, nb, true, true, g.split);
+  w.apply = plan_gemm(cus, g.mp, g.np, w.kt_apply, nb, false);
   w.frag = !g.split && w.gram.tile == w.poly.tile && w.gram.splits == 1 && w.poly.splits == 1;
   w.off_x0 = take(nb * mp * np * 2);
   w.off_x1 = take(nb * mp * np * 2);
@@ -330,7 +352,8 @@ mc_status wait_smax(hipEvent_t ev, const float* s_max, hipStream_t s) {
 mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb, const mc_hparams& hp,
                    const float* s_max, int32_t heads, char* ws, hipStream_t s, float** gamma_once,
                    int32_t slots, hipEvent_t smax_ready) {
-  const WavePlan w = plan_wave(g, nb);
+  const int cus = device_cus();
+  const WavePlan w = plan_wave(g, nb, cus);
   const int64_t mp = g.mp, np = g.np;
   // X ping-pong: iteration it reads X[it % 2] and writes X[(it + 1) % 2]
   uint16_t* X[2] = {(uint16_t*)(ws + w.off_x0), (uint16_t*)(ws + w.off_x1)};
@@ -529,8 +552,9 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
 
 int largest_wave(const Group& g, int limit, size_t ws_bytes) {
   int best = 0;
+  const int cus = device_cus();
   for (int nb = 1; nb <= limit; ++nb)
-    if (plan_wave(g, nb).bytes <= ws_bytes) best = nb;
+    if (plan_wave(g, nb, cus).bytes <= ws_bytes) best = nb;
   return best;
 }
 
@@ -605,7 +629,7 @@ static size_t workspace_for(const mc_matrix* mats, int32_t n, const mc_hparams* 
   for (const Group& g : groups) {
     const int nb = minimal ? 1 : std::min<int>((int)g.idx.size(), kWaveCap);
     cap.push_back(nb);
-    best = std::max(best, plan_wave(g, nb).bytes);
+    best = std::max(best, plan_wave(g, nb, device_cus()).bytes);
   }
   // room for two chains in flight when the step has more than one shape group
   if (!minimal && groups.size() >= 2) best = 2 * align_up(best);
@@ -650,7 +674,7 @@ static mc_status step_impl(const mc_matrix* mats, int32_t n, const mc_hparams* h
     wave_cap[gi] = largest_wave(g, std::min<int>((int)g.idx.size(), kWaveCap), workspace_bytes);
     if (wave_cap[gi] == 0)
       return fail(MC_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for one %lldx%lld matrix", workspace_bytes,
-                  plan_wave(g, 1).bytes, (long long)g.m, (long long)g.n);
+                  plan_wave(g, 1, device_cus()).bytes, (long long)g.m, (long long)g.n);
   }
   // Two lanes (the caller's stream and the library's auxiliary stream, each
   // with half the workspace) when there are at least two shape groups and

@@ -7,6 +7,11 @@
 
 namespace mc {
 
+// Compute units of the current HIP device (cached per device; 256 when no
+// device answers). Tile sizes, split-K counts and the wave layout of the
+// Newton-Schulz products are planned against it.
+int device_cus();
+
 // ---------------------------------------------------------------- bf16 bits
 
 // fp32 -> bf16 with round-to-nearest-even: gfx950's v_cvt_pk_bf16_f32 (NaN
