@@ -6,14 +6,18 @@ muonclip_step (momentum, Newton-Schulz, RMS-matched decoupled update, QK-Clip)
 over every 2-D parameter of the workload. Inputs are resident in HBM before
 the timed region starts.
 
-Default workload: the MHA layer (W_q, W_k, W_v, W_o 2048x2048 bf16 with fp32
-momentum; S_max over 4 x 4096 causal tokens, 16 heads of 128).
+Default workload: one full K2-shaped layer (MLA attention with 64 heads of
+192/128, S_max over one causal sequence of 32768 tokens; the five MLA
+projections, the dense 7168 x 18432 FFN and 385 experts of 7168 x 2048 /
+2048 x 7168, 1163 bf16 matrices with fp32 momentum). --config 2 is the MHA
+layer, 3 the MLA layer, 4 the experts alone, 1 the tiny fp32 case.
 
-Prints one JSON line. `value` is the step time in ms (lower is better); the
-same line carries the Newton-Schulz TFLOP/s, S_max Glogits/s, elementwise
-GB/s, the roofline of the dominant kernel (the NS GEMM) measured with HIP
-events around every launch of the library, and the fp64 oracle timed on the
-host cores on a bounded sample.
+Prints one JSON line. `value` is the median step time in ms over the timed
+steps (lower is better); the same line carries the Newton-Schulz TFLOP/s,
+S_max Glogits/s and its fraction of the MFMA peak, elementwise GB/s, the
+roofline of the dominant kernel (the NS GEMM) measured with HIP events around
+every launch of the library in a second pass that runs one lane, and the fp64
+oracle timed on the host cores on a bounded sample.
 """
 from __future__ import annotations
 
@@ -32,12 +36,17 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
 
+def smax_peak_glogits(d_q: int) -> float:
+    """Logits per second at the bf16 MFMA peak: 2 d_q FLOPs per logit."""
+    return PEAK_BF16_TFLOPS * 1e12 / (2.0 * d_q) / 1e9
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default: 2, the MHA layer)")
+    ap.add_argument("--config", type=int, default=5, help="workload 1..5 (default: 5, the full K2-shaped layer)")
     ap.add_argument("--experts", type=int, default=385, help="expert count for workloads 4/5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--overlap-smax", action="store_true",
@@ -135,10 +144,12 @@ def build_workload(cfg, dev):
     return mats, keep, attn
 
 
-def cpu_baseline(cfg, budget_s):
+def cpu_baseline(cfg, budget_s, dev=None):
     """The fp64 oracle on a bounded sample of the same workload, scaled to a
     full step: whole matrices (momentum -> NS -> update -> clip) until the
-    budget is spent, and S_max of a few (sample, head) slices."""
+    budget is spent (the first device-drawn matrix first, copied to the host,
+    then the host-drawn ones, smallest first), and S_max of a few (sample,
+    head) slices."""
     import numpy as np
 
     import oracle
@@ -151,12 +162,19 @@ def cpu_baseline(cfg, budget_s):
     hp = cfg.hparams
     t_mat, done_mats, flops_done = 0.0, 0, 0.0
     total_flops = sum(ns_flops(s.rows, s.cols, hp["ns_steps"]) for s in cfg.matrices)
-    order = [i for i, s in enumerate(cfg.matrices) if not s.device_drawn] or [0]
+    order = sorted((i for i, s in enumerate(cfg.matrices) if not s.device_drawn),
+                   key=lambda i: ns_flops(cfg.matrices[i].rows, cfg.matrices[i].cols, hp["ns_steps"]))
+    first_dev = next((i for i, s in enumerate(cfg.matrices) if s.device_drawn), None)
+    if first_dev is not None and dev is not None:
+        order = [first_dev] + order
     for i in order:
         s = cfg.matrices[i]
         if s.device_drawn:
-            break
-        w, g, m = wl.draw_weight(cfg, i), wl.draw_grad(cfg, i), wl.draw_momentum(cfg, i)
+            wd, gd, md = wl.draw_device_tensors(cfg, i, dev)
+            w, g, m = wd.float().cpu().numpy(), gd.cpu().numpy(), md.cpu().numpy()
+            del wd, gd, md
+        else:
+            w, g, m = wl.draw_weight(cfg, i), wl.draw_grad(cfg, i), wl.draw_momentum(cfg, i)
         t0 = time.perf_counter()
         oracle.muonclip_step_matrix(w.astype(np.float64), g.astype(np.float64), m.astype(np.float64),
                                     lr=hp["lr"], mu=hp["mu"], weight_decay=hp["weight_decay"],
@@ -380,26 +398,33 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps: every step's time, back to back
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         step()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1) / args.steps
+    step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    ms = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (step_ms[len(step_ms) // 2 - 1] +
+                                                                     step_ms[len(step_ms) // 2])
+    ms_mean = ev[0].elapsed_time(ev[-1]) / args.steps
+    print(f"[bench] median step {ms:.3f} ms; profiling one more pass per kernel", file=sys.stderr, flush=True)
 
     # per-kernel HIP events around every launch of the library, with the S_max
-    # pass serialised so that no kernel's time includes another's
+    # pass serialised and the step on one lane (the library does that while
+    # profiling), so that no kernel's time includes another's
+    prof_steps = min(args.steps, 5) if args.config in (4, 5) else args.steps
     mc.profile_enable(True)
-    for _ in range(args.steps):
+    for _ in range(prof_steps):
         step(overlap=False)
     torch.cuda.synchronize()
     prof = mc.profile_read()
     mc.profile_enable(False)
-    per_step = {k: {"ms": v["ms"] / args.steps, "launches": v["launches"] // args.steps} for k, v in prof.items()}
+    per_step = {k: {"ms": v["ms"] / prof_steps, "launches": v["launches"] // prof_steps} for k, v in prof.items()}
     g = prof.get("ns_gemm", {"ms": float("nan"), "flops": 0.0, "launches": 1})
     gemm_tflops = g["flops"] / (g["ms"] * 1e-3) / 1e12 if g["ms"] else float("nan")
     ml = prof.get("max_logits")
@@ -407,16 +432,16 @@ def main():
     if cfg.attn is not None:
         a = cfg.attn
         n_logits = a.B * a.H * (a.T * (a.T + 1) // 2 if a.causal else a.T * a.T)
-    smax_glogits = (n_logits * args.steps / (ml["ms"] * 1e-3) / 1e9) if ml and ml["ms"] else None
+    smax_glogits = (n_logits * prof_steps / (ml["ms"] * 1e-3) / 1e9) if ml and ml["ms"] else None
     ew_bytes = sum(prof[k]["bytes"] for k in ("momentum_norm", "update_clip") if k in prof)
     ew_ms = sum(prof[k]["ms"] for k in ("momentum_norm", "update_clip") if k in prof)
     ew_gbs = ew_bytes / (ew_ms * 1e-3) / 1e9 if ew_ms else None
     ns_total = sum(ns_flops(s.rows, s.cols, hp.ns_steps) for s in cfg.matrices)
-    ns_ms = sum(prof[k]["ms"] for k in ("ns_gemm", "splitk_reduce", "norm_finalize") if k in prof) / args.steps
+    ns_ms = sum(prof[k]["ms"] for k in ("ns_gemm", "splitk_reduce", "norm_finalize") if k in prof) / prof_steps
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on a host sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(cfg, args.cpu_sample_s)
+        cpu = cpu_baseline(cfg, args.cpu_sample_s, dev)
     out = {
         "metric": METRIC,
         "value": round(ms, 4),
@@ -425,6 +450,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_mean": round(ms_mean, 4),
+        "ms_per_step_min_max": [round(step_ms[0], 4), round(step_ms[-1], 4)],
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -441,12 +468,16 @@ def main():
         "ns_gemm_tflops": round(gemm_tflops, 2),
         "ns_mfma_frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
         "smax_glogits_s": round(smax_glogits, 1) if smax_glogits else None,
+        "smax_mfma_frac": round(smax_glogits / smax_peak_glogits(cfg.attn.d_q), 4) if smax_glogits else None,
         "elementwise_gbs": round(ew_gbs, 1) if ew_gbs else None,
         "kernels_ms_per_step": {k: round(v["ms"], 4) for k, v in per_step.items()},
         "roofline": {"bound": "mfma", "kernel": "ns_gemm", "achieved": round(gemm_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(cfg.name),
                      "launches_per_step": per_step.get("ns_gemm", {}).get("launches"),
+                     "ms_per_step": round(per_step.get("ns_gemm", {}).get("ms", float("nan")), 3),
+                     "flops_per_step": g["flops"] / prof_steps,
+                     "timing": "HIP events around each launch, one lane, %d steps" % prof_steps,
                      "avg_launch_us": round(g["ms"] / max(1, g["launches"]) * 1e3, 2)},
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),

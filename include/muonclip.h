@@ -293,8 +293,10 @@ const char *mc_version(void);
 
 /* ---- kernel timing (host). While enabled, every launch the library makes is
  * bracketed by a pair of hipEvents on the launch stream, and durations are
- * summed per kernel family. Enabling creates events (hipEventCreate) as
- * needed; it is meant for measurement runs, not for capture. */
+ * summed per kernel family; muonclip_step then runs all its chains on the
+ * caller's stream (no auxiliary lane), so no two timed launches overlap.
+ * Enabling creates events (hipEventCreate) as needed; it is meant for
+ * measurement runs, not for capture. */
 typedef struct {
   char name[32];
   int32_t launches;

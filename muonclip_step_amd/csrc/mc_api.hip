@@ -93,6 +93,11 @@ std::vector<ProfRec> g_recs;
 std::vector<hipEvent_t> g_pool;
 size_t g_pool_used = 0;
 
+bool profiling_on() {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  return g_prof;
+}
+
 hipEvent_t pool_event() {
   if (g_pool_used == g_pool.size()) {
     hipEvent_t e;
@@ -683,9 +688,11 @@ static mc_status step_impl(const mc_matrix* mats, int32_t n, const mc_hparams* h
   // waves of one group stay on one lane (on the 1155 MoE experts a second
   // lane measured no faster: the matrix cores are the bound); shape groups of
   // different sizes (the MLA layer's five matrices) gain 9 %.
+  // While kernel timing is on (mc_profile_enable), every chain runs on the
+  // caller's stream, so that no two timed launches overlap.
   const size_t half = (workspace_bytes / 2) & ~(kAlign - 1);
   std::vector<Chain> chains = plan_chains(groups, wave_cap, hp->ns_steps);
-  bool two = groups.size() >= 2 && chains.size() >= 2;
+  bool two = groups.size() >= 2 && chains.size() >= 2 && !profiling_on();
   std::vector<int> cap2(groups.size());
   for (size_t gi = 0; gi < groups.size() && two; ++gi) {
     cap2[gi] = largest_wave(groups[gi], std::min<int>((int)groups[gi].idx.size(), kWaveCap), half);

@@ -94,18 +94,63 @@ def ulp(x: np.ndarray, dtype: str) -> np.ndarray:
     return np.ldexp(1.0, np.maximum(e - bits, -126 - bits + 1))
 
 
-def check_matrix(state: State, hp, gamma_oracle=None, ns_tol=2e-2, gamma_gpu=None):
-    """Compare one matrix after the GPU step against the oracle. Returns the
-    NS relative Frobenius error.
+def clip_scales(spec, gamma_oracle=None, gamma_gpu=None):
+    """Per-row clip factor gamma_h^expo of the oracle (rows x 1) and the
+    relative difference of the GPU's factor from it."""
+    rows = spec.rows
+    sc = np.ones((rows, 1))
+    sc_rel = np.zeros((rows, 1))
+    if gamma_oracle is not None and spec.clip_slot >= 0:
+        for h, gh in enumerate(gamma_oracle):
+            for off, ln, ex in spec.segments:
+                r0 = h * spec.period + off
+                sc[r0:r0 + ln] = gh ** ex
+                if gamma_gpu is not None and gh > 0:
+                    sc_rel[r0:r0 + ln] = abs((gamma_gpu[h] / gh) ** ex - 1.0)
+    return sc, sc_rel
 
-    W bound: the oracle rounds once from fp64 (half an ulp of the param
-    dtype). The kernel computes t = w*decay, f = fma(-lr*rms, o, t), f*s in
-    fp32 with decay, lr*rms and s themselves rounded to fp32, which adds at
-    most s*(ulp(t) + ulp(lr*rms*o) + ulp(f)) + ulp(w') in fp32 ulps of those
+
+def w_bound(spec, hp, w_prev, w_o, w_g, o_g, o_o, gamma_oracle=None, gamma_gpu=None, carried=None):
+    """Elementwise bound on |W_gpu - W_oracle| after one step whose previous
+    weights differed by at most `carried` (None: identical inputs).
+
+    The oracle rounds once from fp64 (half an ulp of the param dtype). The
+    kernel computes t = w*decay, f = fma(-lr*rms, o, t), f*s in fp32 with
+    decay, lr*rms and s themselves rounded to fp32, which adds at most
+    s*(ulp(t) + ulp(lr*rms*o) + ulp(f)) + ulp(w') in fp32 ulps of those
     intermediates (they can be far larger than w' when the update cancels w).
-    On top come the NS difference (lr*rms*|dO|, times the clip factor) and,
-    for clipped rows, the relative difference of the GPU's
-    and the oracle's gamma^expo (observed from gamma_gpu)."""
+    On top come the NS difference (lr*rms*|dO|, times the clip factor), for
+    clipped rows the relative difference of the GPU's and the oracle's
+    gamma^expo, and the carried difference times decay and the clip factor."""
+    rows, cols = spec.rows, spec.cols
+    lr_rms = oracle.f32(hp.lr) * oracle.f32(hp.rms_scale) * math.sqrt(max(rows, cols))
+    lr_wd = oracle.f32(hp.lr) * oracle.f32(hp.weight_decay)
+    decay = 1.0 - lr_wd
+    sc, sc_rel = clip_scales(spec, gamma_oracle, gamma_gpu)
+    c = 0.0 if carried is None else carried
+    t = np.abs(w_prev * decay) + c
+    u = lr_rms * np.abs(o_o)
+    f = np.abs(w_prev * decay - lr_rms * o_o) + c
+    fp32_part = sc * (ulp(t, "f32") + ulp(u, "f32") + ulp(f, "f32")) + ulp(w_o, "f32")
+    # each side rounds its own value to the dtype: half an ulp at each
+    w_big = np.maximum(np.abs(w_o), np.abs(w_g))
+    return (1.001 * ulp(w_big, spec.w_dtype) + fp32_part + lr_rms * np.abs(o_g - o_o) * sc
+            + np.abs(w_o) * sc_rel * 1.01 + sc * decay * c + 1e-30)
+
+
+def assert_within(w_g, w_o, bound, what="W", extra=None):
+    excess = np.abs(w_g - w_o) - bound
+    if (excess > 0).any():
+        i = np.unravel_index(np.argmax(excess), excess.shape)
+        more = "" if extra is None else " " + " ".join(f"{k} {v[i]!r}" for k, v in extra.items())
+        raise AssertionError(f"{what}: {(excess > 0).sum()} elements beyond bound; worst at {i}: gpu {w_g[i]!r} "
+                             f"oracle {w_o[i]!r} bound {bound[i]!r}{more}")
+
+
+def check_matrix(state: State, hp, gamma_oracle=None, ns_tol=2e-2, gamma_gpu=None):
+    """Compare one matrix after the GPU step against the oracle (momentum
+    within 1 fp32 ulp, O within ns_tol relative Frobenius, W within
+    w_bound). Returns the NS relative Frobenius error."""
     w_o, m_o, o_o = oracle_step(state, hp, gamma_oracle)
     # momentum: one rounding of mu*M + G -> within 1 fp32 ulp
     m_g = host64(state.m)
@@ -114,37 +159,10 @@ def check_matrix(state: State, hp, gamma_oracle=None, ns_tol=2e-2, gamma_gpu=Non
     o_g = host64(state.o)
     err = rel_fro(o_g, o_o)
     assert err <= ns_tol, f"NS rel Frobenius {err:.3e} > {ns_tol}"
-    # parameter: one rounding of the update, within 1 ulp plus what the NS
-    # difference moves it (|lr * rms * dO| scaled by the clip factor)
-    s = state.spec
-    rows, cols = s.rows, s.cols
-    lr_rms = oracle.f32(hp.lr) * oracle.f32(hp.rms_scale) * math.sqrt(max(rows, cols))
-    sc = np.ones((rows, 1))
-    sc_rel = np.zeros((rows, 1))
-    if gamma_oracle is not None and s.clip_slot >= 0:
-        for h, gh in enumerate(gamma_oracle):
-            for off, ln, ex in s.segments:
-                r0 = h * s.period + off
-                sc[r0:r0 + ln] = gh ** ex
-                if gamma_gpu is not None and gh > 0:
-                    sc_rel[r0:r0 + ln] = abs((gamma_gpu[h] / gh) ** ex - 1.0)
     w_g = host64(state.w)
     w0 = state.w0.astype(np.float64)
-    lr_wd = oracle.f32(hp.lr) * oracle.f32(hp.weight_decay)
-    t = np.abs(w0 * (1.0 - lr_wd))
-    u = lr_rms * np.abs(o_o)
-    f = np.abs(w0 * (1.0 - lr_wd) - lr_rms * o_o)
-    fp32_part = sc * (ulp(t, "f32") + ulp(u, "f32") + ulp(f, "f32")) + ulp(w_o, "f32")
-    # each side rounds its own value to the dtype: half an ulp at each
-    w_big = np.maximum(np.abs(w_o), np.abs(w_g))
-    bound = (1.001 * ulp(w_big, s.w_dtype) + fp32_part + lr_rms * np.abs(o_g - o_o) * sc
-             + np.abs(w_o) * sc_rel * 1.01 + 1e-30)
-    excess = np.abs(w_g - w_o) - bound
-    if (excess > 0).any():
-        i = np.unravel_index(np.argmax(excess), excess.shape)
-        raise AssertionError(f"W: {(excess > 0).sum()} elements beyond bound; worst at {i}: gpu {w_g[i]!r} "
-                             f"oracle {w_o[i]!r} w0 {w0[i]!r} o_gpu {o_g[i]!r} o_orc {o_o[i]!r} "
-                             f"bound {bound[i]!r}")
+    bound = w_bound(state.spec, hp, w0, w_o, w_g, o_g, o_o, gamma_oracle, gamma_gpu)
+    assert_within(w_g, w_o, bound, "W", {"w0": w0, "o_gpu": o_g, "o_orc": o_o})
     return err
 
 

@@ -215,9 +215,17 @@ def draw_weight(cfg: Config, i: int) -> np.ndarray:
     return quantize_bf16(w) if s.w_dtype == "bf16" else quantize_f32(w)
 
 
-def draw_grad(cfg: Config, i: int) -> np.ndarray:
+KIND_G_LATER = 6                   # kinds 6..15: gradients of steps 2..11
+
+
+def draw_grad(cfg: Config, i: int, step: int = 1) -> np.ndarray:
+    """Gradient of matrix i at optimizer step `step` (1..11), each step its
+    own stream (step 1 is the gradient every configuration starts from)."""
     s = cfg.matrices[i]
-    return quantize_f32(normal(cfg.seed, tensor_id(i, KIND_G), (s.rows, s.cols), s.grad_std))
+    if not 1 <= step <= 11:
+        raise ValueError("step must be in 1..11")
+    kind = KIND_G if step == 1 else KIND_G_LATER + step - 2
+    return quantize_f32(normal(cfg.seed, tensor_id(i, kind), (s.rows, s.cols), s.grad_std))
 
 
 def draw_momentum(cfg: Config, i: int, cold: bool = False) -> np.ndarray:
