@@ -60,6 +60,9 @@ def parse():
                     help="time attention_forward (softmax attention with S_max taken from its own row "
                          "maxima) on the attention shape of --config (2: MHA layer, 3: MLA layer), against "
                          "the same forward without S_max and the separate max_logits_per_head pass")
+    ap.add_argument("--clip", action="store_true",
+                    help="time qk_clip_apply alone on the MLA layer's q_b (12288 x 1536) and kv_b (16384 x 512) "
+                         "with every head above tau (4 bytes per clipped bf16 element)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain streaming copy of MIB MiB (read + write) five times, "
                          "to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -336,6 +339,65 @@ def attention_bench(args):
     }), flush=True)
 
 
+def clip_bench(args):
+    """qk_clip_apply on the MLA projections that carry head rows (q_b: q^C
+    rows by sqrt(gamma), q^R rows by gamma; kv_b: k^C rows by sqrt(gamma))
+    with an S_max above tau on every head, so every head's segments are read
+    and written: 4 bytes per clipped bf16 element. Prints its own JSON line."""
+    import numpy as np
+    import torch
+
+    import muonclip_step_amd as mc
+    import workloads as wl
+    mc.load()
+    dev = torch.device("cuda:0")
+    cfg = wl.config(3)
+    names = [s.name for s in cfg.matrices]
+    mats, keep, clipped = [], [], 0
+    for nm in ("q_b", "kv_b"):
+        i = names.index(nm)
+        s = cfg.matrices[i]
+        w = torch.from_numpy(wl.draw_weight(cfg, i)).to(torch.bfloat16).to(dev)
+        d = torch.zeros(w.shape, dtype=torch.float32, device=dev)   # g, m: unused by the clip
+        keep += [w, d]
+        mats.append(mc.matrix(w, d, d, clip_slot=0, period=s.period, segments=s.segments))
+        clipped += (s.rows // s.period) * sum(seg[1] for seg in s.segments) * s.cols
+    H = cfg.attn.H
+    s_max = torch.from_numpy(np.full(H, 2.0 * cfg.tau, np.float32)).to(dev)   # gamma = 0.5 on every head
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        mc.qk_clip_apply(mats, s_max, 1, H, cfg.tau)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record(stream)
+    for i in range(args.steps):
+        mc.qk_clip_apply(mats, s_max, 1, H, cfg.tau)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    ms = per[len(per) // 2]
+    mc.profile_enable(True)
+    for _ in range(args.steps):
+        mc.qk_clip_apply(mats, s_max, 1, H, cfg.tau)
+    torch.cuda.synchronize()
+    prof = mc.profile_read()
+    mc.profile_enable(False)
+    k = prof["clip_apply"]
+    kern_gbs = clipped * 4.0 * args.steps / (k["ms"] * 1e-3) / 1e9
+    gbs = clipped * 4.0 / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "QK-Clip apply GB/s (standalone, every head clipped)", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "mla_clip", "matrices": "q_b 12288x1536, kv_b 16384x512", "clipped_elements": clipped,
+                   "bytes_per_element": 4},
+        "roofline": {"bound": "hbm", "kernel": "clip_apply", "achieved": round(kern_gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(kern_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(k["ms"] / max(1, k["launches"]) * 1e3, 2),
+                     "launches_per_call": k["launches"] // args.steps},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -352,6 +414,9 @@ def main():
         return
     if args.attention:
         attention_bench(args)
+        return
+    if args.clip:
+        clip_bench(args)
         return
 
     import muonclip_step_amd as mc

@@ -335,7 +335,8 @@ hipError_t launch_gamma(const float* s_max, float* gamma, int32_t slots, int32_t
   return hipGetLastError();
 }
 
-// grid.x: 1024-column chunks, grid.y strides over rows. Rows whose scale is
+// Rows padded, unaligned or with a ragged width: grid.x 1024-column chunks,
+// grid.y strides over rows, one element per access. Rows whose scale is
 // exactly 1 are skipped before touching memory, so gamma = 1 heads stay
 // bit-identical.
 __global__ void __launch_bounds__(256) clip_apply_kernel(const ClipApplyArgs a) {
@@ -358,8 +359,58 @@ __global__ void __launch_bounds__(256) clip_apply_kernel(const ClipApplyArgs a) 
   }
 }
 
+// Rows of whole 16-byte vectors (8 bf16 or 4 fp32; 16-byte aligned base and
+// row stride): the (row, vector) pairs are numbered row-major and each
+// thread takes kClipVPT of them, 256 apart, issuing every load before the
+// first store. A pair whose row scale is exactly 1 is neither read nor
+// written.
+constexpr int kClipVPT = 4;
+__global__ void __launch_bounds__(256) clip_apply_vec_kernel(const ClipApplyArgs a, int32_t vpr, int64_t total) {
+  const int64_t i0 = (int64_t)blockIdx.x * (256 * kClipVPT) + threadIdx.x;
+  const int64_t ld_bytes = a.ld * (a.w_bf16 ? 2 : 4);
+  u32x4_t v[kClipVPT];
+  char* p[kClipVPT];
+  float sc[kClipVPT];
+#pragma unroll
+  for (int k = 0; k < kClipVPT; ++k) {
+    const int64_t i = i0 + (int64_t)k * 256;
+    sc[k] = 1.0f;
+    p[k] = nullptr;
+    if (i < total) {
+      const int row = (int)(i / vpr), c = (int)(i - (int64_t)row * vpr);
+      sc[k] = row_clip_scale(a.clip, row, a.s_max, a.heads, a.tau, 0);
+      p[k] = (char*)a.w + row * ld_bytes + (int64_t)c * 16;
+      if (sc[k] != 1.0f) v[k] = *(const u32x4_t*)p[k];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kClipVPT; ++k) {
+    if (sc[k] == 1.0f) continue;
+    u32x4_t r;
+    if (a.w_bf16) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        r[e] = f32x2_to_bf16x2(bf16_to_f32((uint16_t)v[k][e]) * sc[k], bf16_to_f32((uint16_t)(v[k][e] >> 16)) * sc[k]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = __float_as_uint(__uint_as_float(v[k][e]) * sc[k]);
+    }
+    *(u32x4_t*)p[k] = r;
+  }
+}
+
 hipError_t launch_clip_apply(const ClipApplyArgs& a, hipStream_t s) {
   if (a.rows <= 0 || a.cols <= 0) return hipSuccess;
+  const int es = a.w_bf16 ? 2 : 4, epv = 16 / es;
+  if (a.cols % epv == 0 && (a.ld * es) % 16 == 0 && ((uintptr_t)a.w & 15) == 0) {
+    const int32_t vpr = a.cols / epv;
+    const int64_t total = (int64_t)a.rows * vpr;
+    const int64_t blocks = (total + 256 * kClipVPT - 1) / (256 * kClipVPT);
+    if (blocks < ((int64_t)1 << 31)) {
+      clip_apply_vec_kernel<<<(unsigned)blocks, 256, 0, s>>>(a, vpr, total);
+      return hipGetLastError();
+    }
+  }
   dim3 grid((a.cols + 1023) / 1024, a.rows < 32768 ? a.rows : 32768);
   clip_apply_kernel<<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
