@@ -150,9 +150,9 @@ def build_workload(cfg, dev):
 def cpu_baseline(cfg, budget_s, dev=None):
     """The fp64 oracle on a bounded sample of the same workload, scaled to a
     full step: whole matrices (momentum -> NS -> update -> clip) until the
-    budget is spent (the first device-drawn matrix first, copied to the host,
-    then the host-drawn ones, smallest first), and S_max of a few (sample,
-    head) slices."""
+    budget is spent (the smallest device-drawn matrix first, copied to the
+    host, then the host-drawn ones, smallest first), and S_max of a few
+    (sample, head) slices."""
     import numpy as np
 
     import oracle
@@ -167,7 +167,9 @@ def cpu_baseline(cfg, budget_s, dev=None):
     total_flops = sum(ns_flops(s.rows, s.cols, hp["ns_steps"]) for s in cfg.matrices)
     order = sorted((i for i, s in enumerate(cfg.matrices) if not s.device_drawn),
                    key=lambda i: ns_flops(cfg.matrices[i].rows, cfg.matrices[i].cols, hp["ns_steps"]))
-    first_dev = next((i for i, s in enumerate(cfg.matrices) if s.device_drawn), None)
+    dev_ids = [i for i, s in enumerate(cfg.matrices) if s.device_drawn]
+    first_dev = min(dev_ids, key=lambda i: ns_flops(cfg.matrices[i].rows, cfg.matrices[i].cols, hp["ns_steps"]),
+                    default=None)
     if first_dev is not None and dev is not None:
         order = [first_dev] + order
     for i in order:
