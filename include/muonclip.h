@@ -179,6 +179,22 @@ mc_status muonclip_step_overlapped(const mc_matrix *mats /* host, n */, int32_t 
                                    const float *s_max, int32_t slots, int32_t heads, float *gamma_out,
                                    void *workspace, size_t workspace_bytes, void *stream, void *s_max_ready);
 
+/* muonclip_step for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without the workspace, which is a static device array of
+ * MC_NOALLOC_SCRATCH_BYTES inside the library instead (one per device, held
+ * until the process ends). The call allocates nothing and creates nothing:
+ * all work runs on `stream` (no auxiliary lane). Matrices whose smallest
+ * workspace (mc_workspace_min_size) exceeds the scratch are rejected with
+ * MC_ERR_WORKSPACE before anything is enqueued; within it, waves are as
+ * large as the scratch allows. Results equal muonclip_step's with a
+ * workspace of MC_NOALLOC_SCRATCH_BYTES on one stream. Every call on a
+ * device shares that device's scratch: two calls that overlap on one device
+ * (different streams, no ordering) race and give undefined results. */
+#define MC_NOALLOC_SCRATCH_BYTES (256u << 20)
+mc_status muonclip_step_noalloc(const mc_matrix *mats /* host, n */, int32_t n, const mc_hparams *hp /* host */,
+                                const float *s_max, int32_t slots, int32_t heads, float *gamma_out, void *stream);
+
 /* Per-head max attention logit of one attention layer's forward (the essay's
  * S_max^h equation, section on Muon and attention logits: the largest
  * Q_i^h . K_j^h / sqrt(d) over the batch and over token pairs; the report

@@ -21,7 +21,7 @@ MC_OK, MC_ERR_NULL, MC_ERR_SHAPE, MC_ERR_DTYPE, MC_ERR_WORKSPACE, MC_ERR_HPARAM,
 MC_F32, MC_BF16 = 0, 1
 
 EXPORTS = ("mc_default_hparams", "mc_workspace_size", "mc_workspace_min_size", "muonclip_step",
-           "muonclip_step_overlapped",
+           "muonclip_step_overlapped", "muonclip_step_noalloc",
            "max_logits_per_head", "qk_clip_apply", "mc_last_error", "mc_version",
            "mc_profile_enable", "mc_profile_read", "mc_default_adamw_hparams", "adamw_step",
            "attention_forward")
@@ -89,6 +89,8 @@ def load():
     lib.muonclip_step.restype = c_int32
     lib.muonclip_step_overlapped.argtypes = lib.muonclip_step.argtypes + [c_void_p]
     lib.muonclip_step_overlapped.restype = c_int32
+    lib.muonclip_step_noalloc.argtypes = [MP, c_int32, HP, c_void_p, c_int32, c_int32, c_void_p, c_void_p]
+    lib.muonclip_step_noalloc.restype = c_int32
     lib.max_logits_per_head.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                         c_int32, c_int32, c_int32, POINTER(c_int64), POINTER(c_int64),
                                         POINTER(c_int64), c_int32, c_float, c_void_p, c_void_p]
@@ -207,6 +209,20 @@ def muonclip_step(mats, hp: HParams | None = None, s_max=None, slots: int = 0, h
             raise ValueError("s_max_ready has not been recorded")
         _check(lib.muonclip_step_overlapped(*args, ctypes.c_void_p(ev)))
     return workspace
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20   # MC_NOALLOC_SCRATCH_BYTES of include/muonclip.h
+
+
+def muonclip_step_noalloc(mats, hp: HParams | None = None, s_max=None, slots: int = 0, heads: int = 0,
+                          gamma_out=None, stream=None):
+    """muonclip_step with the library's static per-device scratch as the
+    workspace: allocates nothing (calls on one device must not overlap)."""
+    lib = load()
+    hp = hp or hparams()
+    arr, n = _array(mats)
+    _check(lib.muonclip_step_noalloc(arr, n, ctypes.byref(hp), _ptr(s_max), slots, heads, _ptr(gamma_out),
+                                     _stream(stream)))
 
 
 def max_logits_per_head(q, k, k_shared=None, causal: bool = True, scale: float | None = None, out=None,

@@ -651,7 +651,7 @@ size_t mc_workspace_min_size(const mc_matrix* mats, int32_t n, const mc_hparams*
 // muonclip_step with an optional event that the launches reading s_max wait on.
 static mc_status step_impl(const mc_matrix* mats, int32_t n, const mc_hparams* hp, const float* s_max,
                            int32_t slots, int32_t heads, float* gamma_out, void* workspace, size_t workspace_bytes,
-                           void* stream, hipEvent_t smax_ready) {
+                           void* stream, hipEvent_t smax_ready, bool one_lane = false) {
   mc_status st = check_hparams(hp);
   if (st) return st;
   const bool have_smax = s_max != nullptr;
@@ -692,7 +692,7 @@ static mc_status step_impl(const mc_matrix* mats, int32_t n, const mc_hparams* h
   // caller's stream, so that no two timed launches overlap.
   const size_t half = (workspace_bytes / 2) & ~(kAlign - 1);
   std::vector<Chain> chains = plan_chains(groups, wave_cap, hp->ns_steps);
-  bool two = groups.size() >= 2 && chains.size() >= 2 && !profiling_on();
+  bool two = groups.size() >= 2 && chains.size() >= 2 && !one_lane && !profiling_on();
   std::vector<int> cap2(groups.size());
   for (size_t gi = 0; gi < groups.size() && two; ++gi) {
     cap2[gi] = largest_wave(groups[gi], std::min<int>((int)groups[gi].idx.size(), kWaveCap), half);
@@ -755,6 +755,57 @@ mc_status muonclip_step_overlapped(const mc_matrix* mats, int32_t n, const mc_hp
                                    size_t workspace_bytes, void* stream, void* s_max_ready) {
   return step_impl(mats, n, hp, s_max, slots, heads, gamma_out, workspace, workspace_bytes, stream,
                    (hipEvent_t)s_max_ready);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free step
+
+// The workspace of muonclip_step_noalloc: one copy per device, held from the
+// library's load until the process ends. In host code `scratch` names a host
+// stand-in; kernels get the device address that hipGetSymbolAddress returns
+// for the current device, looked up once per device.
+static __device__ __align__(256) char scratch[MC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scr_mu;
+std::map<int, void*> g_scr;
+
+mc_status scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MC_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_scr_mu);
+  auto it = g_scr.find(dev);
+  if (it != g_scr.end()) { *out = it->second; return MC_OK; }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) return fail(MC_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+  g_scr[dev] = p;
+  *out = p;
+  return MC_OK;
+}
+}  // namespace
+
+extern "C" {
+
+mc_status muonclip_step_noalloc(const mc_matrix* mats, int32_t n, const mc_hparams* hp, const float* s_max,
+                                int32_t slots, int32_t heads, float* gamma_out, void* stream) {
+  mc_status st = check_hparams(hp);
+  if (st) return st;
+  st = check_matrices_step(mats, n, 0, 0, false);
+  if (st) return st;
+  if (n > 0) {
+    const size_t need = workspace_for(mats, n, hp, true);
+    if (need > (size_t)MC_NOALLOC_SCRATCH_BYTES)
+      return fail(MC_ERR_WORKSPACE, "muonclip_step_noalloc: these matrices need %zu bytes of workspace; the "
+                  "static scratch holds %zu (use muonclip_step with a caller workspace)", need,
+                  (size_t)MC_NOALLOC_SCRATCH_BYTES);
+  }
+  void* ws = nullptr;
+  if ((st = scratch_ptr(&ws))) return st;
+  return step_impl(mats, n, hp, s_max, slots, heads, gamma_out, ws, (size_t)MC_NOALLOC_SCRATCH_BYTES, stream,
+                   nullptr, true);
 }
 
 mc_status max_logits_per_head(const void* q, const void* k, const void* k_shared, int32_t dtype, int32_t B, int32_t T,

@@ -246,3 +246,21 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_noalloc_step_rejects_matrices_beyond_its_scratch():
+    # the dense 7168 x 18432 FFN matrix needs about 1.3 GB of workspace, more
+    # than the static scratch: rejected before anything touches a device
+    lib = mc.load()
+    hp = mc.hparams()
+    arr = (mc.Matrix * 1)(fake_matrix(7168, 18432))
+    st = lib.muonclip_step_noalloc(arr, 1, ctypes.byref(hp), None, 0, 0, None, None)
+    assert st == mc.MC_ERR_WORKSPACE
+    assert b"static scratch" in lib.mc_last_error()
+    assert lib.mc_workspace_min_size(arr, 1, ctypes.byref(hp)) > mc.NOALLOC_SCRATCH_BYTES
+    # bad arguments are reported as by muonclip_step
+    bad = (mc.Matrix * 1)(fake_matrix(64, 64, ld=32))
+    assert lib.muonclip_step_noalloc(bad, 1, ctypes.byref(hp), None, 0, 0, None, None) == mc.MC_ERR_SHAPE
+    hp.ns_steps = 0
+    assert lib.muonclip_step_noalloc(arr, 1, ctypes.byref(hp), None, 0, 0, None, None) == mc.MC_ERR_HPARAM
+
