@@ -264,3 +264,39 @@ def test_noalloc_step_rejects_matrices_beyond_its_scratch():
     hp.ns_steps = 0
     assert lib.muonclip_step_noalloc(arr, 1, ctypes.byref(hp), None, 0, 0, None, None) == mc.MC_ERR_HPARAM
 
+
+def test_dispatcher_under_address_and_undefined_behaviour_sanitizers(tmp_path):
+    """The dispatcher (argument validation and workspace planning, host code
+    of mc_api.hip) built with AddressSanitizer and UndefinedBehaviorSanitizer
+    on its host side, linked with the regular kernel objects and driven by
+    tests/sanitize/dispatch_checks.cpp: every documented rejection returns its
+    status and the planning of every configuration's shape set runs clean."""
+    import subprocess
+
+    from muonclip_step_amd import build as b
+    root = os.path.dirname(os.path.dirname(__file__))
+    objs = [os.path.join(b.BUILD, f + ".hip.o") for f in ("ns_gemm", "elementwise", "max_logits", "attn_fwd", "adamw")]
+    if not all(os.path.exists(o) for o in objs):
+        b.build()
+    hipcc = b._hipcc()
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc)), "..", "llvm", "bin", "clang++")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+    api = str(tmp_path / "mc_api_san.o")
+    drv = str(tmp_path / "dispatch_checks.o")
+    exe = str(tmp_path / "dispatch_checks")
+    inc = ["-I", os.path.join(root, "include"), "-I", b.CSRC]
+    steps = [
+        [hipcc, f"--offload-arch={b.ARCH}", "-O1", "-g", "-std=c++17", "-fPIC", *inc, *san,
+         "-c", os.path.join(b.CSRC, "mc_api.hip"), "-o", api],
+        [clang, "-std=c++17", "-O1", "-g", "-I", os.path.join(root, "include"), "-fsanitize=address,undefined",
+         "-fno-omit-frame-pointer", "-c", os.path.join(root, "tests", "sanitize", "dispatch_checks.cpp"), "-o", drv],
+        [hipcc, f"--offload-arch={b.ARCH}", *san, drv, api, *objs, "-o", exe],
+    ]
+    for cmd in steps:
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+        assert r.returncode == 0, r.stderr[-3000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0:exitcode=23",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120, env=env)
+    assert r.returncode == 0 and "dispatch checks ok" in r.stdout, (r.returncode, r.stdout[-2000:], r.stderr[-4000:])
