@@ -567,15 +567,64 @@ int largest_wave(const Group& g, int limit, size_t ws_bytes) {
 // of nb matrices, independent of every other chain.
 struct Chain { int gi, b0, nb; double flops; };
 
-// Waves of at most cap[gi] matrices per group, sized evenly.
+// Relative time of one wave's three Newton-Schulz products: every launch
+// runs in rounds of one tile per CU, so a round that only part of the chip
+// has tiles for costs as much as a full one. A round costs its k-stages
+// times the tile's share of a 256x256 tile's work (128 and 64 tiles run at
+// about 0.8 of that rate per flop), split-K launches their partial k range.
+double wave_cost(const Group& g, int nb, int cus) {
+  const WavePlan w = plan_wave(g, nb, cus);
+  double cost = 0.0;
+  const GemmPlan* ps[3] = {&w.gram, &w.poly, &w.apply};
+  const bool sym[3] = {true, true, false};
+  for (int k = 0; k < 3; ++k) {
+    const GemmPlan& gp = *ps[k];
+    const int d = gemm_tile_dim(gp.tile);
+    const int64_t per = (sym[k] && gp.splits == 1) ? (int64_t)gp.tiles_m * (gp.tiles_m + 1) / 2
+                                                   : (int64_t)gp.tiles_m * gp.tiles_n;
+    const int64_t items = per * gp.splits * nb;
+    const double rounds = (double)((items + cus - 1) / cus);
+    const double share = (double)d * d / (256.0 * 256.0) / (d == 256 ? 1.0 : 0.8);
+    cost += rounds * gp.kt_per_split * share + 2.0;   // + launch and drain, about two k-stages
+  }
+  return cost;
+}
+
+// Waves of at most cap[gi] matrices per group. A group larger than one wave
+// is cut into waves of one size s plus a remainder, s chosen between the
+// even split and the cap to minimise the summed wave_cost (1155 expert
+// matrices: 18 waves of 64 and one of 3, whose launches fill every round,
+// instead of 19 waves of about 61 that leave most launches a partial round).
 std::vector<Chain> plan_chains(const std::vector<Group>& groups, const std::vector<int>& cap, int ns_steps) {
   std::vector<Chain> out;
+  const int cus = device_cus();
   for (size_t gi = 0; gi < groups.size(); ++gi) {
     const Group& g = groups[gi];
     const int count = (int)g.idx.size();
     const int waves = (count + cap[gi] - 1) / cap[gi];
-    for (int w = 0, b0 = 0; w < waves; ++w) {
-      const int nb = count / waves + (w < count % waves ? 1 : 0);
+    std::vector<int> sizes;
+    for (int w = 0; w < waves; ++w) sizes.push_back(count / waves + (w < count % waves ? 1 : 0));
+    if (waves > 1) {
+      std::map<int, double> memo;
+      auto cost_of = [&](int nb) {
+        auto it = memo.find(nb);
+        if (it != memo.end()) return it->second;
+        return memo[nb] = wave_cost(g, nb, cus);
+      };
+      double best = 0.0;
+      for (int nb : sizes) best += cost_of(nb);
+      for (int sz = (count + waves - 1) / waves + 1; sz <= cap[gi]; ++sz) {
+        const int full = count / sz, rest = count - full * sz;
+        const double c = full * cost_of(sz) + (rest ? cost_of(rest) : 0.0);
+        if (c < best * 0.999) {
+          best = c;
+          sizes.assign(full, sz);
+          if (rest) sizes.push_back(rest);
+        }
+      }
+    }
+    for (int b0 = 0, w = 0; w < (int)sizes.size(); ++w) {
+      const int nb = sizes[w];
       const double f = (double)ns_steps * 2.0 * (2.0 * g.n * g.m * g.m + (double)g.m * g.m * g.m) * nb;
       out.push_back({(int)gi, b0, nb, f});
       b0 += nb;
