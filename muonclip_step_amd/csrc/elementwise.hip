@@ -25,6 +25,8 @@
 // Tiles are 64x64 elements per 256-thread block; each thread moves 4
 // consecutive elements per row (128-bit fp32 / 64-bit bf16 accesses) when the
 // row stride and base allow, scalar accesses otherwise.
+#include <algorithm>
+
 #include "mc_internal.h"
 
 namespace mc {
@@ -64,12 +66,13 @@ __global__ void __launch_bounds__(256) momentum_kernel(const MomArgs a) {
       const int row = tr * 64 + ry + 16 * k;
       if (row < mm.rows) {
         const int64_t base = (int64_t)row * mm.ld + col;
-        mvs[k] = *(const f32x4_t*)(mm.m + base);
+        // G and M are streamed once per step: non-temporal accesses
+        mvs[k] = __builtin_nontemporal_load((const f32x4_t*)(mm.m + base));
         if (mm.g_bf16) {
-          const u16x4_t gb = *(const u16x4_t*)((const uint16_t*)mm.g + base);
+          const u16x4_t gb = __builtin_nontemporal_load((const u16x4_t*)((const uint16_t*)mm.g + base));
           gvs[k] = f32x4_t{bf16_to_f32(gb[0]), bf16_to_f32(gb[1]), bf16_to_f32(gb[2]), bf16_to_f32(gb[3])};
         } else {
-          gvs[k] = *(const f32x4_t*)((const float*)mm.g + base);
+          gvs[k] = __builtin_nontemporal_load((const f32x4_t*)((const float*)mm.g + base));
         }
       }
     }
@@ -85,7 +88,7 @@ __global__ void __launch_bounds__(256) momentum_kernel(const MomArgs a) {
         f32x4_t nv;
         nv[0] = fmaf(a.mu, mv[0], gv[0]); nv[1] = fmaf(a.mu, mv[1], gv[1]);
         nv[2] = fmaf(a.mu, mv[2], gv[2]); nv[3] = fmaf(a.mu, mv[3], gv[3]);
-        *(f32x4_t*)(mm.m + base) = nv;
+        __builtin_nontemporal_store(nv, (f32x4_t*)(mm.m + base));
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = a.nesterov ? fmaf(a.mu, nv[e], gv[e]) : nv[e];
       } else if (!mm.vec) {
@@ -360,57 +363,67 @@ __global__ void __launch_bounds__(256) clip_apply_kernel(const ClipApplyArgs a) 
 }
 
 // Rows of whole 16-byte vectors (8 bf16 or 4 fp32; 16-byte aligned base and
-// row stride): the (row, vector) pairs are numbered row-major and each
-// thread takes kClipVPT of them, 256 apart, issuing every load before the
-// first store. A pair whose row scale is exactly 1 is neither read nor
-// written.
-constexpr int kClipVPT = 4;
-__global__ void __launch_bounds__(256) clip_apply_vec_kernel(const ClipApplyArgs a, int32_t vpr, int64_t total) {
-  const int64_t i0 = (int64_t)blockIdx.x * (256 * kClipVPT) + threadIdx.x;
-  const int64_t ld_bytes = a.ld * (a.w_bf16 ? 2 : 4);
-  u32x4_t v[kClipVPT];
-  char* p[kClipVPT];
-  float sc[kClipVPT];
+// row stride) of up to kMaxClipBatch matrices, numbered one matrix after the
+// other. Each wave owns one row at a time (a grid-stride loop over rows), so
+// the row's head, segment and factor are computed once, in scalar registers;
+// a row whose factor is exactly 1 is neither read nor written. The row's
+// vectors go 64 lanes wide, four per lane, every load before the first store.
+constexpr int kClipVPL = 4;
+__global__ void __launch_bounds__(256) clip_apply_vec_kernel(const ClipVecArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  for (int64_t r = wave; r < a.total_rows; r += nwaves) {
+    int j = 0;
+    for (int t = 1; t < a.nmat; ++t)
+      if (r >= a.mat[t].row_start) j = t;
+    const ClipVecMat& m = a.mat[j];
+    const int row = (int)(r - m.row_start);
+    const float sc = row_clip_scale(m.clip, row, a.s_max, a.heads, a.tau, 0);
+    if (sc == 1.0f) continue;
+    char* base = m.w + row * m.ld_bytes;
+    for (int c0 = 0; c0 < m.vpr; c0 += 64 * kClipVPL) {
+      u32x4_t v[kClipVPL];
 #pragma unroll
-  for (int k = 0; k < kClipVPT; ++k) {
-    const int64_t i = i0 + (int64_t)k * 256;
-    sc[k] = 1.0f;
-    p[k] = nullptr;
-    if (i < total) {
-      const int row = (int)(i / vpr), c = (int)(i - (int64_t)row * vpr);
-      sc[k] = row_clip_scale(a.clip, row, a.s_max, a.heads, a.tau, 0);
-      p[k] = (char*)a.w + row * ld_bytes + (int64_t)c * 16;
-      if (sc[k] != 1.0f) v[k] = *(const u32x4_t*)p[k];
+      for (int k = 0; k < kClipVPL; ++k) {
+        const int c = c0 + k * 64 + lane;
+        if (c < m.vpr) v[k] = *(const u32x4_t*)(base + (int64_t)c * 16);
+      }
+#pragma unroll
+      for (int k = 0; k < kClipVPL; ++k) {
+        const int c = c0 + k * 64 + lane;
+        if (c >= m.vpr) break;
+        u32x4_t out;
+        if (m.w_bf16) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            out[e] = f32x2_to_bf16x2(bf16_to_f32((uint16_t)v[k][e]) * sc, bf16_to_f32((uint16_t)(v[k][e] >> 16)) * sc);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[e] = __float_as_uint(__uint_as_float(v[k][e]) * sc);
+        }
+        *(u32x4_t*)(base + (int64_t)c * 16) = out;
+      }
     }
   }
-#pragma unroll
-  for (int k = 0; k < kClipVPT; ++k) {
-    if (sc[k] == 1.0f) continue;
-    u32x4_t r;
-    if (a.w_bf16) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        r[e] = f32x2_to_bf16x2(bf16_to_f32((uint16_t)v[k][e]) * sc[k], bf16_to_f32((uint16_t)(v[k][e] >> 16)) * sc[k]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) r[e] = __float_as_uint(__uint_as_float(v[k][e]) * sc[k]);
-    }
-    *(u32x4_t*)p[k] = r;
-  }
+}
+
+bool clip_apply_vectorizable(const ClipApplyArgs& a) {
+  const int es = a.w_bf16 ? 2 : 4, epv = 16 / es;
+  return a.rows > 0 && a.cols > 0 && a.cols % epv == 0 && (a.ld * es) % 16 == 0 && ((uintptr_t)a.w & 15) == 0;
+}
+
+hipError_t launch_clip_apply_vec(const ClipVecArgs& a, hipStream_t s) {
+  if (a.nmat <= 0 || a.total_rows <= 0) return hipSuccess;
+  // one row per wave up to 32 waves per CU of the device; more rows loop
+  const int64_t cap = (int64_t)device_cus() * 8;
+  const int64_t blocks = std::min<int64_t>((a.total_rows + 3) / 4, cap);
+  clip_apply_vec_kernel<<<(unsigned)blocks, 256, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_clip_apply(const ClipApplyArgs& a, hipStream_t s) {
   if (a.rows <= 0 || a.cols <= 0) return hipSuccess;
-  const int es = a.w_bf16 ? 2 : 4, epv = 16 / es;
-  if (a.cols % epv == 0 && (a.ld * es) % 16 == 0 && ((uintptr_t)a.w & 15) == 0) {
-    const int32_t vpr = a.cols / epv;
-    const int64_t total = (int64_t)a.rows * vpr;
-    const int64_t blocks = (total + 256 * kClipVPT - 1) / (256 * kClipVPT);
-    if (blocks < ((int64_t)1 << 31)) {
-      clip_apply_vec_kernel<<<(unsigned)blocks, 256, 0, s>>>(a, vpr, total);
-      return hipGetLastError();
-    }
-  }
   dim3 grid((a.cols + 1023) / 1024, a.rows < 32768 ? a.rows : 32768);
   clip_apply_kernel<<<grid, 256, 0, s>>>(a);
   return hipGetLastError();

@@ -979,6 +979,17 @@ mc_status qk_clip_apply(const mc_matrix* mats, int32_t n, const float* s_max, in
     hipError_t e = launch_gamma(s_max, gamma_out, slots, heads, tau, 0, s);
     if (e != hipSuccess) return fail(MC_ERR_HIP, "gamma launch: %s", hipGetErrorString(e));
   }
+  // matrices of whole 16-byte row vectors go kMaxClipBatch to a launch; the
+  // rest one launch each with element accesses
+  ClipVecArgs va{};
+  va.s_max = s_max; va.heads = heads; va.tau = tau;
+  auto flush = [&]() -> mc_status {
+    if (va.nmat == 0) return MC_OK;
+    Prof pr(F_CLIP, s, 0.0, 0.0);
+    hipError_t e = launch_clip_apply_vec(va, s);
+    va.nmat = 0; va.total_rows = 0;
+    return e == hipSuccess ? MC_OK : fail(MC_ERR_HIP, "clip_apply launch: %s", hipGetErrorString(e));
+  };
   for (int i = 0; i < n; ++i) {
     const mc_matrix& m = mats[i];
     if (m.clip_slot < 0 || m.nseg == 0) continue;
@@ -987,11 +998,22 @@ mc_status qk_clip_apply(const mc_matrix* mats, int32_t n, const float* s_max, in
     a.rows = (int32_t)m.rows; a.cols = (int32_t)m.cols;
     a.clip = clip_rule(m, true);
     a.s_max = s_max; a.heads = heads; a.tau = tau;
+    if (clip_apply_vectorizable(a)) {
+      ClipVecMat& v = va.mat[va.nmat++];
+      const int es = a.w_bf16 ? 2 : 4;
+      v.w = (char*)m.w; v.ld_bytes = m.ld * es; v.w_bf16 = a.w_bf16; v.vpr = a.cols * es / 16;
+      v.rows = a.rows; v.row_start = va.total_rows; v.clip = a.clip;
+      va.total_rows += a.rows;
+      if (va.nmat == kMaxClipBatch) {
+        if (mc_status st = flush()) return st;
+      }
+      continue;
+    }
     Prof pr(F_CLIP, s, 0.0, 0.0);
     hipError_t e = launch_clip_apply(a, s);
     if (e != hipSuccess) return fail(MC_ERR_HIP, "clip_apply launch: %s", hipGetErrorString(e));
   }
-  return MC_OK;
+  return flush();
 }
 
 void mc_default_adamw_hparams(mc_adamw_hparams* hp) {

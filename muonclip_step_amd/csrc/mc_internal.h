@@ -210,7 +210,26 @@ struct ClipApplyArgs {
   ClipRule clip;
   const float* s_max; int32_t heads; float tau;
 };
+// one matrix, whatever its alignment (element accesses when it has to)
 hipError_t launch_clip_apply(const ClipApplyArgs& a, hipStream_t s);
+// Up to kMaxClipBatch matrices whose rows are whole 16-byte vectors (cols a
+// multiple of 8 bf16 / 4 fp32, 16-byte aligned base and row stride) in one
+// launch: their rows are numbered one matrix after another.
+constexpr int kMaxClipBatch = 8;
+struct ClipVecMat {
+  char* w; int64_t ld_bytes;
+  int32_t w_bf16, vpr;                 // 16-byte vectors per row
+  int32_t rows;
+  int64_t row_start;                   // first row of this matrix in the joint numbering
+  ClipRule clip;
+};
+struct ClipVecArgs {
+  int32_t nmat; int64_t total_rows;
+  const float* s_max; int32_t heads; float tau;
+  ClipVecMat mat[kMaxClipBatch];
+};
+bool clip_apply_vectorizable(const ClipApplyArgs& a);
+hipError_t launch_clip_apply_vec(const ClipVecArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- AdamW
 

@@ -593,3 +593,54 @@ def test_step_overlapped_without_matrices_writes_gamma():
     mc.muonclip_step([], mc.hparams(tau=100.0), s_max=s2, slots=1, heads=4, gamma_out=g, s_max_ready=ready)
     torch.cuda.synchronize()
     assert np.allclose(host64(g), want, rtol=1e-6, atol=0)
+
+
+def test_qk_clip_apply_batches_mixed_layouts():
+    """One qk_clip_apply call over eleven matrices: bf16 and fp32, row widths
+    that are and are not whole 16-byte vectors, padded row strides, MHA and
+    MLA segment layouts (more than one batched launch). Every clipped row is
+    the drawn row times gamma_h^expo rounded once (fp32 factor), every other
+    row is bit-identical (essay, gamma equation and MHA / MLA rules)."""
+    heads, tau = 6, 10.0
+    s_in = np.array([40.0, 5.0, 12.5, np.inf, 10.0, 80.0], np.float32)
+    g_orc = oracle.clip_factor(s_in.astype(np.float64), tau)
+    s_max = torch.from_numpy(s_in).cuda()
+    cases = []   # (rows, cols, ld_pad, dtype, period, segments)
+    for k in range(11):
+        dt = "bf16" if k % 2 == 0 else "f32"
+        cols = [64, 37, 96, 130, 8, 512][k % 6]
+        ld_pad = [0, 3, 8, 0, 1, 4][k % 6]
+        if k % 3 == 0:
+            period, segs = 16, ((0, 16, 0.5),)
+        elif k % 3 == 1:
+            period, segs = 12, ((0, 8, 0.5), (8, 4, 1.0))
+        else:
+            period, segs = 10, ((2, 5, 0.5),)
+        cases.append((heads * period, cols, ld_pad, dt, period, segs))
+    mats, keep = [], []
+    for k, (rows, cols, ld_pad, dt, period, segs) in enumerate(cases):
+        w = wl.normal(60 + k, 0, (rows, cols), 1.0)
+        w = wl.quantize_bf16(w) if dt == "bf16" else wl.quantize_f32(w)
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        full = torch.zeros(rows, cols + ld_pad, dtype=tdt, device="cuda")
+        full[:, :cols] = torch.from_numpy(w).to(tdt).cuda()
+        z = torch.zeros(rows, cols + ld_pad, dtype=torch.float32, device="cuda")[:, :cols]
+        view = full[:, :cols]
+        mats.append(mc.matrix(view, z, z, clip_slot=0, period=period, segments=segs))
+        keep.append((w, full, view, dt, period, segs))
+    gamma = torch.empty(heads, dtype=torch.float32, device="cuda")
+    mc.qk_clip_apply(mats, s_max, 1, heads, tau, gamma_out=gamma)
+    torch.cuda.synchronize()
+    assert np.allclose(host64(gamma), g_orc, rtol=1e-6, atol=0)
+    for w, full, view, dt, period, segs in keep:
+        got = host64(view)
+        want = oracle.qk_clip_rows(w.astype(np.float64), g_orc, period, segs)
+        # fp32 factor and product, then one rounding to the dtype (fp32: the
+        # factor's and the product's roundings, up to two ulps of the result)
+        ulps = 1.001 if dt == "bf16" else 2.001
+        tol = ulps * (2.0 ** (np.frexp(np.abs(want))[1] - (8 if dt == "bf16" else 24))) + 1e-30
+        assert np.all(np.abs(got - want) <= tol), (dt, view.shape, period)
+        untouched = np.isclose(want, w, rtol=0, atol=0)
+        assert np.array_equal(got[untouched], w.astype(np.float64)[untouched])
+        if full.shape[1] > view.shape[1]:   # the padding is never written
+            assert not bool(full[:, view.shape[1]:].any())
