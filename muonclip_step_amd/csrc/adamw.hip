@@ -11,7 +11,9 @@
 // element for a bf16 parameter with fp32 gradient). A block covers 4096
 // consecutive elements of one vector; each thread moves four consecutive
 // elements per access (16-byte fp32, 8-byte bf16) when the vector's pointers
-// allow, element by element otherwise and at a vector's ragged end.
+// allow, element by element otherwise and at a vector's ragged end. Whole
+// blocks of vector accesses issue all their loads before the first store and
+// stream non-temporally (each element is touched once per step).
 #include <math.h>
 
 #include "mc_internal.h"
@@ -20,6 +22,7 @@ namespace mc {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kAdamBlockElems = 4096;
 
@@ -36,8 +39,50 @@ __global__ void __launch_bounds__(256) adamw_kernel(const AdamArgs a) {
     if ((int)blockIdx.x >= a.vec[t].block_start) j = t;
   const AdamVec& d = a.vec[j];
   const int64_t e0 = (int64_t)(blockIdx.x - d.block_start) * kAdamBlockElems;
+  constexpr int KC = kAdamBlockElems / 1024;   // 1024-element chunks per block
+  if (d.vec && e0 + kAdamBlockElems <= d.n) {
+    // a whole block of vector accesses: every load of the four chunks goes
+    // out before the first store (the buffers never alias, but the compiler
+    // cannot know that), and each element is streamed once, non-temporally
+    f32x4_t g4[KC], m4[KC], v4[KC], p4[KC];
 #pragma unroll
-  for (int k = 0; k < kAdamBlockElems / 1024; ++k) {
+    for (int k = 0; k < KC; ++k) {
+      const int64_t e = e0 + k * 1024 + threadIdx.x * 4;
+      if (d.g_bf16) {
+        const u16x4_t gb = __builtin_nontemporal_load((const u16x4_t*)((const uint16_t*)d.g + e));
+        g4[k] = f32x4_t{bf16_to_f32(gb[0]), bf16_to_f32(gb[1]), bf16_to_f32(gb[2]), bf16_to_f32(gb[3])};
+      } else {
+        g4[k] = __builtin_nontemporal_load((const f32x4_t*)((const float*)d.g + e));
+      }
+      m4[k] = __builtin_nontemporal_load((const f32x4_t*)(d.m + e));
+      v4[k] = __builtin_nontemporal_load((const f32x4_t*)(d.v + e));
+      if (d.p_bf16) {
+        const u16x4_t pb = __builtin_nontemporal_load((const u16x4_t*)((const uint16_t*)d.p + e));
+        p4[k] = f32x4_t{bf16_to_f32(pb[0]), bf16_to_f32(pb[1]), bf16_to_f32(pb[2]), bf16_to_f32(pb[3])};
+      } else {
+        p4[k] = __builtin_nontemporal_load((const f32x4_t*)((const float*)d.p + e));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      const int64_t e = e0 + k * 1024 + threadIdx.x * 4;
+      float p[4] = {p4[k][0], p4[k][1], p4[k][2], p4[k][3]};
+      float m[4] = {m4[k][0], m4[k][1], m4[k][2], m4[k][3]}, v[4] = {v4[k][0], v4[k][1], v4[k][2], v4[k][3]};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) adam_one(p[q], g4[k][q], m[q], v[q], a);
+      if (d.p_bf16) {
+        const uint32_t lo = f32x2_to_bf16x2(p[0], p[1]), hi = f32x2_to_bf16x2(p[2], p[3]);
+        __builtin_nontemporal_store(u32x2_t{lo, hi}, (u32x2_t*)((uint16_t*)d.p + e));
+      } else {
+        __builtin_nontemporal_store(f32x4_t{p[0], p[1], p[2], p[3]}, (f32x4_t*)((float*)d.p + e));
+      }
+      __builtin_nontemporal_store(f32x4_t{m[0], m[1], m[2], m[3]}, (f32x4_t*)(d.m + e));
+      __builtin_nontemporal_store(f32x4_t{v[0], v[1], v[2], v[3]}, (f32x4_t*)(d.v + e));
+    }
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
     const int64_t e = e0 + k * 1024 + threadIdx.x * 4;
     if (e >= d.n) break;
     if (d.vec && e + 4 <= d.n) {
