@@ -63,14 +63,21 @@ def parse():
     ap.add_argument("--clip", action="store_true",
                     help="time qk_clip_apply alone on the MLA layer's q_b (12288 x 1536) and kv_b (16384 x 512) "
                          "with every head above tau (4 bytes per clipped bf16 element)")
+    ap.add_argument("--reference", action="store_true",
+                    help="time the vendor baselines on this GPU: torch's streaming kernels (read, copy, add of "
+                         "4 GiB fp32 tensors) and hipBLASLt (torch.bmm / mm) on the Newton-Schulz product shapes of "
+                         "64 expert matrices and an 8192^3 bf16 GEMM")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain streaming copy of MIB MiB (read + write) five times, "
                          "to calibrate the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ns_gemm_traffic_mha_layer.txt")
 GEMM_SOURCE = os.path.join(ROOT, "muonclip_step_amd", "csrc", "ns_gemm.hip")
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"ns_gemm_traffic_{workload}.txt")
 
 
 def gemm_source_hash() -> str:
@@ -80,12 +87,14 @@ def gemm_source_hash() -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per ns_gemm launch from the committed rocprofv3 counter runs,
-    or None when they were taken on another workload or another kernel source."""
-    if workload != "mha_layer" or not os.path.exists(TRAFFIC_FILE):
+    """Memory bytes per ns_gemm launch from the committed rocprofv3 counter
+    runs of this workload (profiles/ns_gemm_traffic_<workload>.txt), or None
+    when there are none or they were taken on another kernel source."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
@@ -341,6 +350,54 @@ def attention_bench(args):
     }), flush=True)
 
 
+def reference_bench(args):
+    """Vendor baselines on this GPU, as context for the roofline fractions:
+    the HBM rates torch's own streaming kernels reach, and the bf16 rates of
+    hipBLASLt (through torch.bmm / torch.mm, every operand contiguous) on the
+    three Newton-Schulz products of a 64-matrix wave of 2048 x 7168 expert
+    matrices (full products: the library computes only the upper tiles of
+    the two symmetric ones) and on an 8192^3 GEMM. Prints one JSON line."""
+    import torch
+    dev = torch.device("cuda:0")
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {}
+    n = 1 << 29                                    # 2 GiB fp32 per tensor (one launch per op)
+    a = torch.ones(n, device=dev)
+    b = torch.ones(n, device=dev)
+    c = torch.empty(n, device=dev)
+    out["hbm_read_sum_gbs"] = round(4 * n / (timed(lambda: a.sum()) * 1e-3) / 1e9, 1)
+    out["hbm_copy_gbs"] = round(8 * n / (timed(lambda: c.copy_(a)) * 1e-3) / 1e9, 1)
+    out["hbm_add_2r1w_gbs"] = round(12 * n / (timed(lambda: torch.add(a, b, out=c)) * 1e-3) / 1e9, 1)
+    del a, b, c
+    B, m, k = 64, 2048, 7168
+    P = torch.randn(B, m, m, device=dev).to(torch.bfloat16)
+    X = torch.randn(B, m, k, device=dev).to(torch.bfloat16)
+    XT = X.transpose(1, 2).contiguous()
+    Y = torch.empty(B, m, k, device=dev, dtype=torch.bfloat16)
+    G = torch.empty(B, m, m, device=dev, dtype=torch.bfloat16)
+    f_mmk, f_mmm = 2.0 * B * m * m * k, 2.0 * B * m ** 3
+    out["hipblaslt_apply_tflops"] = round(f_mmk / (timed(lambda: torch.bmm(P, X, out=Y)) * 1e-3) / 1e12, 1)
+    out["hipblaslt_gram_full_tflops"] = round(f_mmk / (timed(lambda: torch.bmm(X, XT, out=G)) * 1e-3) / 1e12, 1)
+    out["hipblaslt_aa_full_tflops"] = round(f_mmm / (timed(lambda: torch.bmm(P, P, out=G)) * 1e-3) / 1e12, 1)
+    del P, X, XT, Y, G
+    s8 = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    t8 = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    out["hipblaslt_mm8192_tflops"] = round(2.0 * 8192 ** 3 / (timed(lambda: torch.mm(s8, t8)) * 1e-3) / 1e12, 1)
+    print(json.dumps({"metric": "vendor baselines on this GPU", "unit": "GB/s and TFLOP/s", "n_gpus": 1,
+                      "config": {"workload": "reference", "expert_wave": "64 x (2048 x 7168)"}, **out}), flush=True)
+
+
 def clip_bench(args):
     """qk_clip_apply on the MLA projections that carry head rows (q_b: q^C
     rows by sqrt(gamma), q^R rows by gamma; kv_b: k^C rows by sqrt(gamma))
@@ -419,6 +476,9 @@ def main():
         return
     if args.clip:
         clip_bench(args)
+        return
+    if args.reference:
+        reference_bench(args)
         return
 
     import muonclip_step_amd as mc
