@@ -310,6 +310,25 @@ WavePlan plan_wave(const Group& g, int nb, int cus) {
   return w;
 }
 
+// Whether a wave runs its first two Newton-Schulz iterations in Gram space
+// (two m x m products and an m x n apply in place of a Gram and an apply):
+// for groups with n >= 2 m, where the n-sized products saved outweigh the
+// three m x m products added, and with unsplit symmetric products whose A is
+// handed over in fragment order. At least one iteration follows it, so the
+// fused update stays on an ordinary apply.
+bool gram_head(const Group& g, const WavePlan& w, int ns_steps) {
+  return w.frag && ns_steps >= 3 && g.np >= 2 * g.mp;
+}
+
+// Dense-GEMM flops of one wave's Newton-Schulz products (2 m n k each,
+// symmetric products counted in full).
+double wave_flops(const Group& g, const WavePlan& w, int ns_steps) {
+  const double m = (double)g.m, n = (double)g.n;
+  const double mmn = 2.0 * m * m * n, mmm = 2.0 * m * m * m;
+  if (gram_head(g, w, ns_steps)) return ((ns_steps - 1) * 2.0 * mmn + (ns_steps + 3) * mmm) * w.nb;
+  return ns_steps * (2.0 * mmn + mmm) * w.nb;
+}
+
 mc_status launch_gemm_planned(const GemmPlan& gp, GemmKind kind, bool split_pair, GemmArgs a, hipStream_t s,
                               void* ws_base, size_t off_splitk, double flops, const FusedUpd* upd = nullptr,
                               double upd_bytes = 0.0) {
@@ -439,83 +458,115 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
 
   // 2. Newton-Schulz iterations
   const double mm_ = (double)g.m, nn_ = (double)g.n;
-  for (int it = 0; it < hp.ns_steps; ++it) {
-    const bool first = it == 0;
-    uint16_t* x_cur = X[it & 1];
-    uint16_t* x_nxt = X[(it + 1) & 1];
-    // Gram: A = s0^2 X X^T, stored as a bf16 pair A_hi + A_lo
-    {
-      GemmArgs a{};
-      a.M = (int32_t)mp; a.N = (int32_t)mp; a.batch = nb;
-      a.lda = (int32_t)np; a.ldb = (int32_t)np; a.bsa = mp * np; a.bsb = mp * np;
-      a.nseg = 1; a.seg[0] = {x_cur, x_cur, w.kt_gram}; a.ktiles = w.kt_gram;
-      a.epi.alpha = 1.0f; a.epi.scale_pow = first ? 2 : 0; a.epi.scale = scale;
-      a.epi.out_hi = Ahi; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
-      if (w.frag) {
-        a.epi.frag_out = (float*)Alo; a.epi.frag_nb = (int32_t)(mp / 32); a.epi.bs_frag = mp * mp;
-      } else {
-        a.epi.out_lo = Alo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp;
-      }
-      mc_status st = launch_gemm_planned(w.gram, GEMM_GRAM, g.split, a, s, ws, w.off_splitk,
-                                         2.0 * mm_ * mm_ * nn_ * nb);
-      if (st) return st;
+  const int kt_sq = (int)(mp / kGemmBK);
+  // Gram: A = s0^2 X X^T (s0 on the first iteration only), stored as a bf16
+  // pair A_hi + A_lo, or as A_hi and the fp32 fragment copy
+  auto gram = [&](const uint16_t* x, bool first) -> mc_status {
+    GemmArgs a{};
+    a.M = (int32_t)mp; a.N = (int32_t)mp; a.batch = nb;
+    a.lda = (int32_t)np; a.ldb = (int32_t)np; a.bsa = mp * np; a.bsb = mp * np;
+    a.nseg = 1; a.seg[0] = {x, x, w.kt_gram}; a.ktiles = w.kt_gram;
+    a.epi.alpha = 1.0f; a.epi.scale_pow = first ? 2 : 0; a.epi.scale = scale;
+    a.epi.out_hi = Ahi; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
+    if (w.frag) {
+      a.epi.frag_out = (float*)Alo; a.epi.frag_nb = (int32_t)(mp / 32); a.epi.bs_frag = mp * mp;
+    } else {
+      a.epi.out_lo = Alo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp;
     }
-    // Poly: P = a I + b A + c A A
-    {
-      GemmArgs a{};
-      a.M = (int32_t)mp; a.N = (int32_t)mp; a.batch = nb;
-      a.lda = (int32_t)mp; a.ldb = (int32_t)mp; a.bsa = mp * mp; a.bsb = mp * mp;
-      const int kt = (int)(mp / kGemmBK);
-      if (g.split) {
-        a.nseg = 3;
-        a.seg[0] = {Ahi, Ahi, kt}; a.seg[1] = {Ahi, Alo, kt}; a.seg[2] = {Alo, Ahi, kt};
-      } else {
-        a.nseg = 1; a.seg[0] = {Ahi, Ahi, kt};
-      }
-      a.ktiles = w.kt_poly;
-      a.epi.alpha = hp.ns_c; a.epi.beta = hp.ns_b; a.epi.diag = hp.ns_a;
-      if (w.frag) {
-        a.epi.frag_in = (const float*)Alo; a.epi.frag_nb = (int32_t)(mp / 32); a.epi.bs_frag = mp * mp;
-      } else {
-        a.epi.cin_hi = Ahi; a.epi.cin_lo = Alo; a.epi.ld_cin = (int32_t)mp; a.epi.bs_cin = mp * mp;
-      }
-      a.epi.out_hi = Phi; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
-      if (Plo) { a.epi.out_lo = Plo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp; }
-      mc_status st = launch_gemm_planned(w.poly, GEMM_POLY, g.split, a, s, ws, w.off_splitk,
-                                         2.0 * mm_ * mm_ * mm_ * nb);
-      if (st) return st;
+    return launch_gemm_planned(w.gram, GEMM_GRAM, g.split, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * nn_ * nb);
+  };
+  // Poly: P = a I + b A + c A A, to out_hi (+ P_lo with operand pairs)
+  auto poly = [&](uint16_t* out_hi) -> mc_status {
+    GemmArgs a{};
+    a.M = (int32_t)mp; a.N = (int32_t)mp; a.batch = nb;
+    a.lda = (int32_t)mp; a.ldb = (int32_t)mp; a.bsa = mp * mp; a.bsb = mp * mp;
+    if (g.split) {
+      a.nseg = 3;
+      a.seg[0] = {Ahi, Ahi, kt_sq}; a.seg[1] = {Ahi, Alo, kt_sq}; a.seg[2] = {Alo, Ahi, kt_sq};
+    } else {
+      a.nseg = 1; a.seg[0] = {Ahi, Ahi, kt_sq};
     }
-    // Apply: X' = s0 P X, C[i][j] = sum_k P[i][k] X[k][j] with X read as [k][n]
-    {
-      GemmArgs a{};
-      a.M = (int32_t)mp; a.N = (int32_t)np; a.batch = nb;
-      a.lda = (int32_t)mp; a.ldb = (int32_t)np; a.bsa = mp * mp; a.bsb = mp * np;
-      const int kt = (int)(mp / kGemmBK);
-      if (g.split) { a.nseg = 2; a.seg[0] = {Phi, x_cur, kt}; a.seg[1] = {Plo, x_cur, kt}; }
-      else { a.nseg = 1; a.seg[0] = {Phi, x_cur, kt}; }
-      a.ktiles = w.kt_apply;
-      a.epi.alpha = 1.0f; a.epi.scale_pow = first ? 1 : 0; a.epi.scale = scale;
-      a.epi.out_hi = x_nxt; a.epi.ld_hi = (int32_t)np; a.epi.bs_hi = mp * np;
-      const bool last = it + 1 == hp.ns_steps;
-      if (last && fu.n > 0) {
-        mc_status ws_ = wait_smax(smax_ready, s_max, s);
-        if (ws_) return ws_;
-      }
-      if (last && fu.n > 0 && gamma_once && *gamma_once) {
+    a.ktiles = w.kt_poly;
+    a.epi.alpha = hp.ns_c; a.epi.beta = hp.ns_b; a.epi.diag = hp.ns_a;
+    if (w.frag) {
+      a.epi.frag_in = (const float*)Alo; a.epi.frag_nb = (int32_t)(mp / 32); a.epi.bs_frag = mp * mp;
+    } else {
+      a.epi.cin_hi = Ahi; a.epi.cin_lo = Alo; a.epi.ld_cin = (int32_t)mp; a.epi.bs_cin = mp * mp;
+    }
+    a.epi.out_hi = out_hi; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
+    if (Plo) { a.epi.out_lo = Plo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp; }
+    return launch_gemm_planned(w.poly, GEMM_POLY, g.split, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * mm_ * nb);
+  };
+  // C = L R of two exactly symmetric m x m matrices (the Gram-space head):
+  // R is read by rows, which are its columns; C is symmetric up to rounding
+  // (L and R are polynomials in one matrix, so they commute) and only its
+  // upper tiles are computed, then mirrored. to_a: store C as A_hi plus the
+  // fp32 fragment copy the next Poly reads.
+  auto sym_product = [&](const uint16_t* l, const uint16_t* r, uint16_t* out, bool to_a) -> mc_status {
+    GemmArgs a{};
+    a.M = (int32_t)mp; a.N = (int32_t)mp; a.batch = nb;
+    a.lda = (int32_t)mp; a.ldb = (int32_t)mp; a.bsa = mp * mp; a.bsb = mp * mp;
+    a.nseg = 1; a.seg[0] = {l, r, kt_sq}; a.ktiles = kt_sq;
+    a.epi.alpha = 1.0f;
+    a.epi.out_hi = out; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
+    if (to_a) { a.epi.frag_out = (float*)Alo; a.epi.frag_nb = (int32_t)(mp / 32); a.epi.bs_frag = mp * mp; }
+    return launch_gemm_planned(w.poly, GEMM_GRAM, false, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * mm_ * nb);
+  };
+  // Apply: X' = s0 P X (s0 on the first product of X0 only), C[i][j] =
+  // sum_k P[i][k] X[k][j] with X read as [k][n]; the last one carries the
+  // update when it is fused
+  auto apply = [&](const uint16_t* p_hi, const uint16_t* p_lo, const uint16_t* x_in, uint16_t* x_out,
+                   bool first, bool last) -> mc_status {
+    GemmArgs a{};
+    a.M = (int32_t)mp; a.N = (int32_t)np; a.batch = nb;
+    a.lda = (int32_t)mp; a.ldb = (int32_t)np; a.bsa = mp * mp; a.bsb = mp * np;
+    if (p_lo) { a.nseg = 2; a.seg[0] = {p_hi, x_in, kt_sq}; a.seg[1] = {p_lo, x_in, kt_sq}; }
+    else { a.nseg = 1; a.seg[0] = {p_hi, x_in, kt_sq}; }
+    a.ktiles = w.kt_apply;
+    a.epi.alpha = 1.0f; a.epi.scale_pow = first ? 1 : 0; a.epi.scale = scale;
+    a.epi.out_hi = x_out; a.epi.ld_hi = (int32_t)np; a.epi.bs_hi = mp * np;
+    const bool upd = last && fu.n > 0;
+    if (upd) {
+      if (mc_status ws_ = wait_smax(smax_ready, s_max, s)) return ws_;
+      if (gamma_once && *gamma_once) {
         fu.gamma_out = *gamma_once; fu.gamma_slots = slots;
         *gamma_once = nullptr;
       }
-      mc_status st = launch_gemm_planned(w.apply, GEMM_APPLY, false, a, s, ws, w.off_splitk,
-                                         2.0 * mm_ * mm_ * nn_ * nb, last && fu.n > 0 ? &fu : nullptr,
-                                         last ? fu_bytes : 0.0);
-      if (st) return st;
     }
+    return launch_gemm_planned(w.apply, GEMM_APPLY, false, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * nn_ * nb,
+                               upd ? &fu : nullptr, last ? fu_bytes : 0.0);
+  };
+
+  int cur = 0, it0 = 0;   // X[cur] holds iterate X_it0
+  if (gram_head(g, w, hp.ns_steps)) {
+    // The first two iterations in Gram space: with A0 = X0 X0^T and
+    // P0 = p(A0), X1 = P0 X0 gives X1 X1^T = P0 A0 P0, so A1 and P1 = p(A1)
+    // follow from m x m products alone and X2 = (P1 P0) X0 takes one
+    // n-sized product instead of three. The m x m scratch T lives in X[1],
+    // which X2 overwrites last.
+    uint16_t* T = X[1];
+    mc_status st = gram(X[0], true);
+    if (!st) st = poly(Phi);                        // P0
+    if (!st) st = sym_product(Ahi, Phi, T, false);  // A0 P0
+    if (!st) st = sym_product(Phi, T, Ahi, true);   // A1 = P0 (A0 P0)
+    if (!st) st = poly(T);                          // P1
+    if (!st) st = sym_product(T, Phi, Ahi, false);  // Q = P1 P0
+    if (!st) st = apply(Ahi, nullptr, X[0], X[1], true, false);   // X2 = s0 Q X0
+    if (st) return st;
+    cur = 1; it0 = 2;
+  }
+  for (int it = it0; it < hp.ns_steps; ++it) {
+    mc_status st = gram(X[cur], it == 0);
+    if (!st) st = poly(Phi);
+    if (!st) st = apply(Phi, Plo, X[cur], X[cur ^ 1], it == 0, it + 1 == hp.ns_steps);
+    if (st) return st;
+    cur ^= 1;
   }
   if (fu.n > 0) return MC_OK;
 
   // 3. update + decay + QK-Clip rows
   if (mc_status ws_ = wait_smax(smax_ready, s_max, s)) return ws_;
-  uint16_t* x_final = X[hp.ns_steps & 1];   // O in [m][n]: W itself (wide) or W^T (tall)
+  uint16_t* x_final = X[cur];   // O in [m][n]: W itself (wide) or W^T (tall)
   for (int b0 = 0; b0 < nb; b0 += kMaxBatchMats) {
     UpdArgs a{};
     a.decay = decay; a.s_max = s_max; a.heads = heads; a.tau = hp.tau; a.clip_global = hp.clip_global;
@@ -567,27 +618,26 @@ int largest_wave(const Group& g, int limit, size_t ws_bytes) {
 // of nb matrices, independent of every other chain.
 struct Chain { int gi, b0, nb; double flops; };
 
-// Relative time of one wave's three Newton-Schulz products: every launch
-// runs in rounds of one tile per CU, so a round that only part of the chip
-// has tiles for costs as much as a full one. A round costs its k-stages
-// times the tile's share of a 256x256 tile's work (128 and 64 tiles run at
-// about 0.8 of that rate per flop), split-K launches their partial k range.
-double wave_cost(const Group& g, int nb, int cus) {
+// Relative time of one wave's Newton-Schulz products: every launch runs in
+// rounds of one tile per CU, so a round that only part of the chip has
+// tiles for costs as much as a full one. A round costs its k-stages times
+// the tile's share of a 256x256 tile's work (128 and 64 tiles run at about
+// 0.8 of that rate per flop), split-K launches their partial k range.
+double wave_cost(const Group& g, int nb, int cus, int ns_steps) {
   const WavePlan w = plan_wave(g, nb, cus);
-  double cost = 0.0;
-  const GemmPlan* ps[3] = {&w.gram, &w.poly, &w.apply};
-  const bool sym[3] = {true, true, false};
-  for (int k = 0; k < 3; ++k) {
-    const GemmPlan& gp = *ps[k];
+  auto launch = [&](const GemmPlan& gp, bool sym) {
     const int d = gemm_tile_dim(gp.tile);
-    const int64_t per = (sym[k] && gp.splits == 1) ? (int64_t)gp.tiles_m * (gp.tiles_m + 1) / 2
-                                                   : (int64_t)gp.tiles_m * gp.tiles_n;
+    const int64_t per = (sym && gp.splits == 1) ? (int64_t)gp.tiles_m * (gp.tiles_m + 1) / 2
+                                                : (int64_t)gp.tiles_m * gp.tiles_n;
     const int64_t items = per * gp.splits * nb;
     const double rounds = (double)((items + cus - 1) / cus);
     const double share = (double)d * d / (256.0 * 256.0) / (d == 256 ? 1.0 : 0.8);
-    cost += rounds * gp.kt_per_split * share + 2.0;   // + launch and drain, about two k-stages
-  }
-  return cost;
+    return rounds * gp.kt_per_split * share + 2.0;   // + launch and drain, about two k-stages
+  };
+  const double gram = launch(w.gram, true), sq = launch(w.poly, true), apply = launch(w.apply, false);
+  // the Gram-space head trades a Gram and an apply for three m x m products
+  if (gram_head(g, w, ns_steps)) return (ns_steps - 1) * (gram + apply) + (ns_steps + 3) * sq;
+  return ns_steps * (gram + sq + apply);
 }
 
 // Waves of at most cap[gi] matrices per group. A group larger than one wave
@@ -609,7 +659,7 @@ std::vector<Chain> plan_chains(const std::vector<Group>& groups, const std::vect
       auto cost_of = [&](int nb) {
         auto it = memo.find(nb);
         if (it != memo.end()) return it->second;
-        return memo[nb] = wave_cost(g, nb, cus);
+        return memo[nb] = wave_cost(g, nb, cus, ns_steps);
       };
       double best = 0.0;
       for (int nb : sizes) best += cost_of(nb);
@@ -625,7 +675,7 @@ std::vector<Chain> plan_chains(const std::vector<Group>& groups, const std::vect
     }
     for (int b0 = 0, w = 0; w < (int)sizes.size(); ++w) {
       const int nb = sizes[w];
-      const double f = (double)ns_steps * 2.0 * (2.0 * g.n * g.m * g.m + (double)g.m * g.m * g.m) * nb;
+      const double f = wave_flops(g, plan_wave(g, nb, cus), ns_steps);
       out.push_back({(int)gi, b0, nb, f});
       b0 += nb;
     }

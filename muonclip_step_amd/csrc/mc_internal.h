@@ -80,6 +80,8 @@ struct GemmArgs {
 enum GemmTile { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2 };
 // which Newton-Schulz product a launch computes; fixes the epilogue:
 //   GRAM  A = s^2 X X^T      -> bf16 A_hi + A_lo           (symmetric tiles)
+//         (also L R of two symmetric m x m matrices, R read by rows, to bf16
+//         C alone or to C_hi + the fp32 fragment copy)
 //   POLY  P = a I + b A + c A A -> bf16 P_hi (+ P_lo)        (symmetric tiles)
 //   APPLY X' = s P X          -> bf16 X' (B = X read as [k][n])
 enum GemmKind { GEMM_GRAM = 0, GEMM_POLY = 1, GEMM_APPLY = 2 };

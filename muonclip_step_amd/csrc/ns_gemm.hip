@@ -9,8 +9,10 @@
 // so no transposed copy of X is ever written. One kernel serves all three,
 // batched over the matrices of one shape group (grid = tiles x splits x
 // batch, mapped XCD-major so the tiles of one matrix share an XCD's L2). The
-// two symmetric products compute only the tiles on and above the diagonal
-// and store each off-diagonal tile a second time, transposed.
+// symmetric products (X X^T, A A, and the products of two commuting
+// symmetric m x m matrices that run the first iterations in Gram space)
+// compute only the tiles on and above the diagonal and store each
+// off-diagonal tile a second time, transposed.
 //
 // gfx950 design: v_mfma_f32_32x32x16_bf16 with fp32 accumulation; a block of
 // 2x2 waves (or 2x4) owns a BMxBN tile, each wave a (BM/2)x(BN/2) (or
@@ -767,7 +769,8 @@ hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const G
     // fragment order (with them, A_lo is an operand too)
     if (split_pair) launch_epi<E_SYM | E_HI | E_LO>(tile, a, total, s, u);
     else if (frag) launch_epi<E_SYM | E_HI | E_FOUT>(tile, a, total, s, u);
-    else launch_epi<E_SYM | E_HI | E_LO | E_LOMIR>(tile, a, total, s, u);
+    else if (e.out_lo) launch_epi<E_SYM | E_HI | E_LO | E_LOMIR>(tile, a, total, s, u);
+    else launch_epi<E_SYM | E_HI>(tile, a, total, s, u);   // bf16 product of two symmetric matrices
   } else if (kind == GEMM_POLY) {
     if (split_pair) launch_epi<E_SYM | E_CIN | E_DIAG | E_HI | E_LO>(tile, a, total, s, u);
     else if (frag) launch_epi<E_SYM | E_FIN | E_DIAG | E_HI>(tile, a, total, s, u);

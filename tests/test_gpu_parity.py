@@ -171,6 +171,33 @@ def test_group_on_128_tiles_against_oracle():
         check_matrix(st, hp)
 
 
+@pytest.mark.parametrize("ns_steps,f32_weight", [(5, False), (5, True), (3, False), (3, True), (2, False)])
+def test_gram_space_head_against_oracle(ns_steps, f32_weight):
+    """Six matrices of one group with n >= 2 m (m = 1100, n = 2300: wide and
+    tall, padded rows, ragged against the 128 tiles) whose first two
+    Newton-Schulz iterations run in Gram space (X2 = P1 P0 X0 with
+    P1 = p(P0 A0 P0)); ns_steps = 2 leaves no iteration after the head and
+    takes the plain path. An f32 weight turns off the fused update, so the
+    separate update reads O from whichever X buffer holds it."""
+    print("gram head", ns_steps, f32_weight, flush=True)
+    states = []
+    for k in range(6):
+        shape = (1100, 2300) if k % 2 == 0 else (2300, 1100)
+        w_dtype = "f32" if f32_weight and k == 3 else "bf16"
+        spec = wl.MatrixSpec("h", *shape, w_dtype, init_std=0.5, grad_std=1.0, mom_std=1.0)
+        seed = 3100 + k
+        w = wl.normal(seed, 0, shape, 0.5)
+        w = wl.quantize_f32(w) if w_dtype == "f32" else wl.quantize_bf16(w)
+        g = wl.quantize_f32(wl.normal(seed, 1, shape, 1.0))
+        m = wl.quantize_f32(wl.normal(seed, 2, shape, 1.0))
+        states.append(State(spec, w, g, m, ld_pad=8 * (k % 3)))
+    hp = mc.hparams(lr=0.01, ns_steps=ns_steps)
+    mc.muonclip_step([st.desc() for st in states], hp)
+    torch.cuda.synchronize()
+    for st in states:
+        check_matrix(st, hp)
+
+
 def test_zero_gradient_and_momentum_decay_only():
     spec = wl.MatrixSpec("z", 96, 160, "f32")
     w = wl.quantize_f32(wl.normal(77, 0, (96, 160), 1.0))
