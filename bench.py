@@ -601,6 +601,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "ns_gemm", "achieved": round(gemm_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(cfg.name),
+                     "algorithmic_bytes_per_launch": round(g.get("bytes", 0.0) / max(1, g["launches"])),
                      "launches_per_step": per_step.get("ns_gemm", {}).get("launches"),
                      "ms_per_step": round(per_step.get("ns_gemm", {}).get("ms", float("nan")), 3),
                      "flops_per_step": g["flops"] / prof_steps,

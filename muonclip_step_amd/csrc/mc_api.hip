@@ -329,14 +329,17 @@ double wave_flops(const Group& g, const WavePlan& w, int ns_steps) {
   return ns_steps * (2.0 * mmn + mmm) * w.nb;
 }
 
+// flops and bytes are what the profile records for the launch: its dense
+// flops and its algorithmic bytes (bf16 operands read once, the bf16 output
+// written once, plus the weight traffic of a fused update).
 mc_status launch_gemm_planned(const GemmPlan& gp, GemmKind kind, bool split_pair, GemmArgs a, hipStream_t s,
-                              void* ws_base, size_t off_splitk, double flops, const FusedUpd* upd = nullptr,
-                              double upd_bytes = 0.0) {
+                              void* ws_base, size_t off_splitk, double flops, double bytes,
+                              const FusedUpd* upd = nullptr) {
   a.tiles_m = gp.tiles_m; a.tiles_n = gp.tiles_n;
   a.splits = gp.splits; a.kt_per_split = gp.kt_per_split;
   a.partial = gp.splits > 1 ? (float*)((char*)ws_base + off_splitk) : nullptr;
   {
-    Prof pr(F_GEMM, s, flops, upd_bytes);
+    Prof pr(F_GEMM, s, flops, bytes);
     hipError_t e = launch_ns_gemm(gp.tile, kind, split_pair, a, s, upd);
     if (e != hipSuccess) return fail(MC_ERR_HIP, "ns_gemm launch: %s", hipGetErrorString(e));
   }
@@ -473,7 +476,8 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
     } else {
       a.epi.out_lo = Alo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp;
     }
-    return launch_gemm_planned(w.gram, GEMM_GRAM, g.split, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * nn_ * nb);
+    return launch_gemm_planned(w.gram, GEMM_GRAM, g.split, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * nn_ * nb,
+                               (2.0 * mm_ * nn_ + 2.0 * mm_ * mm_) * nb);
   };
   // Poly: P = a I + b A + c A A, to out_hi (+ P_lo with operand pairs)
   auto poly = [&](uint16_t* out_hi) -> mc_status {
@@ -495,7 +499,8 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
     }
     a.epi.out_hi = out_hi; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
     if (Plo) { a.epi.out_lo = Plo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp; }
-    return launch_gemm_planned(w.poly, GEMM_POLY, g.split, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * mm_ * nb);
+    return launch_gemm_planned(w.poly, GEMM_POLY, g.split, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * mm_ * nb,
+                               4.0 * mm_ * mm_ * nb);
   };
   // C = L R of two exactly symmetric m x m matrices (the Gram-space head):
   // R is read by rows, which are its columns; C is symmetric up to rounding
@@ -510,7 +515,8 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
     a.epi.alpha = 1.0f;
     a.epi.out_hi = out; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
     if (to_a) { a.epi.frag_out = (float*)Alo; a.epi.frag_nb = (int32_t)(mp / 32); a.epi.bs_frag = mp * mp; }
-    return launch_gemm_planned(w.poly, GEMM_GRAM, false, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * mm_ * nb);
+    return launch_gemm_planned(w.poly, GEMM_GRAM, false, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * mm_ * nb,
+                               6.0 * mm_ * mm_ * nb);
   };
   // Apply: X' = s0 P X (s0 on the first product of X0 only), C[i][j] =
   // sum_k P[i][k] X[k][j] with X read as [k][n]; the last one carries the
@@ -533,8 +539,10 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
         *gamma_once = nullptr;
       }
     }
+    // operands P and X; X' is written unless the update consumes it
+    const double bytes = (2.0 * mm_ * mm_ + 2.0 * mm_ * nn_ + (upd ? 0.0 : 2.0 * mm_ * nn_)) * nb;
     return launch_gemm_planned(w.apply, GEMM_APPLY, false, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * nn_ * nb,
-                               upd ? &fu : nullptr, last ? fu_bytes : 0.0);
+                               bytes + (upd ? fu_bytes : 0.0), upd ? &fu : nullptr);
   };
 
   int cur = 0, it0 = 0;   // X[cur] holds iterate X_it0
