@@ -18,6 +18,7 @@
 // hi + lo bf16 pairs (3 and 2 MFMA passes), which keeps those small-m shapes
 // well inside the 2e-2 relative Frobenius bound.
 #include <math.h>
+#include <cmath>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -310,14 +311,17 @@ WavePlan plan_wave(const Group& g, int nb, int cus) {
   return w;
 }
 
-// Whether a wave runs its first two Newton-Schulz iterations in Gram space
-// (two m x m products and an m x n apply in place of a Gram and an apply):
-// for groups with n >= 2 m, where the n-sized products saved outweigh the
-// three m x m products added, and with unsplit symmetric products whose A is
-// handed over in fragment order. At least one iteration follows it, so the
-// fused update stays on an ordinary apply.
+// Whether a wave runs its first kGramHead Newton-Schulz iterations in Gram
+// space (each iteration after the first trades a Gram and an apply, both
+// n-sized, for three m x m products): for groups with n >= 2 m, where the
+// n-sized products saved outweigh the m x m products added, with unsplit
+// symmetric products whose A is handed over in fragment order and an unsplit
+// apply (whose epilogue adds the identity part of the accumulated product).
+// At least one iteration follows it, so the fused update stays on an
+// ordinary apply.
+constexpr int kGramHead = 3;   // at least 2
 bool gram_head(const Group& g, const WavePlan& w, int ns_steps) {
-  return w.frag && ns_steps >= 3 && g.np >= 2 * g.mp;
+  return w.frag && w.apply.splits == 1 && ns_steps > kGramHead && g.np >= 2 * g.mp;
 }
 
 // Dense-GEMM flops of one wave's Newton-Schulz products (2 m n k each,
@@ -325,7 +329,9 @@ bool gram_head(const Group& g, const WavePlan& w, int ns_steps) {
 double wave_flops(const Group& g, const WavePlan& w, int ns_steps) {
   const double m = (double)g.m, n = (double)g.n;
   const double mmn = 2.0 * m * m * n, mmm = 2.0 * m * m * m;
-  if (gram_head(g, w, ns_steps)) return ((ns_steps - 1) * 2.0 * mmn + (ns_steps + 3) * mmm) * w.nb;
+  // head: Gram, P_0 .. P_{k-1}, two products per A_j and one per R_j, the apply
+  const int k = kGramHead;
+  if (gram_head(g, w, ns_steps)) return ((ns_steps - k + 1) * 2.0 * mmn + (ns_steps + 3 * (k - 1)) * mmm) * w.nb;
   return ns_steps * (2.0 * mmn + mmm) * w.nb;
 }
 
@@ -502,27 +508,30 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
     return launch_gemm_planned(w.poly, GEMM_POLY, g.split, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * mm_ * nb,
                                4.0 * mm_ * mm_ * nb);
   };
-  // C = L R of two exactly symmetric m x m matrices (the Gram-space head):
-  // R is read by rows, which are its columns; C is symmetric up to rounding
-  // (L and R are polynomials in one matrix, so they commute) and only its
-  // upper tiles are computed, then mirrored. to_a: store C as A_hi plus the
-  // fp32 fragment copy the next Poly reads.
-  auto sym_product = [&](const uint16_t* l, const uint16_t* r, uint16_t* out, bool to_a) -> mc_status {
+  // C = L R + diag I of two exactly symmetric m x m matrices (the Gram-space
+  // head): R is read by rows, which are its columns; C is symmetric up to
+  // rounding (L and R are polynomials in one matrix, so they commute) and only
+  // its upper tiles are computed, then mirrored. to_a: store C as A_hi plus
+  // the fp32 fragment copy the next Poly reads.
+  auto sym_product = [&](const uint16_t* l, const uint16_t* r, uint16_t* out, bool to_a, float diag = 0.0f,
+                         const uint16_t* c = nullptr, float beta = 0.0f) -> mc_status {
     GemmArgs a{};
     a.M = (int32_t)mp; a.N = (int32_t)mp; a.batch = nb;
     a.lda = (int32_t)mp; a.ldb = (int32_t)mp; a.bsa = mp * mp; a.bsb = mp * mp;
     a.nseg = 1; a.seg[0] = {l, r, kt_sq}; a.ktiles = kt_sq;
-    a.epi.alpha = 1.0f;
+    a.epi.alpha = 1.0f; a.epi.diag = diag;
+    if (c) { a.epi.cin_hi = c; a.epi.beta = beta; a.epi.ld_cin = (int32_t)mp; a.epi.bs_cin = mp * mp; }
     a.epi.out_hi = out; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
     if (to_a) { a.epi.frag_out = (float*)Alo; a.epi.frag_nb = (int32_t)(mp / 32); a.epi.bs_frag = mp * mp; }
     return launch_gemm_planned(w.poly, GEMM_GRAM, false, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * mm_ * nb,
-                               6.0 * mm_ * mm_ * nb);
+                               (c ? 8.0 : 6.0) * mm_ * mm_ * nb);
   };
   // Apply: X' = s0 P X (s0 on the first product of X0 only), C[i][j] =
   // sum_k P[i][k] X[k][j] with X read as [k][n]; the last one carries the
-  // update when it is fused
+  // update when it is fused. x_coef != 0: X' = s0 (P X + x_coef X), the
+  // second term added in fp32 to the rounded product.
   auto apply = [&](const uint16_t* p_hi, const uint16_t* p_lo, const uint16_t* x_in, uint16_t* x_out,
-                   bool first, bool last) -> mc_status {
+                   bool first, bool last, float x_coef = 0.0f) -> mc_status {
     GemmArgs a{};
     a.M = (int32_t)mp; a.N = (int32_t)np; a.batch = nb;
     a.lda = (int32_t)mp; a.ldb = (int32_t)np; a.bsa = mp * mp; a.bsb = mp * np;
@@ -531,6 +540,9 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
     a.ktiles = w.kt_apply;
     a.epi.alpha = 1.0f; a.epi.scale_pow = first ? 1 : 0; a.epi.scale = scale;
     a.epi.out_hi = x_out; a.epi.ld_hi = (int32_t)np; a.epi.bs_hi = mp * np;
+    if (x_coef != 0.0f) {
+      a.epi.xadd = x_in; a.epi.ld_xadd = (int32_t)np; a.epi.bs_xadd = mp * np; a.epi.xadd_coef = x_coef;
+    }
     const bool upd = last && fu.n > 0;
     if (upd) {
       if (mc_status ws_ = wait_smax(smax_ready, s_max, s)) return ws_;
@@ -539,7 +551,8 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
         *gamma_once = nullptr;
       }
     }
-    // operands P and X; X' is written unless the update consumes it
+    // operands P and X (read once, also when the epilogue adds it); X' is
+    // written unless the update consumes it
     const double bytes = (2.0 * mm_ * mm_ + 2.0 * mm_ * nn_ + (upd ? 0.0 : 2.0 * mm_ * nn_)) * nb;
     return launch_gemm_planned(w.apply, GEMM_APPLY, false, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * nn_ * nb,
                                bytes + (upd ? fu_bytes : 0.0), upd ? &fu : nullptr);
@@ -547,21 +560,40 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
 
   int cur = 0, it0 = 0;   // X[cur] holds iterate X_it0
   if (gram_head(g, w, hp.ns_steps)) {
-    // The first two iterations in Gram space: with A0 = X0 X0^T and
-    // P0 = p(A0), X1 = P0 X0 gives X1 X1^T = P0 A0 P0, so A1 and P1 = p(A1)
-    // follow from m x m products alone and X2 = (P1 P0) X0 takes one
-    // n-sized product instead of three. The m x m scratch T lives in X[1],
-    // which X2 overwrites last.
-    uint16_t* T = X[1];
+    // The first kGramHead iterations in Gram space. With A0 = s0^2 X0 X0^T and
+    // P_j = p(A_j), X_{j+1} = P_j X_j gives A_{j+1} = P_j A_j P_j, so every
+    // A_j and P_j follows from m x m products alone and X_k = (P_{k-1} ..
+    // P_0) X0 takes one n-sized product. The accumulated product Q_j =
+    // P_j .. P_0 is about a^{j+1} I plus a smaller part (a the quintic's
+    // linear coefficient), so it is kept as R_j = Q_j - a^{j+1} I, whose bf16
+    // rounding is much finer than Q_j's: R_1 = P_1 P_0 - a^2 I, R_j = P_j
+    // R_{j-1} + a^j P_j - a^{j+1} I, and the apply adds a^k X0 back in fp32.
+    // m x m scratch: T0 and T1 in X[1] (n >= 2 m columns), which X_k
+    // overwrites last.
+    uint16_t* T0 = X[1];
+    uint16_t* T1 = X[1] + (size_t)nb * mp * mp;
+    const double a_ = hp.ns_a;
     mc_status st = gram(X[0], true);
-    if (!st) st = poly(Phi);                        // P0
-    if (!st) st = sym_product(Ahi, Phi, T, false);  // A0 P0
-    if (!st) st = sym_product(Phi, T, Ahi, true);   // A1 = P0 (A0 P0)
-    if (!st) st = poly(T);                          // P1
-    if (!st) st = sym_product(T, Phi, Ahi, false);  // Q = P1 P0
-    if (!st) st = apply(Ahi, nullptr, X[0], X[1], true, false);   // X2 = s0 Q X0
+    if (!st) st = poly(Phi);                          // P0
+    if (!st) st = sym_product(Ahi, Phi, T0, false);   // A0 P0
+    if (!st) st = sym_product(Phi, T0, Ahi, true);    // A1 = P0 (A0 P0)
+    if (!st) st = poly(T0);                           // P1
+    if (!st) st = sym_product(T0, Phi, T1, false, (float)(-a_ * a_));   // R1 = P1 P0 - a^2 I
+    // P_{j-1} in T0, R_{j-1} in r_buf, A_{j-1} in A_hi (+ fp32 copy); spare
+    // is free (P0's buffer once R1 is formed)
+    uint16_t* r_buf = T1;
+    uint16_t* spare = Phi;
+    for (int j = 2; j < kGramHead && !st; ++j) {
+      const double aj = std::pow(a_, j);
+      st = sym_product(Ahi, T0, spare, false);                // A_{j-1} P_{j-1}
+      if (!st) st = sym_product(T0, spare, Ahi, true);        // A_j
+      if (!st) st = poly(T0);                                 // P_j
+      if (!st) st = sym_product(T0, r_buf, spare, false, (float)(-aj * a_), T0, (float)aj);   // R_j
+      std::swap(r_buf, spare);
+    }
+    if (!st) st = apply(r_buf, nullptr, X[0], X[1], true, false, (float)std::pow(a_, kGramHead));   // X_k
     if (st) return st;
-    cur = 1; it0 = 2;
+    cur = 1; it0 = kGramHead;
   }
   for (int it = it0; it < hp.ns_steps; ++it) {
     mc_status st = gram(X[cur], it == 0);
@@ -643,8 +675,9 @@ double wave_cost(const Group& g, int nb, int cus, int ns_steps) {
     return rounds * gp.kt_per_split * share + 2.0;   // + launch and drain, about two k-stages
   };
   const double gram = launch(w.gram, true), sq = launch(w.poly, true), apply = launch(w.apply, false);
-  // the Gram-space head trades a Gram and an apply for three m x m products
-  if (gram_head(g, w, ns_steps)) return (ns_steps - 1) * (gram + apply) + (ns_steps + 3) * sq;
+  // each head iteration after the first trades a Gram and an apply for three m x m products
+  const int k = kGramHead;
+  if (gram_head(g, w, ns_steps)) return (ns_steps - k + 1) * (gram + apply) + (ns_steps + 3 * (k - 1)) * sq;
   return ns_steps * (gram + sq + apply);
 }
 

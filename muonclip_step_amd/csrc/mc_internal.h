@@ -61,6 +61,10 @@ struct GemmEpi {
   // so each 16-byte access of a wave covers 1 KB. frag_out: written (the
   // Gram); frag_in: read as the beta term instead of cin (the Poly).
   float* frag_out; const float* frag_in; int32_t frag_nb; int64_t bs_frag;
+  // unsplit apply only: out = bf16(bf16(v) + xadd_coef * scale * xadd[i][j]),
+  // xadd a bf16 matrix laid out like the output (the identity part of the
+  // Gram-space head's Q, added to R X0 at full precision)
+  const uint16_t* xadd; int32_t ld_xadd; int64_t bs_xadd; float xadd_coef;
 };
 
 struct GemmArgs {

@@ -124,6 +124,8 @@ enum : int {
   E_UPD = 512,    // last apply: the weight update with v as O, no store of v
   E_FOUT = 1024,  // also store v in fp32 fragment order (frag_out)
   E_FIN = 2048,   // v += beta * frag_in (fp32 fragment order) instead of cin
+  E_XADD = 4096,  // store pass adds xadd_coef * scale * xadd[i][j] to bf16 v (apply)
+  E_CIN1 = 8192,  // with E_CIN: cin_hi alone (v += beta * cin_hi[i][j])
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -515,7 +517,7 @@ ns_gemm_kernel(const GemmArgs p, const FusedUpd u) {
         for (int g = 0; g < 4; ++g) {
           const uint32_t o = t_cin + (uint32_t)(fj * 32 * ld_cin + fi * 32 + 8 * g);
           c_hi[g] = *(const uint2*)(cin_hi + o);
-          c_lo[g] = *(const uint2*)(cin_lo + o);
+          if (!(EPI & E_CIN1)) c_lo[g] = *(const uint2*)(cin_lo + o);
         }
       }
 #pragma unroll
@@ -528,10 +530,14 @@ ns_gemm_kernel(const GemmArgs p, const FusedUpd u) {
           v[q] = a[4 * g + q] * alpha;
           if (EPI & E_FIN) v[q] += beta * c_f[g][q];
           if (EPI & E_CIN) {
-            const uint32_t wh = q < 2 ? c_hi[g].x : c_hi[g].y, wl = q < 2 ? c_lo[g].x : c_lo[g].y;
+            const uint32_t wh = q < 2 ? c_hi[g].x : c_hi[g].y;
             const float ch = bf16_to_f32((uint16_t)((q & 1) ? wh >> 16 : wh));
-            const float cl = bf16_to_f32((uint16_t)((q & 1) ? wl >> 16 : wl));
-            v[q] += beta * (ch + cl);
+            if (EPI & E_CIN1) {
+              v[q] += beta * ch;
+            } else {
+              const uint32_t wl = q < 2 ? c_lo[g].x : c_lo[g].y;
+              v[q] += beta * (ch + bf16_to_f32((uint16_t)((q & 1) ? wl >> 16 : wl)));
+            }
           }
           if ((EPI & E_DIAG) && wi0 + ur + q == wj0 + uc) v[q] += diag;
         }
@@ -591,6 +597,49 @@ ns_gemm_kernel(const GemmArgs p, const FusedUpd u) {
       const uint4 o = *(const uint4*)(tw + jr * TP + ch * 16);
       const int gj = wj0 + jr, gi = wi0 + ch * 8;
       if (gj < p.N && gi < p.M) *(uint4*)(dst + (uint32_t)(gj * ld + gi)) = o;
+    }
+  };
+
+  // Store pass with a bf16 matrix added at the output's own positions:
+  // out = bf16(v + c s X[i][j]), v the bf16 value staged in T, X read in
+  // 16-byte vectors, each group's loads issued before its first store.
+  auto store_xadd = [&]() __attribute__((always_inline)) {
+    typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+    const uint16_t* xs = p.epi.xadd + (int64_t)b * p.epi.bs_xadd;
+    const int ldx = p.epi.ld_xadd;
+    const float cx = p.epi.xadd_coef * sc;
+    const int t = lane & 15, gr = lane >> 4;
+    const int sq = t >> 2, sa = t & 3;
+    constexpr int NIB = WTM / 16, NV = (WTN / 32) * NIB, CHK = NV < 8 ? NV : 8;
+#pragma unroll
+    for (int c0 = 0; c0 < NV; c0 += CHK) {
+      u16x8_t xv[CHK];
+#pragma unroll
+      for (int q = 0; q < CHK; ++q) {
+        const int jb = (c0 + q) / NIB, ib = (c0 + q) % NIB;
+        const int gi = wi0 + ib * 16 + t, gj = wj0 + jb * 32 + gr * 8;
+        if (gi < p.M && gj < p.N) xv[q] = *(const u16x8_t*)(xs + (int64_t)gi * ldx + gj);
+      }
+#pragma unroll
+      for (int q = 0; q < CHK; ++q) {
+        const int jb = (c0 + q) / NIB, ib = (c0 + q) % NIB;
+        const int i0 = ib * 16, j0 = jb * 32 + gr * 8;
+        typedef short v4i16 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+        const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(tw + (j0 + sq) * TP + (i0 + 4 * sa) * 2));
+        const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(tw + (j0 + 4 + sq) * TP + (i0 + 4 * sa) * 2));
+        const int gi = wi0 + i0 + t, gj = wj0 + j0;
+        if (gi < p.M && gj < p.N) {
+          const u16x8_t o = {(uint16_t)x0[0], (uint16_t)x0[1], (uint16_t)x0[2], (uint16_t)x0[3],
+                             (uint16_t)x1[0], (uint16_t)x1[1], (uint16_t)x1[2], (uint16_t)x1[3]};
+          u16x8_t r;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) r[e] = f32_to_bf16(fmaf(cx, bf16_to_f32(xv[q][e]), bf16_to_f32(o[e])));
+          *(u16x8_t*)(ohi + (uint32_t)(gi * ld_hi + gj)) = r;
+        }
+      }
     }
   };
 
@@ -678,6 +727,11 @@ ns_gemm_kernel(const GemmArgs p, const FusedUpd u) {
     store_update();
     return;
   }
+  if (EPI & E_XADD) {
+    static_assert(!(EPI & E_XADD) || !(EPI & (E_SYM | E_LO)), "xadd: non-symmetric products, hi only");
+    store_xadd();
+    return;
+  }
   if (EPI & E_HI) store_direct(ohi, ld_hi);
   if ((EPI & E_HI) && mirror) store_trans(ohi, ld_hi);
   if (EPI & E_LO) {
@@ -756,7 +810,12 @@ hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const G
     return ptr && ((ld & 7) || (bs & 7) || ((uintptr_t)ptr & 15));
   };
   if ((a.M & 31) || (a.N & 31) || bad(e.cin_hi, e.ld_cin, e.bs_cin) || bad(e.cin_lo, e.ld_cin, e.bs_cin) ||
-      bad(e.out_hi, e.ld_hi, e.bs_hi) || bad(e.out_lo, e.ld_lo, e.bs_lo))
+      bad(e.out_hi, e.ld_hi, e.bs_hi) || bad(e.out_lo, e.ld_lo, e.bs_lo) || bad(e.xadd, e.ld_xadd, e.bs_xadd))
+    return hipErrorInvalidValue;
+  // the added matrix rides on an unsplit, unfused apply that stores only hi
+  if (e.xadd && (kind != GEMM_APPLY || a.splits > 1 || fused || !e.out_hi || e.out_lo)) return hipErrorInvalidValue;
+  // a Gram-kind C input is hi only, on an unsplit product without operand pairs or fragment copy
+  if (kind == GEMM_GRAM && e.cin_hi && (e.cin_lo || a.splits > 1 || split_pair || e.frag_out || e.out_lo))
     return hipErrorInvalidValue;
   const bool frag = (kind == GEMM_GRAM && e.frag_out) || (kind == GEMM_POLY && e.frag_in);
   if (frag && (a.splits > 1 || split_pair || ((uintptr_t)(kind == GEMM_GRAM ? (const void*)e.frag_out : e.frag_in) & 15) ||
@@ -770,13 +829,19 @@ hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const G
     if (split_pair) launch_epi<E_SYM | E_HI | E_LO>(tile, a, total, s, u);
     else if (frag) launch_epi<E_SYM | E_HI | E_FOUT>(tile, a, total, s, u);
     else if (e.out_lo) launch_epi<E_SYM | E_HI | E_LO | E_LOMIR>(tile, a, total, s, u);
-    else launch_epi<E_SYM | E_HI>(tile, a, total, s, u);   // bf16 product of two symmetric matrices
+    // bf16 products of two symmetric matrices (Gram-space head), plus diag on
+    // the diagonal and beta times a third symmetric matrix
+    else if (e.cin_hi) launch_epi<E_SYM | E_CIN | E_CIN1 | E_DIAG | E_HI>(tile, a, total, s, u);
+    else if (e.diag != 0.0f) launch_epi<E_SYM | E_DIAG | E_HI>(tile, a, total, s, u);
+    else launch_epi<E_SYM | E_HI>(tile, a, total, s, u);
   } else if (kind == GEMM_POLY) {
     if (split_pair) launch_epi<E_SYM | E_CIN | E_DIAG | E_HI | E_LO>(tile, a, total, s, u);
     else if (frag) launch_epi<E_SYM | E_FIN | E_DIAG | E_HI>(tile, a, total, s, u);
     else launch_epi<E_SYM | E_CIN | E_DIAG | E_HI>(tile, a, total, s, u);
   } else if (fused) {
     launch_epi<E_UPD, 1>(tile, a, total, s, u);   // last apply with the weight update
+  } else if (e.xadd) {
+    launch_epi<E_HI | E_XADD, 1>(tile, a, total, s, u);   // apply ending the Gram-space head
   } else {
     launch_epi<E_HI, 1>(tile, a, total, s, u);   // apply: B = X stored [k][n]
   }

@@ -171,14 +171,15 @@ def test_group_on_128_tiles_against_oracle():
         check_matrix(st, hp)
 
 
-@pytest.mark.parametrize("ns_steps,f32_weight", [(5, False), (5, True), (3, False), (3, True), (2, False)])
+@pytest.mark.parametrize("ns_steps,f32_weight", [(5, False), (5, True), (4, False), (4, True), (3, False)])
 def test_gram_space_head_against_oracle(ns_steps, f32_weight):
     """Six matrices of one group with n >= 2 m (m = 1100, n = 2300: wide and
-    tall, padded rows, ragged against the 128 tiles) whose first two
-    Newton-Schulz iterations run in Gram space (X2 = P1 P0 X0 with
-    P1 = p(P0 A0 P0)); ns_steps = 2 leaves no iteration after the head and
-    takes the plain path. An f32 weight turns off the fused update, so the
-    separate update reads O from whichever X buffer holds it."""
+    tall, padded rows, ragged against the 128 tiles) whose first three
+    Newton-Schulz iterations run in Gram space (A_{j+1} = P_j A_j P_j, the
+    accumulated product kept as P_j .. P_0 - a^{j+1} I, then one apply to X0);
+    ns_steps = 4 leaves one X-space iteration after the head, ns_steps = 3
+    none, so it takes the plain path. An f32 weight turns off the fused
+    update, so the separate update reads O from whichever X buffer holds it."""
     print("gram head", ns_steps, f32_weight, flush=True)
     states = []
     for k in range(6):
