@@ -770,16 +770,19 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const GemmArgs p) {
   }
 }
 
-// A 256x256 launch of at most one workgroup per CU runs eight waves (2 x 4,
-// two per SIMD, which hide each other's LDS waits and barriers when every CU
-// holds a single tile); larger launches keep four waves, whose 128x128
-// sub-tiles need fewer fragment reads per MFMA (measured: 2.4 % faster on the
-// 4 x 2048^2 chains, 1.2 % slower on the 1155 expert matrices).
+// A 256x256 launch runs eight waves (2 x 4, two per SIMD, which hide each
+// other's LDS waits, barriers and epilogue) when it has at most one workgroup
+// per CU, or when it is a symmetric m x m product (K = m: few k-stages per
+// tile, so the epilogue weighs more); other launches keep four waves, whose
+// 128x128 sub-tiles need fewer fragment reads per MFMA (measured: eight waves
+// 2.4 % faster on the 4 x 2048^2 chains, 1.2 % slower over all launches of
+// the 1155 expert matrices, 7 % faster on their Poly launches).
 template <int EPI, int NNB = 0>
 static void launch_epi(GemmTile tile, const GemmArgs& a, int total, hipStream_t s, const FusedUpd& u) {
+  const bool square = (EPI & E_SYM) && a.ktiles * kGemmBK <= a.M;
   switch (tile) {
     case TILE_256:
-      if (total <= device_cus()) ns_gemm_kernel<256, 256, 2, EPI, NNB, 8><<<total, 512, 0, s>>>(a, u);
+      if (total <= device_cus() || square) ns_gemm_kernel<256, 256, 2, EPI, NNB, 8><<<total, 512, 0, s>>>(a, u);
       else ns_gemm_kernel<256, 256, 2, EPI, NNB, 4><<<total, 256, 0, s>>>(a, u);
       break;
     case TILE_128: ns_gemm_kernel<128, 128, 2, EPI, NNB><<<total, 256, 0, s>>>(a, u); break;
