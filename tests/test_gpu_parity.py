@@ -171,16 +171,20 @@ def test_group_on_128_tiles_against_oracle():
         check_matrix(st, hp)
 
 
-@pytest.mark.parametrize("ns_steps,f32_weight", [(5, False), (5, True), (4, False), (4, True), (3, False)])
-def test_gram_space_head_against_oracle(ns_steps, f32_weight):
+@pytest.mark.parametrize("ns_steps,f32_weight,coef", [(5, False, None), (5, True, None), (4, False, None),
+                                                     (4, True, None), (3, False, None), (7, False, None),
+                                                     (5, False, (2.0, -1.5, 0.5))])
+def test_gram_space_head_against_oracle(ns_steps, f32_weight, coef):
     """Six matrices of one group with n >= 2 m (m = 1100, n = 2300: wide and
     tall, padded rows, ragged against the 128 tiles) whose first three
     Newton-Schulz iterations run in Gram space (A_{j+1} = P_j A_j P_j, the
     accumulated product kept as P_j .. P_0 - a^{j+1} I, then one apply to X0);
     ns_steps = 4 leaves one X-space iteration after the head, ns_steps = 3
-    none, so it takes the plain path. An f32 weight turns off the fused
-    update, so the separate update reads O from whichever X buffer holds it."""
-    print("gram head", ns_steps, f32_weight, flush=True)
+    none, so it takes the plain path; ns_steps = 7 four. An f32 weight turns
+    off the fused update, so the separate update reads O from whichever X
+    buffer holds it. coef: other quintic coefficients (a, b, c), whose a sets
+    the shifts a^j of the accumulated product."""
+    print("gram head", ns_steps, f32_weight, coef, flush=True)
     states = []
     for k in range(6):
         shape = (1100, 2300) if k % 2 == 0 else (2300, 1100)
@@ -192,7 +196,8 @@ def test_gram_space_head_against_oracle(ns_steps, f32_weight):
         g = wl.quantize_f32(wl.normal(seed, 1, shape, 1.0))
         m = wl.quantize_f32(wl.normal(seed, 2, shape, 1.0))
         states.append(State(spec, w, g, m, ld_pad=8 * (k % 3)))
-    hp = mc.hparams(lr=0.01, ns_steps=ns_steps)
+    kw = {} if coef is None else dict(ns_a=coef[0], ns_b=coef[1], ns_c=coef[2])
+    hp = mc.hparams(lr=0.01, ns_steps=ns_steps, **kw)
     mc.muonclip_step([st.desc() for st in states], hp)
     torch.cuda.synchronize()
     for st in states:
