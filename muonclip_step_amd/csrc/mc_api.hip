@@ -569,27 +569,33 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
     // rounding is much finer than Q_j's: R_1 = P_1 P_0 - a^2 I, R_j = P_j
     // R_{j-1} + a^j P_j - a^{j+1} I, and the apply adds a^k X0 back in fp32.
     // m x m scratch: T0 and T1 in X[1] (n >= 2 m columns), which X_k
-    // overwrites last.
+    // overwrites last. The last R goes to A_hi (its A has been read by the
+    // last Poly), so the R the apply reads is never in X[1]; earlier R_j
+    // alternate between T1 and the buffer P0 leaves.
+    static_assert(kGramHead >= 2, "a head of one is an ordinary iteration");
     uint16_t* T0 = X[1];
     uint16_t* T1 = X[1] + (size_t)nb * mp * mp;
     const double a_ = hp.ns_a;
+    uint16_t* r_buf = kGramHead == 2 ? Ahi : T1;
     mc_status st = gram(X[0], true);
     if (!st) st = poly(Phi);                          // P0
     if (!st) st = sym_product(Ahi, Phi, T0, false);   // A0 P0
     if (!st) st = sym_product(Phi, T0, Ahi, true);    // A1 = P0 (A0 P0)
     if (!st) st = poly(T0);                           // P1
-    if (!st) st = sym_product(T0, Phi, T1, false, (float)(-a_ * a_));   // R1 = P1 P0 - a^2 I
+    if (!st) st = sym_product(T0, Phi, r_buf, false, (float)(-a_ * a_));   // R1 = P1 P0 - a^2 I
     // P_{j-1} in T0, R_{j-1} in r_buf, A_{j-1} in A_hi (+ fp32 copy); spare
     // is free (P0's buffer once R1 is formed)
-    uint16_t* r_buf = T1;
     uint16_t* spare = Phi;
     for (int j = 2; j < kGramHead && !st; ++j) {
       const double aj = std::pow(a_, j);
+      const bool last = j + 1 == kGramHead;
       st = sym_product(Ahi, T0, spare, false);                // A_{j-1} P_{j-1}
       if (!st) st = sym_product(T0, spare, Ahi, true);        // A_j
       if (!st) st = poly(T0);                                 // P_j
-      if (!st) st = sym_product(T0, r_buf, spare, false, (float)(-aj * a_), T0, (float)aj);   // R_j
-      std::swap(r_buf, spare);
+      uint16_t* out = last ? Ahi : spare;
+      if (!st) st = sym_product(T0, r_buf, out, false, (float)(-aj * a_), T0, (float)aj);   // R_j
+      if (last) r_buf = out;
+      else std::swap(r_buf, spare);
     }
     if (!st) st = apply(r_buf, nullptr, X[0], X[1], true, false, (float)std::pow(a_, kGramHead));   // X_k
     if (st) return st;
