@@ -154,7 +154,11 @@ size_t mc_workspace_min_size(const mc_matrix *mats /* host, n */, int32_t n, con
  * Matrices are processed in groups of equal (min, max) shape; within a group
  * the momentum kernel, five Newton-Schulz iterations (bf16 MFMA, fp32
  * accumulation) and the fused update/decay/clip kernel run per wave of
- * matrices that fit the workspace. Waves are independent chains: with at
+ * matrices that fit the workspace. For groups with max >= 2 min the first
+ * three iterations are formed in the min x min Gram space (A_{j+1} = P_j A_j
+ * P_j, then one product with X0), which gives the same iterate in exact
+ * arithmetic with fewer max-sized products; results therefore match the
+ * iteration to bf16 rounding, not bit for bit. Waves are independent chains: with at
  * least two shape groups and a workspace that holds a wave of each twice
  * over, the chains are split between `stream` and the library's auxiliary
  * stream, which is forked after the work already on `stream` and joined back
