@@ -180,10 +180,13 @@ def test_gram_space_head_against_oracle(ns_steps, f32_weight, coef):
     Newton-Schulz iterations run in Gram space (A_{j+1} = P_j A_j P_j, the
     accumulated product kept as P_j .. P_0 - a^{j+1} I, then one apply to X0);
     ns_steps = 4 leaves one X-space iteration after the head, ns_steps = 3
-    none, so it takes the plain path; ns_steps = 7 four. An f32 weight turns
-    off the fused update, so the separate update reads O from whichever X
-    buffer holds it. coef: other quintic coefficients (a, b, c), whose a sets
-    the shifts a^j of the accumulated product."""
+    none, so it takes the plain path; ns_steps = 7 four. The oracle check
+    requests O copies, so the update runs as its own kernel and reads O from
+    whichever X buffer holds it; a second run without O copies (the update in
+    the last apply's epilogue, unless an f32 weight keeps the wave on the
+    update kernel) must give the same weights bit for bit. coef: other
+    quintic coefficients (a, b, c), whose a sets the shifts a^j of the
+    accumulated product."""
     print("gram head", ns_steps, f32_weight, coef, flush=True)
     states = []
     for k in range(6):
@@ -202,6 +205,40 @@ def test_gram_space_head_against_oracle(ns_steps, f32_weight, coef):
     torch.cuda.synchronize()
     for st in states:
         check_matrix(st, hp)
+    _same_weights_without_o(states, hp)
+
+
+def _same_weights_without_o(states, hp):
+    """Rerun the step from the drawn inputs without O copies and require the
+    weights of the run just checked, bit for bit."""
+    want = [s.w.cpu().clone() for s in states]
+    _fresh(states)
+    mc.muonclip_step([s.desc(with_o=False) for s in states], hp)
+    torch.cuda.synchronize()
+    for a, s in zip(want, states):
+        assert torch.equal(a, s.w.cpu())
+
+
+def test_gram_space_head_eight_wave_apply_against_oracle():
+    """Four 1024 x 2304 matrices (two wide, two tall): the head's m x m
+    products run on 128 tiles and its final apply on 144 tiles of 256, one
+    per CU, so that apply takes the eight-wave kernel. Against the oracle
+    with O copies, then bit for bit without them (fused update)."""
+    states = []
+    for k in range(4):
+        shape = (1024, 2304) if k % 2 == 0 else (2304, 1024)
+        spec = wl.MatrixSpec("h8", *shape, "bf16", init_std=0.02, grad_std=1e-3, mom_std=1e-3)
+        seed = 3200 + k
+        w = wl.quantize_bf16(wl.normal(seed, 0, shape, 0.02))
+        g = wl.quantize_f32(wl.normal(seed, 1, shape, 1e-3))
+        m = wl.quantize_f32(wl.normal(seed, 2, shape, 1e-3))
+        states.append(State(spec, w, g, m))
+    hp = mc.hparams(lr=0.01)
+    mc.muonclip_step([st.desc() for st in states], hp)
+    torch.cuda.synchronize()
+    for st in states:
+        check_matrix(st, hp)
+    _same_weights_without_o(states, hp)
 
 
 def test_zero_gradient_and_momentum_decay_only():
