@@ -6,10 +6,10 @@
 // A A read their B operand as rows of the same row-major matrix ("NT" form:
 // B[k][j] = X[j][k]); the apply P X reads B = X in its own row-major [k][n]
 // layout and forms the MFMA B fragments with gfx950's transposing LDS read,
-// so no transposed copy of X is ever written. One kernel serves all three,
-// batched over the matrices of one shape group (grid = tiles x splits x
-// batch, mapped XCD-major so the tiles of one matrix share an XCD's L2). The
-// symmetric products (X X^T, A A, and the products of two commuting
+// so no transposed copy of X is ever written. One kernel serves all of them
+// and the Gram-space head's m x m products, batched over the matrices of one
+// shape group (grid = tiles x splits x batch, mapped XCD-major so the tiles
+// of one matrix share an XCD's L2). The symmetric products (X X^T, A A, and the products of two commuting
 // symmetric m x m matrices that run the first iterations in Gram space)
 // compute only the tiles on and above the diagonal and store each
 // off-diagonal tile a second time, transposed.
