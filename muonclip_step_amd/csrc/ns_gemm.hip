@@ -9,10 +9,10 @@
 // so no transposed copy of X is ever written. One kernel serves all of them
 // and the Gram-space head's m x m products, batched over the matrices of one
 // shape group (grid = tiles x splits x batch, mapped XCD-major so the tiles
-// of one matrix share an XCD's L2). The symmetric products (X X^T, A A, and the products of two commuting
-// symmetric m x m matrices that run the first iterations in Gram space)
-// compute only the tiles on and above the diagonal and store each
-// off-diagonal tile a second time, transposed.
+// of one matrix share an XCD's L2). The symmetric products (X X^T, A A,
+// and the products of two commuting symmetric m x m matrices that run the
+// first iterations in Gram space) compute only the tiles on and above the
+// diagonal and store each off-diagonal tile a second time, transposed.
 //
 // gfx950 design: v_mfma_f32_32x32x16_bf16 with fp32 accumulation; a block of
 // 2x2 waves (or 2x4) owns a BMxBN tile, each wave a (BM/2)x(BN/2) (or
