@@ -16,9 +16,9 @@
 //
 // gfx950 design: v_mfma_f32_32x32x16_bf16 with fp32 accumulation; a block of
 // 2x2 waves (or 2x4) owns a BMxBN tile, each wave a (BM/2)x(BN/2) (or
-// (BM/2)x(BN/4)) sub-tile. K advances
-// in 64-wide stages held in a two-slot LDS ring that direct-to-LDS loads
-// (global_load_lds_dwordx4) fill, so no register staging is needed. One
+// (BM/2)x(BN/4)) sub-tile. K advances in 64-wide stages held in a two-slot
+// LDS ring that direct-to-LDS loads (global_load_lds_dwordx4) fill, so no
+// register staging is needed. One
 // barrier per stage retires a slot; the loads of the stage after next go out
 // in two halves, under the last k-step of one stage and the first k-step of
 // the next, each load placed between two MFMAs, and every memory instruction
