@@ -18,14 +18,14 @@
 // 2x2 waves (or 2x4) owns a BMxBN tile, each wave a (BM/2)x(BN/2) (or
 // (BM/2)x(BN/4)) sub-tile. K advances in 64-wide stages held in a two-slot
 // LDS ring that direct-to-LDS loads (global_load_lds_dwordx4) fill, so no
-// register staging is needed. One
-// barrier per stage retires a slot; the loads of the stage after next go out
-// in two halves, under the last k-step of one stage and the first k-step of
-// the next, each load placed between two MFMAs, and every memory instruction
-// of the steady-state loop is unconditional (the last stage is peeled). The
-// MFMA fragments of each 16-k step are read from LDS while the previous
-// step's MFMAs run. The epilogue is specialised at compile time per use and
-// stages each wave's results through LDS for 16-byte stores.
+// register staging is needed. One barrier per stage retires a slot; the
+// loads of the stage after next go out in two halves, under the last k-step
+// of one stage and the first k-step of the next, each load placed between two
+// MFMAs, and every memory instruction of the steady-state loop is
+// unconditional (the last stage is peeled). The MFMA fragments of each 16-k
+// step are read from LDS while the previous step's MFMAs run. The epilogue is
+// specialised at compile time per use and stages each wave's results through
+// LDS for 16-byte stores.
 #include "mc_internal.h"
 
 namespace mc {
