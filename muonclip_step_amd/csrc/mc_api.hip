@@ -314,14 +314,15 @@ WavePlan plan_wave(const Group& g, int nb, int cus) {
 // Whether a wave runs its first kGramHead Newton-Schulz iterations in Gram
 // space (each iteration after the first trades a Gram and an apply, both
 // n-sized, for three m x m products): for groups with n >= 2 m, where the
-// n-sized products saved outweigh the m x m products added, with unsplit
-// symmetric products whose A is handed over in fragment order and an unsplit
-// apply (whose epilogue adds the identity part of the accumulated product).
-// At least one iteration follows it, so the fused update stays on an
-// ordinary apply.
+// n-sized products saved outweigh the m x m products added, without hi/lo
+// operand pairs (A reaches the Poly as the fp32 fragment copy or, when the
+// symmetric products are split or tiled differently, as the bf16 pair
+// A_hi + A_lo), and with an unsplit apply (whose epilogue adds the identity
+// part of the accumulated product). At least one iteration follows it, so
+// the fused update stays on an ordinary apply.
 constexpr int kGramHead = 3;   // at least 2
 bool gram_head(const Group& g, const WavePlan& w, int ns_steps) {
-  return w.frag && w.apply.splits == 1 && ns_steps > kGramHead && g.np >= 2 * g.mp;
+  return !g.split && w.apply.splits == 1 && ns_steps > kGramHead && g.np >= 2 * g.mp;
 }
 
 // Dense-GEMM flops of one wave's Newton-Schulz products (2 m n k each,
@@ -512,7 +513,7 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
   // head): R is read by rows, which are its columns; C is symmetric up to
   // rounding (L and R are polynomials in one matrix, so they commute) and only
   // its upper tiles are computed, then mirrored. to_a: store C as A_hi plus
-  // the fp32 fragment copy the next Poly reads.
+  // what the next Poly reads besides it (the fp32 fragment copy, or A_lo).
   auto sym_product = [&](const uint16_t* l, const uint16_t* r, uint16_t* out, bool to_a, float diag = 0.0f,
                          const uint16_t* c = nullptr, float beta = 0.0f) -> mc_status {
     GemmArgs a{};
@@ -522,7 +523,11 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
     a.epi.alpha = 1.0f; a.epi.diag = diag;
     if (c) { a.epi.cin_hi = c; a.epi.beta = beta; a.epi.ld_cin = (int32_t)mp; a.epi.bs_cin = mp * mp; }
     a.epi.out_hi = out; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
-    if (to_a) { a.epi.frag_out = (float*)Alo; a.epi.frag_nb = (int32_t)(mp / 32); a.epi.bs_frag = mp * mp; }
+    if (to_a && w.frag) {
+      a.epi.frag_out = (float*)Alo; a.epi.frag_nb = (int32_t)(mp / 32); a.epi.bs_frag = mp * mp;
+    } else if (to_a) {
+      a.epi.out_lo = Alo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp;
+    }
     return launch_gemm_planned(w.poly, GEMM_GRAM, false, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * mm_ * nb,
                                (c ? 8.0 : 6.0) * mm_ * mm_ * nb);
   };

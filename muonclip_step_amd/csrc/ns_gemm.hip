@@ -53,7 +53,8 @@ __device__ inline int xcd_remap(int L, int total) {
 }
 
 // The epilogue of eight consecutive columns j0 .. j0+7 of row i (the split-K
-// finish): v = alpha scale acc + beta (cin_hi + cin_lo) + diag (i == j),
+// finish): v = alpha scale acc + beta (cin_hi + cin_lo) + diag (i == j)
+// (cin_lo optional),
 // bf16 v to out_hi and bf16 (v - hi) to out_lo, in 16-byte accesses (row
 // starts and strides are multiples of 8 elements).
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
@@ -64,7 +65,8 @@ __device__ __attribute__((always_inline)) inline void epilogue_store8(const Gemm
   for (int k = 0; k < 8; ++k) v[k] = e.alpha * sc * acc[k];
   if (e.cin_hi) {
     const int64_t o = (int64_t)b * e.bs_cin + (int64_t)i * e.ld_cin + j0;
-    const u16x8_t h = *(const u16x8_t*)(e.cin_hi + o), l = *(const u16x8_t*)(e.cin_lo + o);
+    const u16x8_t h = *(const u16x8_t*)(e.cin_hi + o);
+    const u16x8_t l = e.cin_lo ? *(const u16x8_t*)(e.cin_lo + o) : u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] += e.beta * (bf16_to_f32(h[k]) + bf16_to_f32(l[k]));
   }
@@ -817,8 +819,8 @@ hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const G
     return hipErrorInvalidValue;
   // the added matrix rides on an unsplit, unfused apply that stores only hi
   if (e.xadd && (kind != GEMM_APPLY || a.splits > 1 || fused || !e.out_hi || e.out_lo)) return hipErrorInvalidValue;
-  // a Gram-kind C input is hi only, on an unsplit product without operand pairs or fragment copy
-  if (kind == GEMM_GRAM && e.cin_hi && (e.cin_lo || a.splits > 1 || split_pair || e.frag_out || e.out_lo))
+  // a Gram-kind C input is hi only, on a product without operand pairs or fragment copy
+  if (kind == GEMM_GRAM && e.cin_hi && (e.cin_lo || split_pair || e.frag_out || e.out_lo))
     return hipErrorInvalidValue;
   const bool frag = (kind == GEMM_GRAM && e.frag_out) || (kind == GEMM_POLY && e.frag_in);
   if (frag && (a.splits > 1 || split_pair || ((uintptr_t)(kind == GEMM_GRAM ? (const void*)e.frag_out : e.frag_in) & 15) ||

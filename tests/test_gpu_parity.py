@@ -241,6 +241,30 @@ def test_gram_space_head_eight_wave_apply_against_oracle():
     _same_weights_without_o(states, hp)
 
 
+@pytest.mark.parametrize("shapes", [[(1024, 4096)], [(4096, 1024), (1024, 4096)]])
+def test_gram_space_head_split_k_against_oracle(shapes):
+    """One or two 1024 x 4096 matrices: too few tiles to fill the chip, so the
+    symmetric products run split-K and A reaches the Poly as the bf16 pair
+    A_hi + A_lo from the split-K finish (which also adds the head's diagonal
+    shifts and a^j P_j term), while the applies run unsplit and the head is
+    taken. Against the oracle with O copies, then bit for bit without."""
+    print("gram head split-K", shapes, flush=True)
+    states = []
+    for k, shape in enumerate(shapes):
+        spec = wl.MatrixSpec("hs", *shape, "bf16", init_std=0.02, grad_std=1e-3, mom_std=1e-3)
+        seed = 3300 + k
+        w = wl.quantize_bf16(wl.normal(seed, 0, shape, 0.02))
+        g = wl.quantize_f32(wl.normal(seed, 1, shape, 1e-3))
+        m = wl.quantize_f32(wl.normal(seed, 2, shape, 1e-3))
+        states.append(State(spec, w, g, m, ld_pad=8 * k))
+    hp = mc.hparams(lr=0.01)
+    mc.muonclip_step([st.desc() for st in states], hp)
+    torch.cuda.synchronize()
+    for st in states:
+        check_matrix(st, hp)
+    _same_weights_without_o(states, hp)
+
+
 @pytest.mark.parametrize("shape,count", [((96, 160), 1), ((1024, 2304), 4)])
 def test_zero_gradient_and_momentum_decay_only(shape, count):
     """G = M = 0: O is exactly zero and W only decays. The 1024 x 2304 group
