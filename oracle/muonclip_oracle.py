@@ -29,7 +29,7 @@ Sources, by page title and section:
               transpose when rows > cols, 5 steps, (a,b,c) = (3.4445, -4.7750, 2.0315))
               and "Analysis" (2(2nm^2+m^3) FLOPs per step; Nesterov-style momentum).
 
-Readings where the pages are silent or garbled (each is listed in the design doc):
+Readings where the pages are silent or garbled:
   * Algorithm 1's body is absent on every page; the step is assembled from the
     Muon update paragraph, the Moonlight update rule and the QK-Clip equations.
   * The sign of b: the Moonlight notes print +4.7750, the newtonschulz5 listing
