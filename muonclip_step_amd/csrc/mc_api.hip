@@ -399,12 +399,12 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
   float* scale = (float*)(ws + w.off_scale);
 
   // 1. momentum + norm partials + bf16 X0 = M (wide) or M^T (tall), [mp][np]
-  for (int b0 = 0; b0 < nb; b0 += kMaxBatchMats) {
+  for (int b0 = 0; b0 < nb; b0 += kMaxMomMats) {
     MomArgs a{};
     a.mu = hp.mu; a.nesterov = hp.nesterov;
     int blocks = 0;
     double bytes = 0;
-    for (int j = 0; j < kMaxBatchMats && b0 + j < nb; ++j) {
+    for (int j = 0; j < kMaxMomMats && b0 + j < nb; ++j) {
       const int slot = b0 + j;
       const mc_matrix& m = mats[ids[slot]];
       const bool wide = m.rows <= m.cols;
