@@ -9,7 +9,8 @@
 // width is 128.
 //
 // Layout of the work. A block owns 256 query rows of one (sample, head) in
-// eight waves of 32 rows (two waves per SIMD). Each wave keeps its rows in
+// eight waves of 32 rows (two waves per SIMD; the logit pass: two blocks
+// per CU, of eight such waves or of four waves of 64 rows). Each wave keeps its rows in
 // registers as an MFMA B-fragment for the whole kernel and walks the key axis
 // in tiles of 64 keys, which pass through a double-buffered LDS ring (K rows
 // XOR-swizzled
@@ -51,6 +52,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 #define FA_WAIT_DMA() __builtin_amdgcn_s_waitcnt(0x70 | 0xF00)
 
 constexpr int kBQ = 256, kBKV = 64, kDV = 128;
+constexpr int kWideMinT = 16384;   // MLA logit pass: 64-row waves from this sequence length on
 
 // V rows (256 bytes): a transposing read's 16-lane group covers four
 // consecutive rows at the same columns; chunk ^ 4 (r & 3) puts them on
@@ -104,6 +106,10 @@ __device__ __forceinline__ void mfma_s(f32x16_t& acc, const u32x4_t& a, const bf
 __device__ __forceinline__ void s_wait_logits(f32x16_t& a) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a));
 }
+// the same after two fragments' chains (the second one's MFMA issues last)
+__device__ __forceinline__ void s_wait_logits(f32x16_t& a, f32x16_t& b) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b));
+}
 
 // max of three numbers ignoring quiet NaNs (IEEE maxNum, as fmaxf), in one
 // v_max3_f32 and without the quieting copies the compiler puts before fmaxf
@@ -125,14 +131,20 @@ __device__ __forceinline__ float wave_max(float x) {
 // per SIMD, enough for the fragment traffic). The whole state fits 256
 // VGPRs: every MFMA writes VGPRs and the rescale is plain VALU arithmetic.
 // OUT = false: the logits and S_max only (no values, softmax or output),
-// which serves max_logits_per_head for the MLA head shape.
-template <int DK, int DS, bool SMAX, bool OUT = true>
-__global__ void __launch_bounds__(512, OUT ? 1 : 2) __attribute__((amdgpu_waves_per_eu(OUT ? 2 : 4, OUT ? 2 : 4)))
+// which serves max_logits_per_head for head width 128 and the MLA head
+// shape, with two blocks per CU: eight waves of 32 rows (at most 128
+// registers, four waves per SIMD) or, WIDE, four waves of 64 query rows (two
+// fragments, so each K fragment read from LDS feeds two MFMAs and a wave has
+// two independent accumulation chains; two waves per SIMD).
+template <int DK, int DS, bool SMAX, bool OUT = true, bool WIDE = false>
+__global__ void __launch_bounds__(WIDE ? 256 : 512, OUT ? 1 : 2)
+    __attribute__((amdgpu_waves_per_eu(OUT || WIDE ? 2 : 4, OUT || WIDE ? 2 : 4)))
 attn_fwd_kernel(const AttnArgs a) {
   static_assert(OUT || SMAX, "a pass with neither output nor S_max");
+  static_assert(!(OUT && WIDE), "the output pass runs 32-row waves");
   static_assert(DK == 128 && (DS == 0 || DS == 64), "head widths");
-  constexpr int NF = 1;                      // query fragments per wave
-  constexpr int NW = 8, WR = 32;             // waves per block, query rows per wave
+  constexpr int NF = WIDE ? 2 : 1;            // query fragments per wave
+  constexpr int NW = WIDE ? 4 : 8, WR = 32 * NF;   // waves per block, query rows per wave
   // MLA (192-wide queries): to fit 256 registers a half's K fragments go
   // through a ring of KSL = KS / 2 slots (the second half of the reads is
   // issued under the first half's MFMAs) and the two value k-steps share one
@@ -141,7 +153,7 @@ attn_fwd_kernel(const AttnArgs a) {
   constexpr int D = DK + DS, KS = D / 16;
   constexpr int KSL = kLean ? KS / 2 : KS, NVB = kLean ? 1 : 2;   // K slots, value buffers
   // one LDS stage: K content rows [64][256 B], rotary rows [64][128 B], V rows [64][256 B]
-  // (the logit pass keeps no values: two blocks share a CU, four waves per SIMD)
+  // (the logit pass keeps no values: two blocks share a CU)
   constexpr int KC_BYTES = kBKV * 256, KR_BYTES = kBKV * DS * 2, VT_BYTES = OUT ? kBKV * kDV * 2 : 0;
   constexpr int STAGE = KC_BYTES + KR_BYTES + VT_BYTES;
   // LDS ring stages: each tile's loads go out while the previous tile is
@@ -165,7 +177,7 @@ attn_fwd_kernel(const AttnArgs a) {
   const char* KR = DS > 0 ? (const char*)((const uint16_t*)a.ks + (int64_t)b * a.kss_b) : nullptr;
   const char* V = (const char*)((const uint16_t*)a.v + (int64_t)b * a.vs_b + (int64_t)h * a.vs_h);
 
-  // the wave's 64 query rows as B fragments: lane l holds query l % 32 of
+  // the wave's WR query rows as B fragments: lane l holds query l % 32 of
   // fragment f, dimensions 16 s + 8 (l / 32) .. +7. Rows past T re-read row
   // T - 1: they see exactly row T - 1's keys, so they change no maximum, and
   // their outputs are not stored.
@@ -358,7 +370,8 @@ attn_fwd_kernel(const AttnArgs a) {
         }
         if constexpr (s + KSL < KS) read_k1(g_, std::integral_constant<int, s + KSL>{});
       });
-      s_wait_logits(sacc[0]);
+      if constexpr (NF == 2) s_wait_logits(sacc[0], sacc[1]);
+      else s_wait_logits(sacc[0]);
       if constexpr (OUT) read_v(g_, std::integral_constant<int, 0>{});
       if (MASK) {
 #pragma unroll
@@ -550,8 +563,12 @@ hipError_t launch_attention_smax_only(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.T <= 0 || a.H <= 0) return hipSuccess;
   if (a.d_k != 128 || (a.d_s != 64 && a.d_s != 0) || !a.smax) return hipErrorInvalidValue;
   const int grid = (a.T + kBQ - 1) / kBQ * a.H * a.B;
-  if (a.d_s == 64) attn_fwd_kernel<128, 64, true, false><<<grid, 512, 0, s>>>(a);
-  else attn_fwd_kernel<128, 0, true, false><<<grid, 512, 0, s>>>(a);
+  // 64-row waves: measured faster for head width 128 (MHA layer, T = 4096:
+  // 0.129 vs 0.134 ms) and for MLA at T = 32768 (2.5 %), slower for MLA at
+  // T = 4096 (0.363 vs 0.354 ms); the results are the same bits either way
+  if (a.d_s == 64 && a.T >= kWideMinT) attn_fwd_kernel<128, 64, true, false, true><<<grid, 256, 0, s>>>(a);
+  else if (a.d_s == 64) attn_fwd_kernel<128, 64, true, false><<<grid, 512, 0, s>>>(a);
+  else attn_fwd_kernel<128, 0, true, false, true><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -425,6 +425,7 @@ def test_qk_clip_apply_essay_invariants():
     (2, 63, 3, 128, 0, True, "bf16"),
     (2, 65, 2, 128, 64, True, "bf16"),
     (1, 300, 4, 128, 64, False, "bf16"),
+    (1, 16384 + 77, 2, 128, 64, True, "bf16"),   # MLA at a length that runs 64-row waves
     (3, 257, 2, 64, 0, True, "bf16"),
     (2, 513, 2, 128, 0, False, "bf16"),
     (2, 40, 3, 16, 0, True, "bf16"),      # generic kernel
