@@ -384,6 +384,21 @@ attn_fwd_kernel(const AttnArgs a) {
           }
         }
       }
+      if constexpr (!OUT) {
+        // S_max alone needs no per-row maximum: the half's logits fold into
+        // per-lane running maxima, which meet across lanes once, after the
+        // last tile (no lane-pair exchange through LDS on every half)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          float x = max3_nan_ignoring(m_all[f], sacc[f][0], sacc[f][1]);
+#pragma unroll
+          for (int e = 2; e < 16; e += 2) x = max3_nan_ignoring(x, sacc[f][e], sacc[f][e + 1]);
+          m_all[f] = x;
+        }
+        // outstanding after this: the next half's first KSL K reads only
+        if (g == 0) read_k(std::integral_constant<int, 1>{});
+        return;
+      }
       // row max over the 32 keys (the lane pair l, l ^ 32 holds one query)
       float bm[NF];
       bool grow = false;
@@ -397,11 +412,6 @@ attn_fwd_kernel(const AttnArgs a) {
         bm[f] = x;
         if (SMAX) m_all[f] = fmaxf(m_all[f], x);
         grow = grow || (x > m_use[f] + thr);
-      }
-      if constexpr (!OUT) {
-        // outstanding after this: the next half's first KSL K reads only
-        if (g == 0) read_k(std::integral_constant<int, 1>{});
-        return;
       }
       if (__any(grow)) {
 #pragma unroll
