@@ -9,8 +9,8 @@
 // width is 128.
 //
 // Layout of the work. A block owns 256 query rows of one (sample, head) in
-// eight waves of 32 rows (two waves per SIMD; the logit pass: two blocks
-// per CU, of eight such waves or of four waves of 64 rows). Each wave keeps its rows in
+// eight waves of 32 rows (two waves per SIMD; the logit pass alone: four
+// waves of 64 rows, two blocks per CU). Each wave keeps its rows in
 // registers as an MFMA B-fragment for the whole kernel and walks the key axis
 // in tiles of 64 keys, which pass through a double-buffered LDS ring (K rows
 // XOR-swizzled
@@ -52,7 +52,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 #define FA_WAIT_DMA() __builtin_amdgcn_s_waitcnt(0x70 | 0xF00)
 
 constexpr int kBQ = 256, kBKV = 64, kDV = 128;
-constexpr int kWideMinT = 16384;   // MLA logit pass: 64-row waves from this sequence length on
 
 // V rows (256 bytes): a transposing read's 16-lane group covers four
 // consecutive rows at the same columns; chunk ^ 4 (r & 3) puts them on
@@ -132,19 +131,16 @@ __device__ __forceinline__ float wave_max(float x) {
 // VGPRs: every MFMA writes VGPRs and the rescale is plain VALU arithmetic.
 // OUT = false: the logits and S_max only (no values, softmax or output),
 // which serves max_logits_per_head for head width 128 and the MLA head
-// shape, with two blocks per CU: eight waves of 32 rows (at most 128
-// registers, four waves per SIMD) or, WIDE, four waves of 64 query rows (two
-// fragments, so each K fragment read from LDS feeds two MFMAs and a wave has
-// two independent accumulation chains; two waves per SIMD).
-template <int DK, int DS, bool SMAX, bool OUT = true, bool WIDE = false>
-__global__ void __launch_bounds__(WIDE ? 256 : 512, OUT ? 1 : 2)
-    __attribute__((amdgpu_waves_per_eu(OUT || WIDE ? 2 : 4, OUT || WIDE ? 2 : 4)))
+// shape. It runs four waves of 64 query rows (two fragments, so each K
+// fragment read from LDS feeds two MFMAs and a wave has two independent
+// accumulation chains) and two blocks per CU, again two waves per SIMD.
+template <int DK, int DS, bool SMAX, bool OUT = true>
+__global__ void __launch_bounds__(OUT ? 512 : 256, OUT ? 1 : 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(const AttnArgs a) {
   static_assert(OUT || SMAX, "a pass with neither output nor S_max");
-  static_assert(!(OUT && WIDE), "the output pass runs 32-row waves");
   static_assert(DK == 128 && (DS == 0 || DS == 64), "head widths");
-  constexpr int NF = WIDE ? 2 : 1;            // query fragments per wave
-  constexpr int NW = WIDE ? 4 : 8, WR = 32 * NF;   // waves per block, query rows per wave
+  constexpr int NF = OUT ? 1 : 2;            // query fragments per wave
+  constexpr int NW = OUT ? 8 : 4, WR = 32 * NF;   // waves per block, query rows per wave
   // MLA (192-wide queries): to fit 256 registers a half's K fragments go
   // through a ring of KSL = KS / 2 slots (the second half of the reads is
   // issued under the first half's MFMAs) and the two value k-steps share one
@@ -153,7 +149,7 @@ attn_fwd_kernel(const AttnArgs a) {
   constexpr int D = DK + DS, KS = D / 16;
   constexpr int KSL = kLean ? KS / 2 : KS, NVB = kLean ? 1 : 2;   // K slots, value buffers
   // one LDS stage: K content rows [64][256 B], rotary rows [64][128 B], V rows [64][256 B]
-  // (the logit pass keeps no values: two blocks share a CU)
+  // (the logit pass keeps no values: two blocks of four waves share a CU)
   constexpr int KC_BYTES = kBKV * 256, KR_BYTES = kBKV * DS * 2, VT_BYTES = OUT ? kBKV * kDV * 2 : 0;
   constexpr int STAGE = KC_BYTES + KR_BYTES + VT_BYTES;
   // LDS ring stages: each tile's loads go out while the previous tile is
@@ -370,6 +366,9 @@ attn_fwd_kernel(const AttnArgs a) {
         }
         if constexpr (s + KSL < KS) read_k1(g_, std::integral_constant<int, s + KSL>{});
       });
+      // S_max pass: the next half's first K reads go out before this half's
+      // fold (every ring slot is free once the last MFMA issued)
+      if constexpr (!OUT) { if (g == 0) read_k(std::integral_constant<int, 1>{}); }
       if constexpr (NF == 2) s_wait_logits(sacc[0], sacc[1]);
       else s_wait_logits(sacc[0]);
       if constexpr (OUT) read_v(g_, std::integral_constant<int, 0>{});
@@ -395,8 +394,6 @@ attn_fwd_kernel(const AttnArgs a) {
           for (int e = 2; e < 16; e += 2) x = max3_nan_ignoring(x, sacc[f][e], sacc[f][e + 1]);
           m_all[f] = x;
         }
-        // outstanding after this: the next half's first KSL K reads only
-        if (g == 0) read_k(std::integral_constant<int, 1>{});
         return;
       }
       // row max over the 32 keys (the lane pair l, l ^ 32 holds one query)
@@ -573,12 +570,8 @@ hipError_t launch_attention_smax_only(const AttnArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.T <= 0 || a.H <= 0) return hipSuccess;
   if (a.d_k != 128 || (a.d_s != 64 && a.d_s != 0) || !a.smax) return hipErrorInvalidValue;
   const int grid = (a.T + kBQ - 1) / kBQ * a.H * a.B;
-  // 64-row waves: measured faster for head width 128 (MHA layer, T = 4096:
-  // 0.129 vs 0.134 ms) and for MLA at T = 32768 (2.5 %), slower for MLA at
-  // T = 4096 (0.363 vs 0.354 ms); the results are the same bits either way
-  if (a.d_s == 64 && a.T >= kWideMinT) attn_fwd_kernel<128, 64, true, false, true><<<grid, 256, 0, s>>>(a);
-  else if (a.d_s == 64) attn_fwd_kernel<128, 64, true, false><<<grid, 512, 0, s>>>(a);
-  else attn_fwd_kernel<128, 0, true, false, true><<<grid, 256, 0, s>>>(a);
+  if (a.d_s == 64) attn_fwd_kernel<128, 64, true, false><<<grid, 256, 0, s>>>(a);
+  else attn_fwd_kernel<128, 0, true, false><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
