@@ -421,7 +421,8 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
       mm.block_start = blocks;
       mm.partial = part + (size_t)slot * w.mom_blocks;
       blocks += (mm.rp / 64) * mm.tiles_c;
-      bytes += (double)m.rows * m.cols * (dtype_size(m.g_dtype) + 8);   // read G, M; write M
+      // read G and M, write M and the bf16 copy of M that Newton-Schulz reads
+      bytes += (double)m.rows * m.cols * (dtype_size(m.g_dtype) + 10);
     }
     a.total_blocks = blocks;
     Prof pr(F_MOMENTUM, s, 0.0, bytes);
