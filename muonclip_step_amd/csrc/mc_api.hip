@@ -5,18 +5,22 @@
 // wave, on the caller's stream:
 //   momentum_kernel   M <- mu M + G, norm partials, bf16 X0 ([m][n]: M or M^T)
 //   norm_finalize     s = 1 / (||M||_F + eps)
-//   5 x { Gram  A = s0^2 X X^T          -> A as a bf16 pair A_hi + A_lo
+//   5 x { Gram  A = s0^2 X X^T          -> bf16 A_hi (+ A_lo if m < 1024)
 //         Poly  P = a I + b A + c A A   -> P_hi (+ P_lo if m < 1024)
 //         Apply X' = s0 P X             -> X' (ping-pong; last step: O) }
 //   W <- clip_row ((1 - lr wd) W - lr rms sqrt(max) O): in the last Apply's
 //   epilogue, or by update_kernel for waves that cannot fuse it
 // (s0 = s on the first step, 1 after). The apply is the quintic step of the
 // Notes on Muon blog, "Newton-Schulz", written as X' = (aI + bA + cA^2) X.
-// Operands are bf16, accumulation and every epilogue fp32; the Poly epilogue
-// reads b A from the pair A_hi + A_lo (about 16 significant bits). For
-// m < 1024 the Gram matrix and the polynomial also enter their products as
-// hi + lo bf16 pairs (3 and 2 MFMA passes), which keeps those small-m shapes
-// well inside the 2e-2 relative Frobenius bound.
+// Operands are bf16, accumulation and every epilogue fp32. The Poly
+// evaluates the polynomial at the matrix its product reads: P = a I +
+// b A_hi + c A_hi A_hi in fp32 with A_hi the bf16 Gram, so P is an exact
+// polynomial of one matrix (with b A taken from the fp32 Gram instead, the
+// two terms see different matrices, and a CPU emulation of the iteration
+// gave 1.4-2.5x larger errors against the fp64 iteration). For m < 1024 the
+// Gram matrix and the polynomial enter their products as hi + lo bf16 pairs
+// (3 and 2 MFMA passes; the b A term then reads the pair too), which keeps
+// those small-m shapes well inside the 2e-2 relative Frobenius bound.
 #include <math.h>
 #include <cmath>
 #include <stdarg.h>
@@ -277,9 +281,10 @@ struct WavePlan {
   int64_t mom_blocks;          // momentum blocks per matrix
   GemmPlan gram, poly, apply;
   int kt_gram, kt_poly, kt_apply;
-  // the Gram hands A to the Poly epilogue as fp32 in fragment order (off_alo)
-  // instead of the bf16 residual A_lo: groups without operand pairs whose two
-  // symmetric products run unsplit on the same tiles
+  // the Gram hands A_hi to the Poly epilogue a second time, in fragment
+  // order (off_alo), which the epilogue reads in 1 KB runs: groups without
+  // operand pairs whose two symmetric products run unsplit on the same tiles
+  // (other groups without pairs read A_hi itself, at the transposed position)
   bool frag;
 };
 
@@ -299,7 +304,7 @@ WavePlan plan_wave(const Group& g, int nb, int cus) {
   w.off_x0 = take(nb * mp * np * 2);
   w.off_x1 = take(nb * mp * np * 2);
   w.off_ahi = take(nb * mp * mp * 2);
-  w.off_alo = take(nb * mp * mp * (w.frag ? 4 : 2));
+  w.off_alo = take(nb * mp * mp * 2);
   w.off_phi = take(nb * mp * mp * 2);
   w.off_plo = g.split ? take(nb * mp * mp * 2) : 0;
   w.mom_blocks = (int64_t)(mp / 64) * (int64_t)(np / 64);
@@ -315,9 +320,9 @@ WavePlan plan_wave(const Group& g, int nb, int cus) {
 // space (each iteration after the first trades a Gram and an apply, both
 // n-sized, for three m x m products): for groups with n >= 2 m, where the
 // n-sized products saved outweigh the m x m products added, without hi/lo
-// operand pairs (A reaches the Poly as the fp32 fragment copy or, when the
-// symmetric products are split or tiled differently, as the bf16 pair
-// A_hi + A_lo), and with an unsplit apply (whose epilogue adds the identity
+// operand pairs (A reaches the Poly as A_hi, through the fragment-order copy
+// or, when the symmetric products are split or tiled differently, as
+// itself), and with an unsplit apply (whose epilogue adds the identity
 // part of the accumulated product). At least one iteration follows it, so
 // the fused update stays on an ordinary apply.
 constexpr int kGramHead = 3;   // at least 2
@@ -471,7 +476,8 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
   const double mm_ = (double)g.m, nn_ = (double)g.n;
   const int kt_sq = (int)(mp / kGemmBK);
   // Gram: A = s0^2 X X^T (s0 on the first iteration only), stored as a bf16
-  // pair A_hi + A_lo, or as A_hi and the fp32 fragment copy
+  // pair A_hi + A_lo (operand pairs), or as A_hi and, where the Poly tiles
+  // match, its fragment-order copy
   auto gram = [&](const uint16_t* x, bool first) -> mc_status {
     GemmArgs a{};
     a.M = (int32_t)mp; a.N = (int32_t)mp; a.batch = nb;
@@ -480,8 +486,8 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
     a.epi.alpha = 1.0f; a.epi.scale_pow = first ? 2 : 0; a.epi.scale = scale;
     a.epi.out_hi = Ahi; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
     if (w.frag) {
-      a.epi.frag_out = (float*)Alo; a.epi.frag_nb = (int32_t)(mp / 32); a.epi.bs_frag = mp * mp;
-    } else {
+      a.epi.frag_out = Alo; a.epi.frag_nb = (int32_t)(mp / 32); a.epi.bs_frag = mp * mp;
+    } else if (g.split) {
       a.epi.out_lo = Alo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp;
     }
     return launch_gemm_planned(w.gram, GEMM_GRAM, g.split, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * nn_ * nb,
@@ -501,9 +507,9 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
     a.ktiles = w.kt_poly;
     a.epi.alpha = hp.ns_c; a.epi.beta = hp.ns_b; a.epi.diag = hp.ns_a;
     if (w.frag) {
-      a.epi.frag_in = (const float*)Alo; a.epi.frag_nb = (int32_t)(mp / 32); a.epi.bs_frag = mp * mp;
+      a.epi.frag_in = Alo; a.epi.frag_nb = (int32_t)(mp / 32); a.epi.bs_frag = mp * mp;
     } else {
-      a.epi.cin_hi = Ahi; a.epi.cin_lo = Alo; a.epi.ld_cin = (int32_t)mp; a.epi.bs_cin = mp * mp;
+      a.epi.cin_hi = Ahi; a.epi.cin_lo = g.split ? Alo : nullptr; a.epi.ld_cin = (int32_t)mp; a.epi.bs_cin = mp * mp;
     }
     a.epi.out_hi = out_hi; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
     if (Plo) { a.epi.out_lo = Plo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp; }
@@ -513,8 +519,8 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
   // C = L R + diag I of two exactly symmetric m x m matrices (the Gram-space
   // head): R is read by rows, which are its columns; C is symmetric up to
   // rounding (L and R are polynomials in one matrix, so they commute) and only
-  // its upper tiles are computed, then mirrored. to_a: store C as A_hi plus
-  // what the next Poly reads besides it (the fp32 fragment copy, or A_lo).
+  // its upper tiles are computed, then mirrored. to_a: C is the next A, so
+  // its fragment-order copy is also written where the Poly reads one.
   auto sym_product = [&](const uint16_t* l, const uint16_t* r, uint16_t* out, bool to_a, float diag = 0.0f,
                          const uint16_t* c = nullptr, float beta = 0.0f) -> mc_status {
     GemmArgs a{};
@@ -525,9 +531,7 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
     if (c) { a.epi.cin_hi = c; a.epi.beta = beta; a.epi.ld_cin = (int32_t)mp; a.epi.bs_cin = mp * mp; }
     a.epi.out_hi = out; a.epi.ld_hi = (int32_t)mp; a.epi.bs_hi = mp * mp;
     if (to_a && w.frag) {
-      a.epi.frag_out = (float*)Alo; a.epi.frag_nb = (int32_t)(mp / 32); a.epi.bs_frag = mp * mp;
-    } else if (to_a) {
-      a.epi.out_lo = Alo; a.epi.ld_lo = (int32_t)mp; a.epi.bs_lo = mp * mp;
+      a.epi.frag_out = Alo; a.epi.frag_nb = (int32_t)(mp / 32); a.epi.bs_frag = mp * mp;
     }
     return launch_gemm_planned(w.poly, GEMM_GRAM, false, a, s, ws, w.off_splitk, 2.0 * mm_ * mm_ * mm_ * nb,
                                (c ? 8.0 : 6.0) * mm_ * mm_ * nb);
@@ -589,7 +593,7 @@ mc_status run_wave(const mc_matrix* mats, const Group& g, const int* ids, int nb
     if (!st) st = sym_product(Phi, T0, Ahi, true);    // A1 = P0 (A0 P0)
     if (!st) st = poly(T0);                           // P1
     if (!st) st = sym_product(T0, Phi, r_buf, false, (float)(-a_ * a_));   // R1 = P1 P0 - a^2 I
-    // P_{j-1} in T0, R_{j-1} in r_buf, A_{j-1} in A_hi (+ fp32 copy); spare
+    // P_{j-1} in T0, R_{j-1} in r_buf, A_{j-1} in A_hi (+ its copy); spare
     // is free (P0's buffer once R1 is formed)
     uint16_t* spare = Phi;
     for (int j = 2; j < kGramHead && !st; ++j) {

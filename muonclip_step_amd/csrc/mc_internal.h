@@ -43,8 +43,8 @@ struct GemmSeg {
 
 // Epilogue: v = alpha * scale[b]^pow * acc + beta * (cin_hi + cin_lo)[i][j]
 // + diag * (i==j), then any of: bf16 store (hi), bf16 residual store
-// (lo = v - hi). cin is a bf16 hi + lo pair
-// (about 16 significant bits). Every pointer is the batch-0 base; bs_* are the
+// (lo = v - hi). cin is a bf16 hi + lo pair (about 16 significant bits), or
+// cin_hi alone when cin_lo is NULL. Every pointer is the batch-0 base; bs_* are the
 // per-batch strides in elements.
 struct GemmEpi {
   float alpha;
@@ -55,12 +55,13 @@ struct GemmEpi {
   float diag;
   uint16_t* out_hi; int32_t ld_hi; int64_t bs_hi;
   uint16_t* out_lo; int32_t ld_lo; int64_t bs_lo;
-  // fp32 v in MFMA fragment order, for a later epilogue whose tiles cover the
-  // same 32x32 blocks: register 4g+q of lane l of block (bi, bj) of batch b
-  // sits at (((bi * frag_nb + bj) * 4 + g) * 64 + l) * 4 + q + b * bs_frag,
+  // bf16(v), rounded as the out_hi store rounds it, in MFMA fragment order,
+  // for a later epilogue whose tiles cover the same 32x32 blocks: register
+  // r = 4g+q of lane l of block (bi, bj) of batch b sits at
+  // (((bi * frag_nb + bj) * 2 + r / 8) * 64 + l) * 8 + r % 8 + b * bs_frag,
   // so each 16-byte access of a wave covers 1 KB. frag_out: written (the
   // Gram); frag_in: read as the beta term instead of cin (the Poly).
-  float* frag_out; const float* frag_in; int32_t frag_nb; int64_t bs_frag;
+  uint16_t* frag_out; const uint16_t* frag_in; int32_t frag_nb; int64_t bs_frag;
   // unsplit apply only: out = bf16(bf16(v) + xadd_coef * scale * xadd[i][j]),
   // xadd a bf16 matrix laid out like the output (the identity part of the
   // Gram-space head's Q, added to R X0 at full precision)
@@ -85,7 +86,7 @@ enum GemmTile { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2 };
 // which Newton-Schulz product a launch computes; fixes the epilogue:
 //   GRAM  A = s^2 X X^T      -> bf16 A_hi + A_lo           (symmetric tiles)
 //         (also L R of two symmetric m x m matrices, R read by rows, to bf16
-//         C alone or to C_hi + the fp32 fragment copy)
+//         C alone or to C_hi + its bf16 fragment-order copy)
 //   POLY  P = a I + b A + c A A -> bf16 P_hi (+ P_lo)        (symmetric tiles)
 //   APPLY X' = s P X          -> bf16 X' (B = X read as [k][n])
 enum GemmKind { GEMM_GRAM = 0, GEMM_POLY = 1, GEMM_APPLY = 2 };

@@ -58,6 +58,7 @@ __device__ inline int xcd_remap(int L, int total) {
 // bf16 v to out_hi and bf16 (v - hi) to out_lo, in 16-byte accesses (row
 // starts and strides are multiples of 8 elements).
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __attribute__((always_inline)) inline void epilogue_store8(const GemmEpi& e, int b, int i, int j0,
                                                                       const float (&acc)[8], float sc) {
   float v[8];
@@ -121,11 +122,9 @@ enum : int {
   E_DIAG = 32,    // v += diag on i == j
   E_PART = 64,    // split-K: raw fp32 partial, no epilogue
   E_SYM = 128,    // upper tiles only; off-diagonal tiles also stored mirrored
-  E_LOMIR = 256,  // the lo part is read only transposed (by the Poly epilogue):
-                  // off-diagonal tiles store it mirrored only
   E_UPD = 512,    // last apply: the weight update with v as O, no store of v
-  E_FOUT = 1024,  // also store v in fp32 fragment order (frag_out)
-  E_FIN = 2048,   // v += beta * frag_in (fp32 fragment order) instead of cin
+  E_FOUT = 1024,  // also store bf16(v) in fragment order (frag_out)
+  E_FIN = 2048,   // v += beta * frag_in (bf16, fragment order) instead of cin
   E_XADD = 4096,  // store pass adds xadd_coef * scale * xadd[i][j] to bf16 v (apply)
   E_CIN1 = 8192,  // with E_CIN: cin_hi alone (v += beta * cin_hi[i][j])
 };
@@ -475,20 +474,23 @@ ns_gemm_kernel(const GemmArgs p, const FusedUpd u) {
   uint16_t* ohi = (EPI & E_HI) ? p.epi.out_hi + (int64_t)b * p.epi.bs_hi : nullptr;
   uint16_t* olo = (EPI & E_LO) ? p.epi.out_lo + (int64_t)b * p.epi.bs_lo : nullptr;
   const uint32_t t_cin = (uint32_t)((wj0 + lj) * ld_cin + wi0 + li);
-  // this lane's registers 4g .. 4g+3 of fragment (fi, fj) in the fp32
-  // fragment-order copy (g = 0 here; the next g is 256 floats further)
+  // this lane's registers 0 .. 7 of fragment (fi, fj) in the bf16
+  // fragment-order copy (registers 8 .. 15 are 512 elements further)
   auto frag_ptr = [&](auto* base, int fi, int fj) __attribute__((always_inline)) {
     const int bi = (wi0 + fi * 32) >> 5, bj = (wj0 + fj * 32) >> 5;
-    return base + (int64_t)b * p.epi.bs_frag + (int64_t)(bi * p.epi.frag_nb + bj) * 1024 + lane * 4;
+    return base + (int64_t)b * p.epi.bs_frag + (int64_t)(bi * p.epi.frag_nb + bj) * 1024 + lane * 8;
   };
-  if (EPI & E_FOUT) {   // straight from the accumulators
+  if (EPI & E_FOUT) {   // straight from the accumulators, rounded as the bf16 store below rounds them
     auto frag_out = [&](const f32x16_t& a, int fi, int fj) __attribute__((always_inline)) {
       if (wi0 + fi * 32 >= p.M || wj0 + fj * 32 >= p.N) return;
-      float* d = frag_ptr(p.epi.frag_out, fi, fj);
+      uint16_t* d = frag_ptr(p.epi.frag_out, fi, fj);
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *(f32x4_t*)(d + 256 * g) =
-            f32x4_t{a[4 * g] * alpha, a[4 * g + 1] * alpha, a[4 * g + 2] * alpha, a[4 * g + 3] * alpha};
+      for (int h = 0; h < 2; ++h) {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = f32x2_to_bf16x2(a[8 * h + 2 * k] * alpha, a[8 * h + 2 * k + 1] * alpha);
+        *(u32x4_t*)(d + 512 * h) = u32x4_t{w[0], w[1], w[2], w[3]};
+      }
     };
     FragVisit<0, FM * FN, FN>::run(acc, frag_out);
   }
@@ -500,19 +502,19 @@ ns_gemm_kernel(const GemmArgs p, const FusedUpd u) {
   __builtin_amdgcn_s_barrier();          // every wave is done with the ring
 
   // write pass: v (or its bf16 residual when lo_pass) into T
-  // The fp32 A of the Poly's b A term (E_FIN) is read for a group of
+  // The bf16 A of the Poly's b A term (E_FIN) is read for a group of
   // fragments before they are staged, so its latency is paid once per group.
   constexpr int kFinGrp = NW == 4 ? 8 : 4;   // registers free in the epilogue (4 and 16 measured slower)
   constexpr int NFR = FM * FN, FGRP = (EPI & E_FIN) ? (NFR < kFinGrp ? NFR : kFinGrp) : 1;
-  auto load_fin = [&](int fi, int fj, f32x4_t (&c_f)[4]) __attribute__((always_inline)) {
+  auto load_fin = [&](int fi, int fj, u32x4_t (&c_f)[2]) __attribute__((always_inline)) {
     // (fragments past M or N are never stored and read nothing)
     const bool in = wi0 + fi * 32 < p.M && wj0 + fj * 32 < p.N;
-    const float* src = frag_ptr(p.epi.frag_in, in ? fi : 0, in ? fj : 0);
+    const uint16_t* src = frag_ptr(p.epi.frag_in, in ? fi : 0, in ? fj : 0);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) c_f[g] = in ? *(const f32x4_t*)(src + 256 * g) : f32x4_t{};
+    for (int h = 0; h < 2; ++h) c_f[h] = in ? *(const u32x4_t*)(src + 512 * h) : u32x4_t{};
   };
   auto stage = [&](bool lo_pass) __attribute__((always_inline)) {
-    auto frag_stage = [&](const f32x16_t& a, int fi, int fj, const f32x4_t (&c_f)[4]) __attribute__((always_inline)) {
+    auto frag_stage = [&](const f32x16_t& a, int fi, int fj, const u32x4_t (&c_f)[2]) __attribute__((always_inline)) {
       uint2 c_hi[4], c_lo[4];
       if (EPI & E_CIN) {   // rows r..r+3 at column c of the symmetric A, read as row c
 #pragma unroll
@@ -530,7 +532,10 @@ ns_gemm_kernel(const GemmArgs p, const FusedUpd u) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           v[q] = a[4 * g + q] * alpha;
-          if (EPI & E_FIN) v[q] += beta * c_f[g][q];
+          if (EPI & E_FIN) {   // register 4g + q: half g / 2, element 4 (g % 2) + q
+            const uint32_t wf = c_f[g >> 1][2 * (g & 1) + (q >> 1)];
+            v[q] += beta * bf16_to_f32((uint16_t)((q & 1) ? wf >> 16 : wf));
+          }
           if (EPI & E_CIN) {
             const uint32_t wh = q < 2 ? c_hi[g].x : c_hi[g].y;
             const float ch = bf16_to_f32((uint16_t)((q & 1) ? wh >> 16 : wh));
@@ -553,7 +558,7 @@ ns_gemm_kernel(const GemmArgs p, const FusedUpd u) {
     };
 #pragma unroll
     for (int I0 = 0; I0 < NFR; I0 += FGRP) {
-      f32x4_t cf[FGRP][4];
+      u32x4_t cf[FGRP][2];
       if (EPI & E_FIN) {
 #pragma unroll
         for (int k = 0; k < FGRP; ++k) load_fin((I0 + k) / FN, (I0 + k) % FN, cf[k]);
@@ -739,7 +744,7 @@ ns_gemm_kernel(const GemmArgs p, const FusedUpd u) {
   if (EPI & E_LO) {
     MC_WAIT_LGKM_ALL();
     stage(true);
-    if (!(EPI & E_LOMIR) || !mirror) store_direct(olo, ld_lo);
+    store_direct(olo, ld_lo);
     if (mirror) store_trans(olo, ld_lo);
   }
 }
@@ -822,18 +827,19 @@ hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const G
   // a Gram-kind C input is hi only, on a product without operand pairs or fragment copy
   if (kind == GEMM_GRAM && e.cin_hi && (e.cin_lo || split_pair || e.frag_out || e.out_lo))
     return hipErrorInvalidValue;
+  // a residual (lo) store needs operand pairs, which a Poly without them does not read
+  if ((e.out_lo && !split_pair) || (kind == GEMM_POLY && e.cin_lo && !split_pair)) return hipErrorInvalidValue;
   const bool frag = (kind == GEMM_GRAM && e.frag_out) || (kind == GEMM_POLY && e.frag_in);
   if (frag && (a.splits > 1 || split_pair || ((uintptr_t)(kind == GEMM_GRAM ? (const void*)e.frag_out : e.frag_in) & 15) ||
-               e.frag_nb * 32 < a.M || e.frag_nb * 32 < a.N || (e.bs_frag & 3)))
+               e.frag_nb * 32 < a.M || e.frag_nb * 32 < a.N || (e.bs_frag & 7)))
     return hipErrorInvalidValue;
   if (a.splits > 1) {
     launch_epi<E_PART>(tile, a, total, s, u);
   } else if (kind == GEMM_GRAM) {
-    // without operand pairs the Poly epilogue reads A from the fp32 copy in
-    // fragment order (with them, A_lo is an operand too)
+    // without operand pairs the Poly epilogue reads A_hi from the bf16 copy
+    // in fragment order (with them, A_lo is an operand too)
     if (split_pair) launch_epi<E_SYM | E_HI | E_LO>(tile, a, total, s, u);
     else if (frag) launch_epi<E_SYM | E_HI | E_FOUT>(tile, a, total, s, u);
-    else if (e.out_lo) launch_epi<E_SYM | E_HI | E_LO | E_LOMIR>(tile, a, total, s, u);
     // bf16 products of two symmetric matrices (Gram-space head), plus diag on
     // the diagonal and beta times a third symmetric matrix
     else if (e.cin_hi) launch_epi<E_SYM | E_CIN | E_CIN1 | E_DIAG | E_HI>(tile, a, total, s, u);
@@ -842,7 +848,7 @@ hipError_t launch_ns_gemm(GemmTile tile, GemmKind kind, bool split_pair, const G
   } else if (kind == GEMM_POLY) {
     if (split_pair) launch_epi<E_SYM | E_CIN | E_DIAG | E_HI | E_LO>(tile, a, total, s, u);
     else if (frag) launch_epi<E_SYM | E_FIN | E_DIAG | E_HI>(tile, a, total, s, u);
-    else launch_epi<E_SYM | E_CIN | E_DIAG | E_HI>(tile, a, total, s, u);
+    else launch_epi<E_SYM | E_CIN | E_CIN1 | E_DIAG | E_HI>(tile, a, total, s, u);   // b A_hi
   } else if (fused) {
     launch_epi<E_UPD, 1>(tile, a, total, s, u);   // last apply with the weight update
   } else if (e.xadd) {
