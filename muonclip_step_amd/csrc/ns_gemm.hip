@@ -504,7 +504,7 @@ ns_gemm_kernel(const GemmArgs p, const FusedUpd u) {
   // write pass: v (or its bf16 residual when lo_pass) into T
   // The bf16 A of the Poly's b A term (E_FIN) is read for a group of
   // fragments before they are staged, so its latency is paid once per group.
-  constexpr int kFinGrp = NW == 4 ? 8 : 4;   // registers free in the epilogue (4 and 16 measured slower)
+  constexpr int kFinGrp = 8;   // eight fragments' bf16 A: 64 registers (the fp32 copy allowed four with eight waves)
   constexpr int NFR = FM * FN, FGRP = (EPI & E_FIN) ? (NFR < kFinGrp ? NFR : kFinGrp) : 1;
   auto load_fin = [&](int fi, int fj, u32x4_t (&c_f)[2]) __attribute__((always_inline)) {
     // (fragments past M or N are never stored and read nothing)
