@@ -24,6 +24,14 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 # [0.002, 1] into this interval (pinned on the oracle by the CPU tests)
 BAND = (0.68, 1.21)
 
+# The workloads' momenta are well-conditioned Gaussian matrices, on which the
+# kernels' precision scheme (bf16 operands, fp32 accumulation, the polynomial
+# evaluated at the bf16 Gram it multiplies) lands at 4.4e-3 to 8.1e-3
+# relative Frobenius against the fp64 oracle, as a CPU emulation of that
+# arithmetic also gives. Above this guard the result would still be inside
+# the 2e-2 tolerance, but the scheme would have lost precision.
+WORKLOAD_NS_GUARD = 1e-2
+
 
 def weights_of(cfg):
     return {s.name: wl.draw_weight(cfg, i) for i, s in enumerate(cfg.matrices) if not s.device_drawn}
@@ -88,6 +96,7 @@ def test_config3_step_all_matrices(cfg3):
             continue
         err = check_matrix(s, hp, g_orc, gamma_gpu=g_gpu)
         print(s.spec.name, "NS rel err %.3e" % err, flush=True)
+        assert err <= WORKLOAD_NS_GUARD, f"NS rel err {err:.3e} above the workload guard"
     ia = names.index("kv_a")
     assert torch.equal(a[ia].w, b[ia].w)
     for nm, period, segs in (("q_b", 192, ((0, 128, 0.5), (128, 64, 1.0))), ("kv_b", 256, ((0, 128, 0.5),))):
@@ -118,6 +127,7 @@ def test_config3_o_projection():
     torch.cuda.synchronize()
     err = check_matrix(st, hp)
     print("o NS rel err %.3e" % err, flush=True)
+    assert err <= WORKLOAD_NS_GUARD, f"NS rel err {err:.3e} above the workload guard"
 
 
 @pytest.mark.timeout(300)
@@ -224,6 +234,7 @@ def test_config4_moe_experts_sampled():
         st = host_state(cfg.matrices[i], *host[i], w, g, m, o_out[i])
         err = check_matrix(st, hp)
         print(cfg.matrices[i].name, "NS rel err %.3e" % err, flush=True)
+        assert err <= WORKLOAD_NS_GUARD, f"NS rel err {err:.3e} above the workload guard"
     print("config 4: momentum of all %d matrices" % n, flush=True)
     _momentum_all(cfg, keep, hp)
     for i in range(n):
@@ -287,6 +298,7 @@ def test_config5_full_layer_sampled():
         st = host_state(spec, *host[i], w, g, m, o_out[i])
         err = check_matrix(st, hp, g_orc if spec.clip_slot >= 0 else None, gamma_gpu=g_gpu)
         print(spec.name, "NS rel err %.3e" % err, flush=True)
+        assert err <= WORKLOAD_NS_GUARD, f"NS rel err {err:.3e} above the workload guard"
         host.pop(i)
     print("config 5: momentum of every device-drawn matrix", flush=True)
     _momentum_all(cfg, keep, hp)
