@@ -17,10 +17,11 @@
 // b A_hi + c A_hi A_hi in fp32 with A_hi the bf16 Gram, so P is an exact
 // polynomial of one matrix (with b A taken from the fp32 Gram instead, the
 // two terms see different matrices, and a CPU emulation of the iteration
-// gave 1.2-2.5x larger errors against the fp64 iteration on full-rank inputs). For m < 1024 the
-// Gram matrix and the polynomial enter their products as hi + lo bf16 pairs
-// (3 and 2 MFMA passes; the b A term then reads the pair too), which keeps
-// those small-m shapes well inside the 2e-2 relative Frobenius bound.
+// gave 1.2-2.5x larger errors against the fp64 iteration on full-rank
+// inputs). For m < 1024 the Gram matrix and the polynomial enter their
+// products as hi + lo bf16 pairs (3 and 2 MFMA passes; the b A term then
+// reads the pair too), which keeps those small-m shapes well inside the
+// 2e-2 relative Frobenius bound.
 #include <math.h>
 #include <cmath>
 #include <stdarg.h>
