@@ -840,13 +840,11 @@ static mc_status step_impl(const mc_matrix* mats, int32_t n, const mc_hparams* h
   }
   // Two lanes (the caller's stream and the library's auxiliary stream, each
   // with half the workspace) when there are at least two shape groups and
-  // every group fits a half. A single wave is never split to fill a second
-  // lane (on the MHA layer two half-waves measured slower than one wave), and
-  // waves of one group stay on one lane (on the 1155 MoE experts a second
-  // lane measured no faster: the matrix cores are the bound); shape groups of
-  // different sizes (the MLA layer's five matrices) gain 9 %.
-  // While kernel timing is on (mc_profile_enable), every chain runs on the
-  // caller's stream, so that no two timed launches overlap.
+  // every group fits a half; which chain runs on which lane is decided below.
+  // A single wave is never split to fill a second lane (on the MHA layer two
+  // half-waves measured slower than one wave). While kernel timing is on
+  // (mc_profile_enable), every chain runs on the caller's stream, so that no
+  // two timed launches overlap.
   const size_t half = (workspace_bytes / 2) & ~(kAlign - 1);
   std::vector<Chain> chains = plan_chains(groups, wave_cap, hp->ns_steps);
   bool two = groups.size() >= 2 && chains.size() >= 2 && !one_lane && !profiling_on();
@@ -881,14 +879,30 @@ static mc_status step_impl(const mc_matrix* mats, int32_t n, const mc_hparams* h
   // fork: the auxiliary stream starts after everything enqueued on `stream`
   if (hipEventRecord(aux->fork, s) != hipSuccess || hipStreamWaitEvent(aux->s, aux->fork, 0) != hipSuccess)
     return fail(MC_ERR_HIP, "stream fork failed");
-  // largest chains first, each to the lane with less work so far
+  // Lanes. A chain whose Gram launch runs unsplit with a tile for every CU
+  // ("large") runs on `stream`, after the other large ones: two large chains
+  // side by side only interleave their workgroups (each takes whole CUs) and
+  // break up the launches' full rounds (full K2 layer: 525-527 ms this way,
+  // 530-532 ms with every chain balanced over the two lanes). The small
+  // chains (split-K, or fewer tiles than CUs: launches that leave CUs idle)
+  // go to the auxiliary stream beside them (MLA layer: 8.5 ms either way,
+  // 10.2 ms on one lane). Without large chains, the chains are balanced over
+  // both lanes, largest first.
+  const int cus = device_cus();
+  std::vector<char> small(chains.size());
+  bool any_large = false;
+  for (size_t i = 0; i < chains.size(); ++i) {
+    const GemmPlan gp = plan_wave(groups[chains[i].gi], chains[i].nb, cus).gram;
+    small[i] = gp.splits > 1 || (int64_t)gp.tiles_m * (gp.tiles_m + 1) / 2 * chains[i].nb < cus;
+    any_large = any_large || !small[i];
+  }
   std::vector<int> order(chains.size());
   for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
   std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return chains[x].flops > chains[y].flops; });
   double load[2] = {0.0, 0.0};
   for (int i : order) {
     const Chain& c = chains[i];
-    const int lane = load[1] < load[0] ? 1 : 0;
+    const int lane = any_large ? (small[i] ? 1 : 0) : (load[1] < load[0] ? 1 : 0);
     load[lane] += c.flops;
     st = run_wave(mats, groups[c.gi], groups[c.gi].idx.data() + c.b0, c.nb, *hp, s_max, heads,
                   (char*)workspace + lane * half, lane ? aux->s : s, &gamma_once, slots, smax_ready);
