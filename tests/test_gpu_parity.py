@@ -382,6 +382,42 @@ def test_two_lanes_match_one_lane_bit_for_bit():
             assert torch.equal(w0, w1) and torch.equal(m0, m1) and torch.equal(o0, o1)
 
 
+
+def test_large_and_small_waves_on_two_lanes_bit_for_bit():
+    """Eight 2048^2 matrices (their Gram launch has a tile for every CU: a
+    large wave, on the caller's stream) and two 256 x 512 ones (a small wave,
+    on the auxiliary stream beside it): the weights, momenta and O must equal
+    bit for bit those of the same waves run on one stream (kernel timing on,
+    which keeps every chain on the caller's stream; the waves are the same, so
+    are the kernels), and sampled matrices of both groups match the oracle."""
+    states = []
+    for k in range(10):
+        shape = (2048, 2048) if k < 8 else (256, 512)
+        spec = wl.MatrixSpec("ls", *shape, "bf16", init_std=0.02, grad_std=1e-3, mom_std=1e-3)
+        seed = 3400 + k
+        w = wl.quantize_bf16(wl.normal(seed, 0, shape, 0.02))
+        g = wl.quantize_f32(wl.normal(seed, 1, shape, 1e-3))
+        m = wl.quantize_f32(wl.normal(seed, 2, shape, 1e-3))
+        states.append(State(spec, w, g, m))
+    hp = mc.hparams(lr=0.01)
+    descs = [st.desc() for st in states]
+    ws = torch.empty(mc.workspace_size(descs, hp), dtype=torch.uint8, device="cuda")
+    outs = []
+    for one_stream in (False, True):
+        print("large and small waves, one stream:", one_stream, flush=True)
+        _fresh(states)
+        mc.profile_enable(one_stream)
+        try:
+            mc.muonclip_step(descs, hp, workspace=ws)
+            torch.cuda.synchronize()
+        finally:
+            mc.profile_enable(False)
+        outs.append([(st.w.cpu().clone(), st.m.cpu().clone(), st.o.cpu().clone()) for st in states])
+    for (w0, m0, o0), (w1, m1, o1) in zip(outs[0], outs[1]):
+        assert torch.equal(w0, w1) and torch.equal(m0, m1) and torch.equal(o0, o1)
+    for k in (0, 9):
+        check_matrix(states[k], hp)
+
 # ----------------------------------------------------------------- QK-Clip alone
 
 def test_qk_clip_apply_essay_invariants():
