@@ -854,6 +854,29 @@ static mc_status step_impl(const mc_matrix* mats, int32_t n, const mc_hparams* h
     two = cap2[gi] > 0;
   }
   if (two) chains = plan_chains(groups, cap2, hp->ns_steps);
+  // Lanes. A chain whose Gram launch runs unsplit with a tile for every CU
+  // ("large") runs on `stream`, after the other large ones: two large chains
+  // side by side only interleave their workgroups (each takes whole CUs) and
+  // break up the launches' full rounds (full K2 layer: 525-527 ms this way,
+  // 530-532 ms with every chain balanced over the two lanes). The small
+  // chains (split-K, or fewer tiles than CUs: launches that leave CUs idle)
+  // go to the auxiliary stream beside them (MLA layer: 8.5 ms either way,
+  // 10.2 ms on one lane). Without large chains, the chains are balanced over
+  // both lanes, largest first; without small ones, one lane with the whole
+  // workspace runs them all.
+  const int cus = device_cus();
+  std::vector<char> small(chains.size());
+  bool any_large = false, any_small = false;
+  for (size_t i = 0; i < chains.size() && two; ++i) {
+    const GemmPlan gp = plan_wave(groups[chains[i].gi], chains[i].nb, cus).gram;
+    small[i] = gp.splits > 1 || (int64_t)gp.tiles_m * (gp.tiles_m + 1) / 2 * chains[i].nb < cus;
+    any_large = any_large || !small[i];
+    any_small = any_small || small[i];
+  }
+  if (two && !any_small) {
+    two = false;
+    chains = plan_chains(groups, wave_cap, hp->ns_steps);
+  }
 
   hipStream_t s = (hipStream_t)stream;
   float* gamma_once = gamma_out;   // written by the first update launch
@@ -879,23 +902,6 @@ static mc_status step_impl(const mc_matrix* mats, int32_t n, const mc_hparams* h
   // fork: the auxiliary stream starts after everything enqueued on `stream`
   if (hipEventRecord(aux->fork, s) != hipSuccess || hipStreamWaitEvent(aux->s, aux->fork, 0) != hipSuccess)
     return fail(MC_ERR_HIP, "stream fork failed");
-  // Lanes. A chain whose Gram launch runs unsplit with a tile for every CU
-  // ("large") runs on `stream`, after the other large ones: two large chains
-  // side by side only interleave their workgroups (each takes whole CUs) and
-  // break up the launches' full rounds (full K2 layer: 525-527 ms this way,
-  // 530-532 ms with every chain balanced over the two lanes). The small
-  // chains (split-K, or fewer tiles than CUs: launches that leave CUs idle)
-  // go to the auxiliary stream beside them (MLA layer: 8.5 ms either way,
-  // 10.2 ms on one lane). Without large chains, the chains are balanced over
-  // both lanes, largest first.
-  const int cus = device_cus();
-  std::vector<char> small(chains.size());
-  bool any_large = false;
-  for (size_t i = 0; i < chains.size(); ++i) {
-    const GemmPlan gp = plan_wave(groups[chains[i].gi], chains[i].nb, cus).gram;
-    small[i] = gp.splits > 1 || (int64_t)gp.tiles_m * (gp.tiles_m + 1) / 2 * chains[i].nb < cus;
-    any_large = any_large || !small[i];
-  }
   std::vector<int> order(chains.size());
   for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
   std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return chains[x].flops > chains[y].flops; });
