@@ -418,6 +418,41 @@ def test_large_and_small_waves_on_two_lanes_bit_for_bit():
     for k in (0, 9):
         check_matrix(states[k], hp)
 
+def test_two_groups_of_large_waves_run_on_one_lane():
+    """Two shape groups whose waves are all large (eight 2048^2 matrices and
+    eight 2048 x 4096 ones, the latter through the Gram-space head): nothing
+    is left for a second lane, so the step runs on the caller's stream with
+    waves planned for the whole workspace, the same waves as with kernel
+    timing on. Weights, momenta and O must match that run bit for bit, and
+    a matrix of each group matches the oracle."""
+    states = []
+    for k in range(16):
+        shape = (2048, 2048) if k < 8 else (2048, 4096)
+        spec = wl.MatrixSpec("ll", *shape, "bf16", init_std=0.02, grad_std=1e-3, mom_std=1e-3)
+        seed = 3500 + k
+        w = wl.quantize_bf16(wl.normal(seed, 0, shape, 0.02))
+        g = wl.quantize_f32(wl.normal(seed, 1, shape, 1e-3))
+        m = wl.quantize_f32(wl.normal(seed, 2, shape, 1e-3))
+        states.append(State(spec, w, g, m))
+    hp = mc.hparams(lr=0.01)
+    descs = [st.desc() for st in states]
+    ws = torch.empty(mc.workspace_size(descs, hp), dtype=torch.uint8, device="cuda")
+    outs = []
+    for one_stream in (False, True):
+        print("two groups of large waves, one stream:", one_stream, flush=True)
+        _fresh(states)
+        mc.profile_enable(one_stream)
+        try:
+            mc.muonclip_step(descs, hp, workspace=ws)
+            torch.cuda.synchronize()
+        finally:
+            mc.profile_enable(False)
+        outs.append([(st.w.cpu().clone(), st.m.cpu().clone(), st.o.cpu().clone()) for st in states])
+    for (w0, m0, o0), (w1, m1, o1) in zip(outs[0], outs[1]):
+        assert torch.equal(w0, w1) and torch.equal(m0, m1) and torch.equal(o0, o1)
+    for k in (0, 15):
+        check_matrix(states[k], hp)
+
 # ----------------------------------------------------------------- QK-Clip alone
 
 def test_qk_clip_apply_essay_invariants():
