@@ -12,6 +12,8 @@
 //   epilogue, or by update_kernel for waves that cannot fuse it
 // (s0 = s on the first step, 1 after). The apply is the quintic step of the
 // Notes on Muon blog, "Newton-Schulz", written as X' = (aI + bA + cA^2) X.
+// Groups with n >= 2m (m >= 1024) run the first kGramHead iterations on
+// m x m products instead (the Gram-space head, gram_head and run_wave).
 // Operands are bf16, accumulation and every epilogue fp32. The Poly
 // evaluates the polynomial at the matrix its product reads: P = a I +
 // b A_hi + c A_hi A_hi in fp32 with A_hi the bf16 Gram, so P is an exact
@@ -29,6 +31,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <string>
@@ -94,15 +97,12 @@ const char* kFamilyNames[F_COUNT] = {"momentum_norm", "norm_finalize", "ns_gemm"
 
 struct ProfRec { int fam; hipEvent_t a, b; double flops, bytes; };
 std::mutex g_prof_mu;
-bool g_prof = false;
+std::atomic<bool> g_prof{false};   // written under g_prof_mu, read without it
 std::vector<ProfRec> g_recs;
 std::vector<hipEvent_t> g_pool;
 size_t g_pool_used = 0;
 
-bool profiling_on() {
-  std::lock_guard<std::mutex> lk(g_prof_mu);
-  return g_prof;
-}
+bool profiling_on() { return g_prof.load(); }
 
 hipEvent_t pool_event() {
   if (g_pool_used == g_pool.size()) {
