@@ -241,6 +241,29 @@ def test_gram_space_head_eight_wave_apply_against_oracle():
     _same_weights_without_o(states, hp)
 
 
+def test_nesterov_bf16_gradients_through_the_gram_space_head():
+    """Nesterov momentum with bf16 gradients and padded rows on a group that
+    takes the Gram-space head (1024 x 2304, two wide and two tall): the
+    matrix the head orthogonalises is the look-ahead G + mu (mu M + G).
+    Against the oracle with O copies, then bit for bit without them (the
+    update in the last apply's epilogue)."""
+    states = []
+    for k in range(4):
+        shape = (1024, 2304) if k % 2 == 0 else (2304, 1024)
+        spec = wl.MatrixSpec("hn", *shape, "bf16", init_std=0.02, grad_std=1e-3, mom_std=1e-3)
+        seed = 3600 + k
+        w = wl.quantize_bf16(wl.normal(seed, 0, shape, 0.02))
+        g = wl.quantize_bf16(wl.normal(seed, 1, shape, 1e-3))
+        m = wl.quantize_f32(wl.normal(seed, 2, shape, 1e-3))
+        states.append(State(spec, w, g, m, g_dtype="bf16", ld_pad=8 * k))
+    hp = mc.hparams(lr=0.01, nesterov=1)
+    mc.muonclip_step([st.desc() for st in states], hp)
+    torch.cuda.synchronize()
+    for st in states:
+        check_matrix(st, hp)
+    _same_weights_without_o(states, hp)
+
+
 @pytest.mark.parametrize("shapes", [[(1024, 4096)], [(4096, 1024), (1024, 4096)]])
 def test_gram_space_head_split_k_against_oracle(shapes):
     """One or two 1024 x 4096 matrices: too few tiles to fill the chip, so the
